@@ -1,0 +1,223 @@
+/*
+ * msa.h -- C ABI of the MI355X (gfx950) Multi-Segment Attention library.
+ *
+ * Multi-Segment Attention (MSA) computes attention for a decode query, or a
+ * chunk of prefill queries, over only the blocks of a paged KV cache that
+ * survived lossless eviction.  The surviving blocks of each sequence are cut
+ * into maximal physically-contiguous segments, attention runs over the
+ * segments inside one launch, and the per-split partials are stitched by a
+ * log-sum-exp normaliser.
+ *   Source: "AsymCache：把 KV Cache 决策摆到 GPU 注意力内核的同一张桌子上"
+ *   (papers.ananclaw.com explainer of arXiv 2606.02964), section
+ *   "核心方法 / 1. Multi-Segment Attention (MSA)", its pseudocode
+ *   (multi_segment_attention, split_into_contiguous_segments,
+ *   attention_kernel(Q, seg.K, seg.V) * normalizer(seg)) and the paragraph
+ *   after it; "Multi-Segment Attention: Enabling Efficient KV-Cache
+ *   Management for Faster LLM Serving" (gptget.net), Methodology and Key
+ *   Results (one kernel processes many disjoint segments).
+ *
+ * Conventions for every call
+ *   - All array pointers are DEVICE pointers, owned by the caller; the
+ *     library keeps none of them after the call returns.
+ *   - Calls are asynchronous on `stream` (a hipStream_t passed as void*;
+ *     NULL = the null stream).  MSA_OK means "validated and enqueued", not
+ *     "finished".  No call synchronises with the host.
+ *   - The library allocates no memory and keeps no state between calls.
+ *     Scratch memory is a caller-provided `workspace` whose size comes from
+ *     the matching *_workspace_size function.  Calls that share a workspace
+ *     must be ordered on one stream.
+ *   - Host-detectable argument errors return a negative msa_status before
+ *     anything is enqueued.  Data errors that only the device can see are
+ *     reported through the plan's `dev_error` word (see below); the kernels
+ *     never read or write outside the buffers described here, whatever the
+ *     data.
+ *   - Logarithms are natural: LSE = ln(sum exp(score)), score = scale*q.k.
+ *
+ * Memory layouts (row-major, innermost last)
+ *   K/V pool    [P, block_size, Hkv, D]   dtype; P = num_phys_blocks
+ *   decode Q    [B, Hq, D]                dtype
+ *   decode O    [B, Hq, D]                dtype;  LSE [B, Hq] float32
+ *   prefill Q   [B, C, Hq, D]             dtype
+ *   prefill O   [B, C, Hq, D]             dtype;  LSE [B, C, Hq] float32
+ *   Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
+ *
+ * Supported kernels: block_size 16; D in {64, 128}; Hq/Hkv in {1, 2, 4, 8};
+ * decode in float32 or bfloat16; prefill in bfloat16.  Anything else
+ * returns MSA_ERR_UNSUPPORTED.  The plan itself accepts any block_size >= 1.
+ */
+#ifndef MSA_H
+#define MSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define MSA_VERSION 1
+
+typedef enum {
+  MSA_OK = 0,
+  MSA_ERR_INVALID_ARG = -1, /* null pointer, non-positive size, Hq % Hkv != 0, ... */
+  MSA_ERR_UNSUPPORTED = -2, /* dtype / head_dim / block_size / group size not built */
+  MSA_ERR_CAPACITY = -3,    /* workspace or output capacity too small */
+  MSA_ERR_DEVICE = -4       /* a HIP runtime call failed (launch error) */
+} msa_status;
+
+typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+
+/* Bits of the plan's device error word. */
+#define MSA_DEVERR_PHYS_RANGE 1 /* an alive block's physical id is outside [0, P); it was treated as evicted */
+#define MSA_DEVERR_CAPACITY 2   /* more segments than seg_capacity; extra records dropped, indptr clamped */
+#define MSA_DEVERR_CTX_RANGE 4  /* ctx_len < 0 or > max_blocks*block_size; clamped into range */
+
+/* One segment: a maximal run of alive blocks of one sequence that are
+ * consecutive both in logical index and in physical id.  24 bytes, plain
+ * int32 fields.  Tokens of the segment sit at logical positions
+ * logical_block*block_size + t and physical block phys_block + t/block_size,
+ * slot t%block_size, for t < num_tokens.  alive_token_start is the number of
+ * alive tokens of the sequence that precede the segment. */
+typedef struct {
+  int32_t seq;
+  int32_t logical_block;
+  int32_t phys_block;
+  int32_t num_blocks;
+  int32_t num_tokens;
+  int32_t alive_token_start;
+} msa_segment;
+
+/* ------------------------------------------------------------------------ */
+/* a1: segment plan                                                          */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes msa_plan_segments needs for B sequences. */
+size_t msa_plan_workspace_size(int32_t B);
+
+/* split_into_contiguous_segments (P1, MSA pseudocode; the split follows the
+ * physical layout, and the hole an evicted block leaves breaks a run).
+ *
+ * Reading used: logical block l+1 continues the segment holding block l iff
+ * both are alive and phys(l+1) == phys(l)+1.  Records are written per
+ * sequence in logical order, sequences in order; seg_indptr is the CSR
+ * offset array, so the segments of sequence b are
+ * segs[seg_indptr[b] .. seg_indptr[b+1]).
+ *
+ *   block_table  int32 [B, max_blocks]  physical id of each logical block;
+ *                entries of dead blocks are ignored (any value)
+ *   alive        uint8 [B, max_blocks]  nonzero = block resident
+ *   ctx_len      int32 [B]              tokens of each sequence; only blocks
+ *                l < ceil(ctx_len/block_size) are considered
+ *   segs         msa_segment [seg_capacity]   output
+ *   seg_indptr   int32 [B+1]            output
+ *   dev_error    int32 [1]              output, required: overwritten with the
+ *                OR of MSA_DEVERR_* bits found by this call (0 = none)
+ *   workspace    >= msa_plan_workspace_size(B) bytes
+ * seg_capacity >= B*max_blocks can never overflow.  The plan is valid for as
+ * long as table, alive and ctx_len are unchanged; attention over a stale
+ * plan reads the pool where the plan says (in bounds) but is undefined. */
+int msa_plan_segments(const int32_t* block_table, const uint8_t* alive, const int32_t* ctx_len,
+                      int32_t B, int32_t max_blocks, int32_t block_size, int32_t num_phys_blocks,
+                      msa_segment* segs, int32_t seg_capacity, int32_t* seg_indptr,
+                      int32_t* dev_error, void* workspace, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* a2+a3(+a5): decode                                                        */
+/* ------------------------------------------------------------------------ */
+
+/* Workspace bytes for msa_decode with the same shape arguments.  Zero when
+ * one split covers max_ctx_len (then no partials and no merge launch). */
+size_t msa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t max_ctx_len, int32_t block_size, int32_t split_blocks);
+
+/* multi_segment_attention for one decode query per sequence (P1 MSA
+ * pseudocode; P2 Key Results: one kernel over many disjoint segments).
+ *
+ * The query of sequence b attends to every alive token of b (it sits after
+ * all of them: no mask).  Work split: each sequence's alive-token stream is
+ * cut into splits of split_blocks blocks (0 = chosen by the library from
+ * B, Hkv and max_ctx_len); each (sequence, KV head, split) is one workgroup
+ * that walks its segments in logical order and folds them into a running
+ * (max, sum-exp, unnormalised output).  When a sequence needs more than one
+ * split the partials go to `workspace` and a merge kernel stitches them by
+ * log-sum-exp (same as msa_merge_partials).
+ *
+ *   q            [B, Hq, D] dtype           k_pool, v_pool  [P, 16, Hkv, D] dtype
+ *   segs, seg_indptr   a plan from msa_plan_segments over the same pool
+ *   max_ctx_len  >= every sequence's number of alive tokens (sizes the grid)
+ *   scale        softmax scale; <= 0 selects 1/sqrt(D)
+ *   out          [B, Hq, D] dtype           lse_out  [B, Hq] float32, may be NULL
+ * A sequence with no alive token gets out = 0 and lse = -inf. */
+int msa_decode(const void* q, const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
+               int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr, int32_t B,
+               int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype,
+               float scale, int32_t split_blocks, void* out, float* lse_out, void* workspace,
+               size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* a2+a4(+a5): chunked prefill                                               */
+/* ------------------------------------------------------------------------ */
+
+size_t msa_prefill_workspace_size(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t max_ctx_len, int32_t block_size, int32_t split_blocks);
+
+/* multi_segment_attention for a chunk of C query rows per sequence (P1 MSA
+ * pseudocode; P1 "3. 自适应分块调度器": prefill runs in chunks).
+ *
+ * Row i of sequence b sits at logical position q_pos0[b] + i; key at
+ * logical position p is visible to it iff p <= q_pos0[b] + i (causal by
+ * logical position; evicted tokens are simply absent).  The chunk's own K/V
+ * must already be written into the pool as alive blocks covered by the
+ * plan.  QK^T and PV run on bf16 MFMA with float32 accumulation; the
+ * softmax weights are rounded to bf16 for PV.
+ *
+ *   q       [B, C, Hq, D] bf16     q_pos0  int32 [B] (device)
+ *   out     [B, C, Hq, D] bf16     lse_out [B, C, Hq] float32, may be NULL
+ *   split_blocks  0 = one split per (row tile, KV head, sequence); otherwise
+ *                 the alive-key stream is cut into splits of that many
+ *                 blocks, merged by log-sum-exp through `workspace`.
+ * A row that sees no key gets out = 0 and lse = -inf. */
+int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const void* k_pool,
+                      const void* v_pool, int32_t num_phys_blocks, int32_t block_size,
+                      const msa_segment* segs, const int32_t* seg_indptr, int32_t B, int32_t Hq,
+                      int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype, float scale,
+                      int32_t split_blocks, void* out, float* lse_out, void* workspace,
+                      size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* a5: log-sum-exp merge of partials                                         */
+/* ------------------------------------------------------------------------ */
+
+/* out += attention_kernel(Q, seg.K, seg.V) * normalizer(seg) (P1 MSA
+ * pseudocode), with normalizer read as the log-sum-exp weight.
+ *
+ * Partials of sequence b are rows [part_indptr[b], part_indptr[b+1]) of
+ *   o_part  float32 [N, R, H, D]   unnormalised output  sum_j exp(s_j - m) v_j
+ *   m_part  float32 [N, R, H]      running max m (natural-log units; -inf = empty)
+ *   l_part  float32 [N, R, H]      sum_j exp(s_j - m)
+ * merged in that (logical) order:
+ *   M = max_i m_i,  w_i = exp(m_i - M) (0 if m_i = -inf),  L = sum_i w_i l_i,
+ *   out = sum_i w_i o_i / L,  lse = M + ln L;  all empty -> out 0, lse -inf.
+ * o_part of an empty partial is never read.
+ *   out  [B, R, H, D] out_dtype      lse_out [B, R, H] float32, may be NULL
+ * R is 1 for decode and C for prefill. */
+int msa_merge_partials(const float* o_part, const float* m_part, const float* l_part,
+                       const int32_t* part_indptr, int32_t B, int32_t R, int32_t H, int32_t D,
+                       msa_dtype out_dtype, void* out, float* lse_out, void* stream);
+
+/* ------------------------------------------------------------------------ */
+
+/* 1 if the attention kernels were built for this shape, else 0.
+ * prefill = 0 asks about msa_decode, 1 about msa_prefill_chunk;
+ * group_size = Hq / Hkv.  No device work, no side effects. */
+int msa_attention_supported(int prefill, msa_dtype dtype, int32_t head_dim, int32_t group_size,
+                            int32_t block_size);
+
+const char* msa_status_string(int status);
+int msa_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MSA_H */

@@ -1,0 +1,247 @@
+"""Multi-Segment Attention (MSA) on MI355X: thin PyTorch binding of libmsa.
+
+The four calls mirror the C ABI in include/msa.h one to one; this module
+only checks tensor shapes/dtypes/devices, allocates outputs and workspaces
+with torch (device memory plumbing), and passes raw pointers plus the
+current HIP stream.  Every step of the computation runs in libmsa's HIP
+kernels; there is no CPU or PyTorch fallback, and a missing library raises.
+
+  msa_plan_segments   block table + alive mask -> segment list (a1)
+  msa_decode          decode attention over the segments (a2, a3, a5)
+  msa_prefill_chunk   chunked-prefill attention over the segments (a2, a4, a5)
+  msa_merge_partials  log-sum-exp merge of (m, l, o) partials (a5)
+"""
+from __future__ import annotations
+
+import ctypes
+
+import torch
+
+from . import _lib
+from ._lib import (MsaError, MSA_F32, MSA_BF16, MSA_DEVERR_PHYS_RANGE, MSA_DEVERR_CAPACITY,
+                   MSA_DEVERR_CTX_RANGE)
+
+__all__ = ["msa_plan_segments", "msa_decode", "msa_prefill_chunk", "msa_merge_partials",
+           "msa_plan_workspace_size", "msa_decode_workspace_size", "msa_prefill_workspace_size",
+           "MsaError", "MSA_F32", "MSA_BF16", "MSA_DEVERR_PHYS_RANGE", "MSA_DEVERR_CAPACITY",
+           "MSA_DEVERR_CTX_RANGE", "SEG_FIELDS", "library_path", "prefill_available", "decode_available"]
+
+SEG_FIELDS = ("seq", "logical_block", "phys_block", "num_blocks", "num_tokens",
+              "alive_token_start")
+
+
+def library_path() -> str:
+    return _lib.LIB_PATH
+
+
+def prefill_available(dtype: int = MSA_BF16, D: int = 128, G: int = 4) -> bool:
+    """True if libmsa was built with the chunked-prefill kernel for this shape."""
+    return bool(_lib.load().msa_attention_supported(1, dtype, D, G, 16))
+
+
+def decode_available(dtype: int = MSA_BF16, D: int = 128, G: int = 4) -> bool:
+    """True if libmsa was built with the decode kernel for this shape."""
+    return bool(_lib.load().msa_attention_supported(0, dtype, D, G, 16))
+
+
+def _lib_handle():
+    return _lib.load()
+
+
+def _dev_ptr(t: torch.Tensor | None, name: str):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device (HIP) tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream, device):
+    if stream is None:
+        stream = torch.cuda.current_stream(device)
+    return ctypes.c_void_p(stream.cuda_stream)
+
+
+def _dtype_enum(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return MSA_BF16
+    if t.dtype == torch.float32:
+        return MSA_F32
+    raise ValueError(f"unsupported dtype {t.dtype}")
+
+
+def _expect(t, dtype, name, ndim=None):
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
+
+
+# ---------------------------------------------------------------------------
+# a1: plan
+# ---------------------------------------------------------------------------
+
+def msa_plan_workspace_size(B: int) -> int:
+    return int(_lib_handle().msa_plan_workspace_size(B))
+
+
+def msa_plan_segments(block_table: torch.Tensor, alive: torch.Tensor, ctx_len: torch.Tensor,
+                      block_size: int, num_phys_blocks: int, seg_capacity: int | None = None,
+                      segs: torch.Tensor | None = None, seg_indptr: torch.Tensor | None = None,
+                      dev_error: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+                      stream=None):
+    """Segment plan.  Returns (segs int32 [seg_capacity, 6], seg_indptr int32 [B+1],
+    dev_error int32 [1]); rows of segs beyond seg_indptr[B] are unspecified."""
+    lib = _lib_handle()
+    _expect(block_table, torch.int32, "block_table", 2)
+    _expect(alive, torch.uint8, "alive", 2)
+    _expect(ctx_len, torch.int32, "ctx_len", 1)
+    B, max_blocks = block_table.shape
+    if tuple(alive.shape) != (B, max_blocks) or ctx_len.shape[0] != B:
+        raise ValueError("block_table, alive and ctx_len disagree on shape")
+    dev = block_table.device
+    cap = B * max_blocks if seg_capacity is None else int(seg_capacity)
+    if segs is None:
+        segs = torch.empty((max(cap, 1), 6), dtype=torch.int32, device=dev)
+    if seg_indptr is None:
+        seg_indptr = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    if dev_error is None:
+        dev_error = torch.empty(1, dtype=torch.int32, device=dev)
+    wsb = int(lib.msa_plan_workspace_size(B))
+    if workspace is None:
+        workspace = torch.empty(max(wsb, 1), dtype=torch.uint8, device=dev)
+    st = lib.msa_plan_segments(_dev_ptr(block_table, "block_table"), _dev_ptr(alive, "alive"),
+                               _dev_ptr(ctx_len, "ctx_len"), B, max_blocks, block_size,
+                               num_phys_blocks, _dev_ptr(segs, "segs"), cap,
+                               _dev_ptr(seg_indptr, "seg_indptr"), _dev_ptr(dev_error, "dev_error"),
+                               _dev_ptr(workspace, "workspace"), workspace.numel(),
+                               _stream(stream, dev))
+    _lib.check(st, "msa_plan_segments")
+    return segs, seg_indptr, dev_error
+
+
+# ---------------------------------------------------------------------------
+# a2/a3/a5: decode
+# ---------------------------------------------------------------------------
+
+def msa_decode_workspace_size(B, Hq, Hkv, D, max_ctx_len, block_size=16, split_blocks=0) -> int:
+    return int(_lib_handle().msa_decode_workspace_size(B, Hq, Hkv, D, max_ctx_len, block_size,
+                                                       split_blocks))
+
+
+def msa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs: torch.Tensor,
+               seg_indptr: torch.Tensor, max_ctx_len: int, scale: float = 0.0,
+               split_blocks: int = 0, out: torch.Tensor | None = None,
+               lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
+               want_lse: bool = True, stream=None):
+    """Decode attention.  q [B, Hq, D]; pools [P, 16, Hkv, D] (same dtype as q).
+    Returns (out [B, Hq, D], lse [B, Hq] float32 or None)."""
+    lib = _lib_handle()
+    if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("q must be [B,Hq,D]; k_pool/v_pool [P,bs,Hkv,D] of equal shape")
+    if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
+        raise ValueError("q, k_pool and v_pool must share a dtype")
+    _expect(segs, torch.int32, "segs", 2)
+    _expect(seg_indptr, torch.int32, "seg_indptr", 1)
+    B, Hq, D = q.shape
+    P, bs, Hkv, Dk = k_pool.shape
+    if Dk != D or seg_indptr.shape[0] != B + 1:
+        raise ValueError("shape mismatch between q, pools and seg_indptr")
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, Hq), dtype=torch.float32, device=dev)
+    wsb = int(lib.msa_decode_workspace_size(B, Hq, Hkv, D, max_ctx_len, bs, split_blocks))
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = lib.msa_decode(_dev_ptr(q, "q"), _dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"),
+                        P, bs, _dev_ptr(segs, "segs"), _dev_ptr(seg_indptr, "seg_indptr"),
+                        B, Hq, Hkv, D, int(max_ctx_len), _dtype_enum(q), float(scale),
+                        int(split_blocks), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
+                        _dev_ptr(workspace, "workspace"),
+                        0 if workspace is None else workspace.numel() * workspace.element_size(),
+                        _stream(stream, dev))
+    _lib.check(st, "msa_decode")
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# a2/a4/a5: chunked prefill
+# ---------------------------------------------------------------------------
+
+def msa_prefill_workspace_size(B, C, Hq, Hkv, D, max_ctx_len, block_size=16, split_blocks=0) -> int:
+    return int(_lib_handle().msa_prefill_workspace_size(B, C, Hq, Hkv, D, max_ctx_len, block_size,
+                                                        split_blocks))
+
+
+def msa_prefill_chunk(q: torch.Tensor, q_pos0: torch.Tensor, k_pool: torch.Tensor,
+                      v_pool: torch.Tensor, segs: torch.Tensor, seg_indptr: torch.Tensor,
+                      max_ctx_len: int, scale: float = 0.0, split_blocks: int = 0,
+                      out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                      workspace: torch.Tensor | None = None, want_lse: bool = True, stream=None):
+    """Chunked-prefill attention.  q [B, C, Hq, D] bf16; q_pos0 int32 [B].
+    Returns (out [B, C, Hq, D], lse [B, C, Hq] float32 or None)."""
+    lib = _lib_handle()
+    if q.dim() != 4 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
+        raise ValueError("q must be [B,C,Hq,D]; k_pool/v_pool [P,bs,Hkv,D] of equal shape")
+    if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
+        raise ValueError("q, k_pool and v_pool must share a dtype")
+    _expect(q_pos0, torch.int32, "q_pos0", 1)
+    _expect(segs, torch.int32, "segs", 2)
+    _expect(seg_indptr, torch.int32, "seg_indptr", 1)
+    B, C, Hq, D = q.shape
+    P, bs, Hkv, Dk = k_pool.shape
+    if Dk != D or seg_indptr.shape[0] != B + 1 or q_pos0.shape[0] != B:
+        raise ValueError("shape mismatch between q, pools, q_pos0 and seg_indptr")
+    dev = q.device
+    if out is None:
+        out = torch.empty_like(q)
+    if lse is None and want_lse:
+        lse = torch.empty((B, C, Hq), dtype=torch.float32, device=dev)
+    wsb = int(lib.msa_prefill_workspace_size(B, C, Hq, Hkv, D, max_ctx_len, bs, split_blocks))
+    if workspace is None and wsb > 0:
+        workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
+    st = lib.msa_prefill_chunk(_dev_ptr(q, "q"), C, _dev_ptr(q_pos0, "q_pos0"),
+                               _dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"), P, bs,
+                               _dev_ptr(segs, "segs"), _dev_ptr(seg_indptr, "seg_indptr"),
+                               B, Hq, Hkv, D, int(max_ctx_len), _dtype_enum(q), float(scale),
+                               int(split_blocks), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
+                               _dev_ptr(workspace, "workspace"),
+                               0 if workspace is None else workspace.numel() * workspace.element_size(),
+                               _stream(stream, dev))
+    _lib.check(st, "msa_prefill_chunk")
+    return out, lse
+
+
+# ---------------------------------------------------------------------------
+# a5: merge
+# ---------------------------------------------------------------------------
+
+def msa_merge_partials(o_part: torch.Tensor, m_part: torch.Tensor, l_part: torch.Tensor,
+                       part_indptr: torch.Tensor, out_dtype: torch.dtype = torch.float32,
+                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
+                       want_lse: bool = True, stream=None):
+    """Merge partials o [N, R, H, D], m/l [N, R, H] (float32) per part_indptr [B+1].
+    Returns (out [B, R, H, D] out_dtype, lse [B, R, H] float32 or None)."""
+    lib = _lib_handle()
+    for t, n in ((o_part, "o_part"), (m_part, "m_part"), (l_part, "l_part")):
+        _expect(t, torch.float32, n)
+    _expect(part_indptr, torch.int32, "part_indptr", 1)
+    N, R, H, D = o_part.shape
+    if tuple(m_part.shape) != (N, R, H) or tuple(l_part.shape) != (N, R, H):
+        raise ValueError("m_part/l_part must be [N, R, H]")
+    B = part_indptr.shape[0] - 1
+    dev = o_part.device
+    if out is None:
+        out = torch.empty((B, R, H, D), dtype=out_dtype, device=dev)
+    if lse is None and want_lse:
+        lse = torch.empty((B, R, H), dtype=torch.float32, device=dev)
+    st = lib.msa_merge_partials(_dev_ptr(o_part, "o_part"), _dev_ptr(m_part, "m_part"),
+                                _dev_ptr(l_part, "l_part"), _dev_ptr(part_indptr, "part_indptr"),
+                                B, R, H, D, _dtype_enum(out), _dev_ptr(out, "out"),
+                                _dev_ptr(lse, "lse"), _stream(stream, dev))
+    _lib.check(st, "msa_merge_partials")
+    return out, lse

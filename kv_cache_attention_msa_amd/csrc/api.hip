@@ -1,0 +1,247 @@
+// C ABI of libmsa: argument validation, workspace carving, launches.
+// Every entry point checks what the host can check before it enqueues
+// anything, and returns a negative msa_status on the first problem.
+#include <math.h>
+#include <stdint.h>
+
+#include "msa_internal.h"
+
+using namespace msa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+inline size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct PartLayout {
+  size_t o_off, m_off, l_off, total;
+};
+
+// partials for N splits, R rows, H heads, D dims: o [N,R,H,D], m and l [N,R,H]
+inline PartLayout part_layout(int64_t N, int64_t R, int64_t H, int64_t D) {
+  PartLayout L;
+  L.o_off = 0;
+  L.m_off = align_up(size_t(N * R * H * D) * sizeof(float));
+  L.l_off = L.m_off + align_up(size_t(N * R * H) * sizeof(float));
+  L.total = L.l_off + align_up(size_t(N * R * H) * sizeof(float));
+  return L;
+}
+
+inline hipStream_t as_stream(void* s) { return reinterpret_cast<hipStream_t>(s); }
+
+inline int from_hip(hipError_t e) { return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE; }
+
+// shape checks common to decode and prefill
+int check_attn_shape(const void* q, const void* k_pool, const void* v_pool, int32_t P,
+                     int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr,
+                     int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len,
+                     msa_dtype dtype, float scale, int32_t split_blocks, const void* out) {
+  if (!q || !k_pool || !v_pool || !segs || !seg_indptr || !out) return MSA_ERR_INVALID_ARG;
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || P <= 0 || max_ctx_len < 0 || block_size <= 0)
+    return MSA_ERR_INVALID_ARG;
+  if (Hq % Hkv != 0) return MSA_ERR_INVALID_ARG;
+  if (split_blocks < 0) return MSA_ERR_INVALID_ARG;
+  if (isnan(scale) || isinf(scale)) return MSA_ERR_INVALID_ARG;
+  if (dtype != MSA_F32 && dtype != MSA_BF16) return MSA_ERR_UNSUPPORTED;
+  if (block_size != 16) return MSA_ERR_UNSUPPORTED;
+  if (B > 65535 || Hkv > 65535) return MSA_ERR_UNSUPPORTED;  // grid y/z limits
+  return MSA_OK;
+}
+
+inline float resolve_scale(float scale, int32_t D) {
+  return scale > 0.f ? scale : 1.0f / sqrtf(float(D));
+}
+
+constexpr float kLog2e = 1.44269504088896340736f;
+
+}  // namespace
+
+extern "C" {
+
+int msa_version(void) { return MSA_VERSION; }
+
+int msa_attention_supported(int prefill, msa_dtype dtype, int32_t head_dim, int32_t group_size,
+                            int32_t block_size) {
+  if (block_size != 16) return 0;
+  return (prefill ? prefill_supported(dtype, head_dim, group_size)
+                  : decode_supported(dtype, head_dim, group_size)) ? 1 : 0;
+}
+
+const char* msa_status_string(int status) {
+  switch (status) {
+    case MSA_OK: return "MSA_OK";
+    case MSA_ERR_INVALID_ARG: return "MSA_ERR_INVALID_ARG: invalid argument";
+    case MSA_ERR_UNSUPPORTED: return "MSA_ERR_UNSUPPORTED: configuration not built";
+    case MSA_ERR_CAPACITY: return "MSA_ERR_CAPACITY: workspace or output too small";
+    case MSA_ERR_DEVICE: return "MSA_ERR_DEVICE: HIP runtime error";
+  }
+  return "unknown msa status";
+}
+
+// ---------------------------------------------------------------------------
+size_t msa_plan_workspace_size(int32_t B) { return B > 0 ? align_up(size_t(B) * 2 * sizeof(int32_t)) : 0; }
+
+int msa_plan_segments(const int32_t* block_table, const uint8_t* alive, const int32_t* ctx_len,
+                      int32_t B, int32_t max_blocks, int32_t block_size, int32_t num_phys_blocks,
+                      msa_segment* segs, int32_t seg_capacity, int32_t* seg_indptr,
+                      int32_t* dev_error, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!block_table || !alive || !ctx_len || !seg_indptr || !dev_error || !workspace)
+    return MSA_ERR_INVALID_ARG;
+  if (B <= 0 || max_blocks <= 0 || block_size <= 0 || num_phys_blocks <= 0 || seg_capacity < 0)
+    return MSA_ERR_INVALID_ARG;
+  if (seg_capacity > 0 && !segs) return MSA_ERR_INVALID_ARG;
+  if (int64_t(max_blocks) * block_size > INT32_MAX) return MSA_ERR_INVALID_ARG;
+  if (int64_t(B) * max_blocks > INT32_MAX) return MSA_ERR_INVALID_ARG;
+  if (B > 2147483647 / 2) return MSA_ERR_INVALID_ARG;
+  if (workspace_bytes < msa_plan_workspace_size(B)) return MSA_ERR_CAPACITY;
+  PlanParams p;
+  p.table = block_table;
+  p.alive = alive;
+  p.ctx_len = ctx_len;
+  p.B = B;
+  p.max_blocks = max_blocks;
+  p.bs = block_size;
+  p.P = num_phys_blocks;
+  p.segs = segs;
+  p.cap = seg_capacity;
+  p.indptr = seg_indptr;
+  p.dev_error = dev_error;
+  p.ws = static_cast<int32_t*>(workspace);
+  return from_hip(launch_plan(p, as_stream(stream)));
+}
+
+// ---------------------------------------------------------------------------
+size_t msa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                                 int32_t max_ctx_len, int32_t block_size, int32_t split_blocks) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || max_ctx_len < 0) return 0;
+  const SplitPlan sp = decode_split(B, Hkv, max_ctx_len, block_size, split_blocks);
+  if (sp.S <= 1) return 0;
+  return part_layout(int64_t(B) * sp.S, 1, Hq, D).total;
+}
+
+int msa_decode(const void* q, const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
+               int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr, int32_t B,
+               int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype,
+               float scale, int32_t split_blocks, void* out, float* lse_out, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  int st = check_attn_shape(q, k_pool, v_pool, num_phys_blocks, block_size, segs, seg_indptr, B,
+                            Hq, Hkv, D, max_ctx_len, dtype, scale, split_blocks, out);
+  if (st != MSA_OK) return st;
+  if (!decode_supported(dtype, D, Hq / Hkv)) return MSA_ERR_UNSUPPORTED;
+  if (split_blocks > decode_max_split_blocks()) return MSA_ERR_INVALID_ARG;
+  const SplitPlan sp = decode_split(B, Hkv, max_ctx_len, block_size, split_blocks);
+  const size_t need = msa_decode_workspace_size(B, Hq, Hkv, D, max_ctx_len, block_size, split_blocks);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MSA_ERR_CAPACITY;
+
+  DecodeParams p;
+  p.q = q;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.P = num_phys_blocks;
+  p.segs = segs;
+  p.indptr = seg_indptr;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.dtype = dtype;
+  p.scale_log2 = resolve_scale(scale, D) * kLog2e;
+  p.split_blocks = sp.split_blocks;
+  p.S = sp.S;
+  p.out = out;
+  p.lse = lse_out;
+  p.o_part = p.m_part = p.l_part = nullptr;
+  if (sp.S > 1) {
+    const PartLayout L = part_layout(int64_t(B) * sp.S, 1, Hq, D);
+    char* ws = static_cast<char*>(workspace);
+    p.o_part = reinterpret_cast<float*>(ws + L.o_off);
+    p.m_part = reinterpret_cast<float*>(ws + L.m_off);
+    p.l_part = reinterpret_cast<float*>(ws + L.l_off);
+  }
+  hipError_t e = launch_decode(p, as_stream(stream));
+  if (e != hipSuccess) return MSA_ERR_DEVICE;
+  if (sp.S > 1) {
+    e = launch_merge_from_plan(p.o_part, p.m_part, p.l_part, segs, seg_indptr, B, 1, Hq, D, sp.S,
+                               sp.split_blocks, dtype, out, lse_out, as_stream(stream));
+    if (e != hipSuccess) return MSA_ERR_DEVICE;
+  }
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+size_t msa_prefill_workspace_size(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t D,
+                                  int32_t max_ctx_len, int32_t block_size, int32_t split_blocks) {
+  if (B <= 0 || C <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || max_ctx_len < 0)
+    return 0;
+  const SplitPlan sp = prefill_split(B, C, Hq, Hkv, max_ctx_len, block_size, split_blocks);
+  if (sp.S <= 1) return 0;
+  return part_layout(int64_t(B) * sp.S, C, Hq, D).total;
+}
+
+int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const void* k_pool,
+                      const void* v_pool, int32_t num_phys_blocks, int32_t block_size,
+                      const msa_segment* segs, const int32_t* seg_indptr, int32_t B, int32_t Hq,
+                      int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype, float scale,
+                      int32_t split_blocks, void* out, float* lse_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  int st = check_attn_shape(q, k_pool, v_pool, num_phys_blocks, block_size, segs, seg_indptr, B,
+                            Hq, Hkv, D, max_ctx_len, dtype, scale, split_blocks, out);
+  if (st != MSA_OK) return st;
+  if (!q_pos0 || C <= 0) return MSA_ERR_INVALID_ARG;
+  if (!prefill_supported(dtype, D, Hq / Hkv)) return MSA_ERR_UNSUPPORTED;
+  if (split_blocks > prefill_max_split_blocks()) return MSA_ERR_INVALID_ARG;
+  const SplitPlan sp = prefill_split(B, C, Hq, Hkv, max_ctx_len, block_size, split_blocks);
+  const size_t need =
+      msa_prefill_workspace_size(B, C, Hq, Hkv, D, max_ctx_len, block_size, split_blocks);
+  if (need > 0 && (!workspace || workspace_bytes < need)) return MSA_ERR_CAPACITY;
+
+  PrefillParams p;
+  p.q = q;
+  p.q_pos0 = q_pos0;
+  p.C = C;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.P = num_phys_blocks;
+  p.segs = segs;
+  p.indptr = seg_indptr;
+  p.B = B;
+  p.Hq = Hq;
+  p.Hkv = Hkv;
+  p.D = D;
+  p.scale_log2 = resolve_scale(scale, D) * kLog2e;
+  p.split_blocks = sp.split_blocks;
+  p.S = sp.S;
+  p.out = out;
+  p.lse = lse_out;
+  p.o_part = p.m_part = p.l_part = nullptr;
+  if (sp.S > 1) {
+    const PartLayout L = part_layout(int64_t(B) * sp.S, C, Hq, D);
+    char* ws = static_cast<char*>(workspace);
+    p.o_part = reinterpret_cast<float*>(ws + L.o_off);
+    p.m_part = reinterpret_cast<float*>(ws + L.m_off);
+    p.l_part = reinterpret_cast<float*>(ws + L.l_off);
+  }
+  hipError_t e = launch_prefill(p, as_stream(stream));
+  if (e != hipSuccess) return MSA_ERR_DEVICE;
+  if (sp.S > 1) {
+    e = launch_merge_from_plan(p.o_part, p.m_part, p.l_part, segs, seg_indptr, B, C, Hq, D, sp.S,
+                               sp.split_blocks, dtype, out, lse_out, as_stream(stream));
+    if (e != hipSuccess) return MSA_ERR_DEVICE;
+  }
+  return MSA_OK;
+}
+
+// ---------------------------------------------------------------------------
+int msa_merge_partials(const float* o_part, const float* m_part, const float* l_part,
+                       const int32_t* part_indptr, int32_t B, int32_t R, int32_t H, int32_t D,
+                       msa_dtype out_dtype, void* out, float* lse_out, void* stream) {
+  if (!o_part || !m_part || !l_part || !part_indptr || !out) return MSA_ERR_INVALID_ARG;
+  if (B <= 0 || R <= 0 || H <= 0 || D <= 0) return MSA_ERR_INVALID_ARG;
+  if (out_dtype != MSA_F32 && out_dtype != MSA_BF16) return MSA_ERR_UNSUPPORTED;
+  if (B > 65535 || R > 65535) return MSA_ERR_UNSUPPORTED;
+  if (int64_t(H) * D > INT32_MAX) return MSA_ERR_INVALID_ARG;
+  return from_hip(launch_merge_indptr(o_part, m_part, l_part, part_indptr, B, R, H, D, out_dtype,
+                                      out, lse_out, as_stream(stream)));
+}
+
+}  // extern "C"

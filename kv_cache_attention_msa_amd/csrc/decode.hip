@@ -1,0 +1,422 @@
+// a2 + a3: MSA decode over the alive-token stream of a segment plan.
+//
+// multi_segment_attention for one decode query per sequence (P1, "Core
+// method 1: MSA" pseudocode; P2, Key Results: one kernel over many disjoint
+// KV segments).  Decode is bandwidth-bound (it reads every resident K/V
+// row once per generated token; P3, "解决什么真问题", item 2), so this is a
+// VALU kernel built around the HBM stream, not a matrix-core kernel.
+//
+// Grid: (split s, KV head g, sequence b); 256 threads = 4 wavefronts.
+//   * The sequence's alive blocks, in logical order, are numbered
+//     0..nAB-1 (block j holds alive tokens [16j, 16j+16)); split s owns
+//     blocks [s*T, (s+1)*T).  The workgroup finds the segment holding its
+//     first block with a workgroup-parallel search over alive_token_start,
+//     then expands its segments into a per-block physical id list in LDS.
+//     Consecutive segments are folded into one running softmax state in
+//     registers; partials exist only per split, never per segment.
+//   * Each wavefront takes tiles of 4 blocks (64 tokens), interleaved with
+//     the other wavefronts.  K rows are loaded with coalesced 16-byte loads
+//     (4 rows of 256 B per instruction for bf16, D=128), staged through LDS
+//     with an XOR swizzle, and read back one token per lane; the G query
+//     heads of the KV head (GQA group) are broadcast from LDS, so each K/V
+//     row is read from HBM once for all G heads.  Scores use v_dot2 on bf16
+//     pairs with fp32 accumulation.
+//   * Online softmax per wavefront: wave max by DPP + cross-row shuffles,
+//     exp2 with the scale folded into log2 units; the weights go through
+//     LDS and are broadcast to the PV loop, in which each lane owns a slice
+//     of D and accumulates fp32 for all G heads.  V rows of masked tokens
+//     (padding past ctx_len, blocks outside the split) are zeroed by a
+//     select, never multiplied by 0, so NaN-poisoned slots cannot leak.
+//   * At the end the 4 wavefront states are merged in LDS; a sequence with
+//     one split writes O and LSE directly, otherwise the split writes its
+//     (m, l, o) partial for the merge kernel.
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kNW = kThreads / kWave;
+constexpr int kTileTok = 64;      // tokens per wavefront tile (4 blocks of 16)
+constexpr int kBlk = 16;          // block size the kernels are built for
+constexpr int kMaxSplitBlocks = 512;
+constexpr float kLn2 = 0.69314718055994530942f;
+
+template <typename KV, int D>
+struct Geo {
+  static constexpr int ES = sizeof(KV);
+  static constexpr int ROW = D * ES;              // bytes of one head's row
+  static constexpr int CH = ROW / 16;             // 16-byte chunks per row
+  static constexpr int SW = CH < 16 ? CH : 16;    // swizzle period
+  static constexpr int LPR = ROW / 4 < 64 ? ROW / 4 : 64;  // lanes per V row
+  static constexpr int BPL = ROW / LPR;           // V bytes per lane per row
+  static constexpr int RPL = kWave / LPR;         // V rows per load instruction
+  static constexpr int EPL = BPL / ES;            // V elements per lane
+  static constexpr int KLOADS = kTileTok * CH / kWave;
+  static constexpr int VLOADS = kTileTok / RPL;
+  static_assert(BPL == 4, "V lane slice must be one dword");
+};
+
+__device__ __forceinline__ float dot_chunk(uint4 q, uint4 k, float acc, uint16_t) {
+  typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.x),
+                                        __builtin_bit_cast(bf16x2_t, k.x), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.y),
+                                        __builtin_bit_cast(bf16x2_t, k.y), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.z),
+                                        __builtin_bit_cast(bf16x2_t, k.z), acc, false);
+  acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, q.w),
+                                        __builtin_bit_cast(bf16x2_t, k.w), acc, false);
+  return acc;
+}
+
+__device__ __forceinline__ float dot_chunk(uint4 q, uint4 k, float acc, float) {
+  acc = fmaf(__uint_as_float(q.x), __uint_as_float(k.x), acc);
+  acc = fmaf(__uint_as_float(q.y), __uint_as_float(k.y), acc);
+  acc = fmaf(__uint_as_float(q.z), __uint_as_float(k.z), acc);
+  acc = fmaf(__uint_as_float(q.w), __uint_as_float(k.w), acc);
+  return acc;
+}
+
+template <typename KV>
+__device__ __forceinline__ void unpack_v(uint32_t w, float* v);
+template <>
+__device__ __forceinline__ void unpack_v<uint16_t>(uint32_t w, float* v) {
+  v[0] = bf16lo_to_f32(w);
+  v[1] = bf16hi_to_f32(w);
+}
+template <>
+__device__ __forceinline__ void unpack_v<float>(uint32_t w, float* v) {
+  v[0] = __uint_as_float(w);
+}
+
+template <typename KV>
+__device__ __forceinline__ void store_out(void* out, size_t idx, float v);
+template <>
+__device__ __forceinline__ void store_out<uint16_t>(void* out, size_t idx, float v) {
+  static_cast<uint16_t*>(out)[idx] = f32_to_bf16(v);
+}
+template <>
+__device__ __forceinline__ void store_out<float>(void* out, size_t idx, float v) {
+  static_cast<float*>(out)[idx] = v;
+}
+
+// Largest i in [lo, hi) with segs[i].alive_token_start <= x, given that
+// segs[lo] satisfies it.  Workgroup-uniform; every thread must call it.
+__device__ __forceinline__ int wg_search_segment(const msa_segment* segs, int lo, int hi, int x) {
+  while (hi - lo > 1) {
+    const int step = (hi - lo + kThreads - 1) / kThreads;
+    const int idx = lo + int(threadIdx.x) * step;
+    const bool pred = idx < hi && segs[idx].alive_token_start <= x;
+    const int cnt = __syncthreads_count(pred);
+    lo = lo + (cnt - 1) * step;
+    hi = min(hi, lo + step);
+  }
+  return lo;
+}
+
+template <typename KV, int D, int G>
+__global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
+  using GE = Geo<KV, D>;
+  constexpr int ROW = GE::ROW, CH = GE::CH, SW = GE::SW;
+  constexpr int LPR = GE::LPR, RPL = GE::RPL, EPL = GE::EPL;
+
+  // K tiles; during set-up the same bytes hold the staged segment list, and
+  // at the end the per-wavefront states for the cross-wave merge.
+  __shared__ __align__(16) uint8_t k_lds[kNW][kTileTok * ROW];
+  __shared__ __align__(16) float p_lds[kNW][kTileTok][G];
+  __shared__ __align__(16) uint8_t q_lds[G * ROW];
+  __shared__ int32_t blk_phys[kMaxSplitBlocks];
+  static_assert(sizeof(k_lds) >= 3 * (kMaxSplitBlocks + 1) * sizeof(int32_t), "staging");
+  static_assert(sizeof(k_lds) >= (kNW * G * D + 2 * kNW * G) * sizeof(float), "merge");
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  const int T = p.split_blocks;
+
+  const int s0 = p.indptr[b], s1 = p.indptr[b + 1];
+  int A = 0;
+  if (s1 > s0) {
+    const msa_segment last = p.segs[s1 - 1];
+    A = last.alive_token_start + last.num_tokens;
+  }
+  // a plan with more alive tokens than max_ctx_len promised is cut at the grid
+  const int nAB = min((A + kBlk - 1) / kBlk, p.S * T);
+  const int Sb = (nAB + T - 1) / T;
+  if (s >= Sb) {
+    if (s == 0 && p.S == 1) {  // no alive token at all: O = 0, LSE = -inf
+      for (int i = tid; i < G * D; i += kThreads) {
+        const int h = g * G + i / D;
+        store_out<KV>(p.out, (size_t(b) * p.Hq + h) * D + i % D, 0.f);
+        if (p.lse && i % D == 0) p.lse[size_t(b) * p.Hq + h] = -INFINITY;
+      }
+    }
+    return;
+  }
+  const int j0 = s * T;
+  const int nblk = min(nAB, j0 + T) - j0;
+  const int last_tokens = min(kBlk, A - kBlk * (nAB - 1));  // tokens in the final alive block
+
+  // ---- expand this split's segments into per-block physical ids ----------
+  const int sf = wg_search_segment(p.segs, s0, s1, j0 * kBlk);
+  const int ns = min(nblk, s1 - sf);
+  int32_t* st_start = reinterpret_cast<int32_t*>(&k_lds[0][0]);
+  int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
+  int32_t* st_nblk = st_phys + kMaxSplitBlocks + 1;
+  for (int i = tid; i < ns; i += kThreads) {
+    const msa_segment sg = p.segs[sf + i];
+    st_start[i] = sg.alive_token_start / kBlk;
+    // the plan never emits a segment outside the pool; a foreign one is dropped
+    const bool in_pool = sg.phys_block >= 0 && sg.num_blocks >= 0 &&
+                         int64_t(sg.phys_block) + sg.num_blocks <= p.P;
+    st_phys[i] = in_pool ? sg.phys_block : -1;
+    st_nblk[i] = in_pool ? sg.num_blocks : 0;
+  }
+  {  // this KV head's G query rows -> LDS (contiguous G*ROW bytes)
+    const uint8_t* qsrc = static_cast<const uint8_t*>(p.q) + (size_t(b) * p.Hq + size_t(g) * G) * ROW;
+    for (int i = tid; i < G * CH; i += kThreads)
+      *reinterpret_cast<uint4*>(q_lds + i * 16) = *reinterpret_cast<const uint4*>(qsrc + i * 16);
+  }
+  __syncthreads();
+  for (int jj = tid; jj < nblk; jj += kThreads) {
+    const int j = j0 + jj;
+    int lo = 0, hi = ns;  // largest i with st_start[i] <= j
+    while (hi - lo > 1) {
+      const int mid = (lo + hi) >> 1;
+      if (st_start[mid] <= j) lo = mid; else hi = mid;
+    }
+    const int off = j - st_start[lo];
+    blk_phys[jj] = (st_phys[lo] >= 0 && off >= 0 && off < st_nblk[lo]) ? st_phys[lo] + off : -1;
+  }
+  __syncthreads();
+
+  // ---- main loop: one 64-token tile per wavefront per iteration ----------
+  const char* kbase = static_cast<const char*>(p.k_pool) + size_t(g) * ROW;
+  const char* vbase = static_cast<const char*>(p.v_pool) + size_t(g) * ROW;
+  const size_t tok_stride = size_t(p.Hkv) * ROW;  // bytes between slots
+  uint8_t* kt = &k_lds[w][0];
+
+  float m_run[G], l_lane[G], o[G][EPL];
+#pragma unroll
+  for (int h = 0; h < G; ++h) {
+    m_run[h] = -INFINITY;
+    l_lane[h] = 0.f;
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+  }
+
+  const int ntiles = (nblk + 3) / 4;
+  for (int ti = w; ti < ntiles; ti += kNW) {
+    const int jb = ti * 4;
+    // K: chunk c*64+lane of the tile = row r, 16-byte chunk ch
+    uint4 kreg[GE::KLOADS];
+#pragma unroll
+    for (int c = 0; c < GE::KLOADS; ++c) {
+      const int id = c * kWave + lane;
+      const int r = id / CH, ch = id % CH;
+      const int jj = jb + r / kBlk;
+      const int ph = jj < nblk ? blk_phys[jj] : -1;
+      kreg[c] = make_uint4(0, 0, 0, 0);
+      if (ph >= 0)
+        kreg[c] = *reinterpret_cast<const uint4*>(kbase + (size_t(ph) * kBlk + r % kBlk) * tok_stride + ch * 16);
+    }
+    // V: row t*RPL + lane/LPR, dword lane%LPR
+    uint32_t vreg[GE::VLOADS];
+#pragma unroll
+    for (int t = 0; t < GE::VLOADS; ++t) {
+      const int r = t * RPL + lane / LPR;
+      const int jj = jb + r / kBlk, slot = r % kBlk;
+      const int ph = jj < nblk ? blk_phys[jj] : -1;
+      const bool ok = ph >= 0 && (j0 + jj != nAB - 1 || slot < last_tokens);
+      uint32_t x = 0;
+      if (ph >= 0)
+        x = *reinterpret_cast<const uint32_t*>(vbase + (size_t(ph) * kBlk + slot) * tok_stride + (lane % LPR) * 4);
+      vreg[t] = ok ? x : 0u;
+    }
+#pragma unroll
+    for (int c = 0; c < GE::KLOADS; ++c) {
+      const int id = c * kWave + lane;
+      const int r = id / CH, ch = id % CH;
+      *reinterpret_cast<uint4*>(kt + r * ROW + ((ch ^ (r % SW)) * 16)) = kreg[c];
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // scores: one token per lane.  The query rows are re-read from LDS
+    // (broadcast) every tile: an opaque offset keeps the compiler from
+    // hoisting G*D loop-invariant values into registers.
+    int qoff = 0;
+    asm volatile("" : "+v"(qoff));
+    const uint8_t* qt = q_lds + qoff;
+    float sc[G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) sc[h] = 0.f;
+    {
+      const int r = lane;
+#pragma unroll 2
+      for (int c = 0; c < CH; ++c) {
+        const uint4 kc = *reinterpret_cast<const uint4*>(kt + r * ROW + ((c ^ (r % SW)) * 16));
+#pragma unroll
+        for (int h = 0; h < G; ++h) {
+          const uint4 qc = *reinterpret_cast<const uint4*>(qt + h * ROW + c * 16);
+          sc[h] = dot_chunk(qc, kc, sc[h], KV());
+        }
+      }
+      const int jj = jb + r / kBlk, slot = r % kBlk;
+      const int ph = jj < nblk ? blk_phys[jj] : -1;
+      const bool ok = ph >= 0 && (j0 + jj != nAB - 1 || slot < last_tokens);
+#pragma unroll
+      for (int h = 0; h < G; ++h) sc[h] = ok ? sc[h] * p.scale_log2 : -INFINITY;
+    }
+
+    // online softmax (log2 units)
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float m_new = fmaxf(m_run[h], wave_max(sc[h]));
+      float alpha = 1.f, pw = 0.f;
+      if (m_new != -INFINITY) {
+        alpha = exp2f(m_run[h] - m_new);
+        pw = exp2f(sc[h] - m_new);
+      }
+      m_run[h] = m_new;
+      l_lane[h] = l_lane[h] * alpha + pw;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
+      p_lds[w][lane][h] = pw;
+    }
+    __builtin_amdgcn_wave_barrier();
+
+    // PV: lane owns EPL elements of D for all G heads
+#pragma unroll
+    for (int t = 0; t < GE::VLOADS; ++t) {
+      const int r = t * RPL + lane / LPR;
+      float v[EPL];
+      unpack_v<KV>(vreg[t], v);
+      float pw[G];
+#pragma unroll
+      for (int h = 0; h < G; ++h) pw[h] = p_lds[w][r][h];
+#pragma unroll
+      for (int h = 0; h < G; ++h)
+#pragma unroll
+        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(pw[h], v[e], o[h][e]);
+    }
+    __builtin_amdgcn_wave_barrier();
+  }
+
+  // ---- merge the 4 wavefront states --------------------------------------
+  float l_w[G];
+#pragma unroll
+  for (int h = 0; h < G; ++h) l_w[h] = wave_sum(l_lane[h]);
+  if constexpr (RPL == 2) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) o[h][e] += __shfl_xor(o[h][e], 32);
+  }
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(&k_lds[0][0]);  // [kNW][G][D]
+  float* mm = mo + kNW * G * D;                        // [kNW][G]
+  float* ml = mm + kNW * G;
+  if (lane < LPR) {
+#pragma unroll
+    for (int h = 0; h < G; ++h)
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) mo[(w * G + h) * D + lane * EPL + e] = o[h][e];
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      mm[w * G + h] = m_run[h];
+      ml[w * G + h] = l_w[h];
+    }
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int hh = i / D, d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kNW; ++k) M = fmaxf(M, mm[k * G + hh]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < kNW; ++k) {
+        const float mk = mm[k * G + hh];
+        const float wt = mk == -INFINITY ? 0.f : exp2f(mk - M);
+        L = fmaf(wt, ml[k * G + hh], L);
+        O = fmaf(wt, mo[(k * G + hh) * D + d], O);
+      }
+    }
+    const int h = g * G + hh;
+    if (Sb == 1) {
+      store_out<KV>(p.out, (size_t(b) * p.Hq + h) * D + d, L > 0.f ? O / L : 0.f);
+      if (p.lse && d == 0) p.lse[size_t(b) * p.Hq + h] = L > 0.f ? (M + log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      const size_t n = size_t(b) * p.S + s;
+      p.o_part[(n * p.Hq + h) * D + d] = O;
+      if (d == 0) {
+        p.m_part[n * p.Hq + h] = M == -INFINITY ? -INFINITY : M * kLn2;
+        p.l_part[n * p.Hq + h] = L;
+      }
+    }
+  }
+}
+
+template <typename KV, int D, int G>
+hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
+  dim3 grid(p.S, p.Hkv, p.B);
+  hipLaunchKernelGGL((decode_kernel<KV, D, G>), grid, dim3(kThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+template <typename KV, int D>
+hipError_t launch_g(const DecodeParams& p, hipStream_t stream) {
+  switch (p.Hq / p.Hkv) {
+    case 1: return launch_t<KV, D, 1>(p, stream);
+    case 2: return launch_t<KV, D, 2>(p, stream);
+    case 4: return launch_t<KV, D, 4>(p, stream);
+    case 8: return launch_t<KV, D, 8>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+bool decode_supported(msa_dtype dtype, int32_t D, int32_t G) {
+  const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
+  if (dtype == MSA_BF16) return g_ok && (D == 64 || D == 128);
+  if (dtype == MSA_F32) return g_ok && D == 64;
+  return false;
+}
+
+SplitPlan decode_split(int32_t B, int32_t Hkv, int32_t max_ctx_len, int32_t block_size,
+                       int32_t split_blocks) {
+  SplitPlan sp;
+  const int64_t nbm = (int64_t(max_ctx_len) + block_size - 1) / block_size;
+  int64_t T = split_blocks;
+  if (T <= 0) {
+    // aim for ~1024 workgroups (4 per CU on a 256-CU part) without splits
+    // shorter than 16 blocks (4 tiles per wavefront)
+    const int64_t pairs = int64_t(B) * Hkv;
+    int64_t S = (1024 + pairs - 1) / pairs;
+    T = (nbm + S - 1) / S;
+    T = ((T + 15) / 16) * 16;
+    if (T < 16) T = 16;
+    if (T > kMaxSplitBlocks) T = kMaxSplitBlocks;
+  }
+  sp.split_blocks = int32_t(T);
+  sp.S = int32_t(nbm == 0 ? 1 : (nbm + T - 1) / T);
+  return sp;
+}
+
+int32_t decode_max_split_blocks() { return kMaxSplitBlocks; }
+
+hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
+  if (p.dtype == MSA_BF16) {
+    if (p.D == 128) return launch_g<uint16_t, 128>(p, stream);
+    if (p.D == 64) return launch_g<uint16_t, 64>(p, stream);
+  } else if (p.dtype == MSA_F32) {
+    if (p.D == 64) return launch_g<float, 64>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace msa

@@ -1,0 +1,248 @@
+// a1: segment plan on the device.
+//
+// split_into_contiguous_segments (P1, "Core method 1: MSA" pseudocode and the
+// paragraph after it): the alive blocks of each sequence are cut into
+// maximal runs that are consecutive both in logical index and in physical
+// id; the hole an evicted block leaves always breaks a run.
+//
+// Two launches, one workgroup per sequence each:
+//   count  -- number of segment starts per sequence + data-error flags
+//   write  -- prefix of the counts -> seg_indptr; every block that ENDS a
+//             run writes that run's whole record, so each record has exactly
+//             one writer and no cross-workgroup coordination is needed.
+// A block l "is alive" iff alive[b][l] != 0 and its physical id is in
+// [0, P); an out-of-range id is reported and the block treated as evicted,
+// so no consumer of the plan can be sent outside the pool.
+#include "msa_internal.h"
+
+namespace msa {
+namespace {
+
+constexpr int kPlanThreads = 256;
+constexpr int kPerThread = 4;  // consecutive blocks per thread per chunk
+constexpr int kChunk = kPlanThreads * kPerThread;
+
+struct SeqView {
+  const int32_t* trow;
+  const uint8_t* arow;
+  int32_t n_tok;
+  int32_t nb;
+};
+
+__device__ __forceinline__ SeqView seq_view(const PlanParams& p, int b, int& flags) {
+  SeqView v;
+  v.trow = p.table + size_t(b) * p.max_blocks;
+  v.arow = p.alive + size_t(b) * p.max_blocks;
+  int32_t n = p.ctx_len[b];
+  const int32_t lim = p.max_blocks * p.bs;  // host checked it fits in int32
+  if (n < 0 || n > lim) {
+    flags |= MSA_DEVERR_CTX_RANGE;
+    n = n < 0 ? 0 : lim;
+  }
+  v.n_tok = n;
+  v.nb = (n + p.bs - 1) / p.bs;
+  return v;
+}
+
+// alive-and-valid predicate; phys is meaningful only when it returns true
+__device__ __forceinline__ bool live(const PlanParams& p, const SeqView& v, int l, int32_t& phys,
+                                     int& flags) {
+  if (l < 0 || l >= v.nb || v.arow[l] == 0) return false;
+  const int32_t ph = v.trow[l];
+  if (ph < 0 || ph >= p.P) {
+    flags |= MSA_DEVERR_PHYS_RANGE;
+    return false;
+  }
+  phys = ph;
+  return true;
+}
+
+__device__ __forceinline__ int block_sum_int(int x, int* red) {
+  // wave reduce with shuffles, then across the 4 waves through LDS
+  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = x;
+  __syncthreads();
+  int t = 0;
+  for (int i = 0; i < kPlanThreads / kWave; ++i) t += red[i];
+  return t;
+}
+
+__device__ __forceinline__ int block_or_int(int x, int* red) {
+  for (int o = 32; o > 0; o >>= 1) x |= __shfl_xor(x, o);
+  const int w = threadIdx.x / kWave;
+  __syncthreads();
+  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = x;
+  __syncthreads();
+  int t = 0;
+  for (int i = 0; i < kPlanThreads / kWave; ++i) t |= red[i];
+  return t;
+}
+
+__global__ void __launch_bounds__(kPlanThreads) plan_count_kernel(PlanParams p) {
+  __shared__ int red[kPlanThreads / kWave];
+  const int b = blockIdx.x;
+  int flags = 0;
+  const SeqView v = seq_view(p, b, flags);
+  int starts = 0;
+  for (int l = threadIdx.x; l < v.nb; l += kPlanThreads) {
+    int32_t ph = 0, pp = 0;
+    if (live(p, v, l, ph, flags)) {
+      int dummy = 0;  // the previous block's flags are counted by its own thread
+      const bool cont = live(p, v, l - 1, pp, dummy) && pp + 1 == ph;
+      starts += cont ? 0 : 1;
+    }
+  }
+  const int total = block_sum_int(starts, red);
+  const int f = block_or_int(flags, red);
+  if (threadIdx.x == 0) {
+    p.ws[b] = total;
+    p.ws[p.B + b] = f;
+  }
+}
+
+// Inclusive block scan of three values: two sums and a max.
+struct Scan3 {
+  int a, t, m;
+};
+
+__device__ __forceinline__ Scan3 block_exclusive_scan3(Scan3 v, Scan3* lds, Scan3& total) {
+  const int lane = threadIdx.x & (kWave - 1);
+  const int w = threadIdx.x / kWave;
+  Scan3 inc = v;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int a = __shfl_up(inc.a, o), t = __shfl_up(inc.t, o), m = __shfl_up(inc.m, o);
+    if (lane >= o) {
+      inc.a += a;
+      inc.t += t;
+      inc.m = max(inc.m, m);
+    }
+  }
+  __syncthreads();
+  if (lane == kWave - 1) lds[w] = inc;
+  __syncthreads();
+  Scan3 pre = {0, 0, -1};
+  total = {0, 0, -1};
+  for (int i = 0; i < kPlanThreads / kWave; ++i) {
+    const Scan3 s = lds[i];
+    if (i < w) {
+      pre.a += s.a;
+      pre.t += s.t;
+      pre.m = max(pre.m, s.m);
+    }
+    total.a += s.a;
+    total.t += s.t;
+    total.m = max(total.m, s.m);
+  }
+  // exclusive = prefix of earlier waves + inclusive within wave - own value;
+  // the max part is kept inclusive-of-earlier-lanes only.
+  Scan3 ex;
+  ex.a = pre.a + inc.a - v.a;
+  ex.t = pre.t + inc.t - v.t;
+  const int prev_m = __shfl_up(inc.m, 1);
+  ex.m = max(pre.m, lane > 0 ? prev_m : -1);
+  return ex;
+}
+
+__global__ void __launch_bounds__(kPlanThreads) plan_write_kernel(PlanParams p) {
+  __shared__ int red[kPlanThreads / kWave];
+  __shared__ Scan3 scan_lds[kPlanThreads / kWave];
+  const int b = blockIdx.x;
+
+  // offset of this sequence's records; workgroup 0 also publishes the totals
+  int before = 0, all = 0, fl = 0;
+  for (int i = threadIdx.x; i < p.B; i += kPlanThreads) {
+    const int c = p.ws[i];
+    if (i < b) before += c;
+    all += c;
+    fl |= p.ws[p.B + i];
+  }
+  const int off = block_sum_int(before, red);
+  const int count_b = p.ws[b];
+  if (threadIdx.x == 0) p.indptr[b + 1] = min(off + count_b, p.cap);
+  if (b == 0) {
+    const int total = block_sum_int(all, red);
+    const int flags = block_or_int(fl, red);
+    if (threadIdx.x == 0) {
+      p.indptr[0] = 0;
+      p.dev_error[0] = flags | (total > p.cap ? MSA_DEVERR_CAPACITY : 0);
+    }
+  }
+
+  int dummy = 0;  // flags were gathered by the count pass
+  const SeqView v = seq_view(p, b, dummy);
+  Scan3 carry = {0, 0, -1};
+  for (int base = 0; base < v.nb; base += kChunk) {
+    const int l0 = base + threadIdx.x * kPerThread;
+    bool a[kPerThread];
+    int32_t ph[kPerThread];
+    int tok[kPerThread];
+    bool st[kPerThread];
+    int32_t prev_ph = 0;
+    bool prev_a = live(p, v, l0 - 1, prev_ph, dummy);
+    Scan3 mine = {0, 0, -1};
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      const int l = l0 + k;
+      ph[k] = 0;
+      a[k] = live(p, v, l, ph[k], dummy);
+      st[k] = a[k] && !(prev_a && prev_ph + 1 == ph[k]);
+      tok[k] = a[k] ? min(p.bs, v.n_tok - l * p.bs) : 0;
+      mine.a += st[k] ? 1 : 0;
+      mine.t += tok[k];
+      if (st[k]) mine.m = l;
+      prev_a = a[k];
+      prev_ph = ph[k];
+    }
+    int32_t next_ph = 0;
+    const bool next_a = live(p, v, l0 + kPerThread, next_ph, dummy);
+
+    Scan3 total;
+    const Scan3 ex = block_exclusive_scan3(mine, scan_lds, total);
+    int run_cnt = carry.a + ex.a;
+    int run_tok = carry.t + ex.t;
+    int run_start = max(carry.m, ex.m);
+#pragma unroll
+    for (int k = 0; k < kPerThread; ++k) {
+      run_cnt += st[k] ? 1 : 0;
+      run_tok += tok[k];
+      if (st[k]) run_start = l0 + k;
+      if (!a[k]) continue;
+      const bool nxt_a = (k + 1 < kPerThread) ? a[k + 1] : next_a;
+      const int32_t nxt_ph = (k + 1 < kPerThread) ? ph[k + 1] : next_ph;
+      const bool ends = !(nxt_a && nxt_ph == ph[k] + 1);
+      if (!ends) continue;
+      const int l = l0 + k;
+      const int nblk = l - run_start + 1;
+      const int ntok = (nblk - 1) * p.bs + tok[k];
+      const int rec = off + run_cnt - 1;
+      if (rec < p.cap) {
+        msa_segment s;
+        s.seq = b;
+        s.logical_block = run_start;
+        s.phys_block = ph[k] - (nblk - 1);
+        s.num_blocks = nblk;
+        s.num_tokens = ntok;
+        s.alive_token_start = run_tok - ntok;
+        p.segs[rec] = s;
+      }
+    }
+    carry.a += total.a;
+    carry.t += total.t;
+    carry.m = max(carry.m, total.m);
+    __syncthreads();
+  }
+}
+
+}  // namespace
+
+hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
+  hipLaunchKernelGGL(plan_count_kernel, dim3(p.B), dim3(kPlanThreads), 0, stream, p);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(plan_write_kernel, dim3(p.B), dim3(kPlanThreads), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace msa

@@ -1,0 +1,109 @@
+"""The C-ABI library: it loads, exports every function include/msa.h declares,
+and rejects bad arguments on the host before touching the GPU (these calls
+return before any HIP runtime call, so they run without a GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from kv_cache_attention_msa_amd import _lib
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "msa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH), reason="libmsa.so not built")
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", src)))
+
+
+def test_header_declares_the_four_calls():
+    names = declared_functions()
+    for n in ("msa_plan_segments", "msa_decode", "msa_prefill_chunk", "msa_merge_partials"):
+        assert n in names
+
+
+def test_every_declared_symbol_is_exported():
+    lib = _lib.load()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert set(declared_functions()) == set(_lib.SIGNATURES)
+
+
+def test_version_and_strings():
+    lib = _lib.load()
+    assert lib.msa_version() == 1
+    assert b"INVALID" in lib.msa_status_string(-1)
+
+
+NULL = None
+FAKE = ctypes.c_void_p(0x1000)  # never dereferenced: validation fails first
+
+
+def test_plan_rejects_bad_args():
+    lib = _lib.load()
+    ws = lib.msa_plan_workspace_size(4)
+    assert ws >= 32
+    # null table
+    assert lib.msa_plan_segments(NULL, FAKE, FAKE, 4, 8, 16, 100, FAKE, 32, FAKE, FAKE, FAKE, ws, NULL) == _lib.MSA_ERR_INVALID_ARG
+    # B = 0
+    assert lib.msa_plan_segments(FAKE, FAKE, FAKE, 0, 8, 16, 100, FAKE, 32, FAKE, FAKE, FAKE, ws, NULL) == _lib.MSA_ERR_INVALID_ARG
+    # null dev_error
+    assert lib.msa_plan_segments(FAKE, FAKE, FAKE, 4, 8, 16, 100, FAKE, 32, FAKE, NULL, FAKE, ws, NULL) == _lib.MSA_ERR_INVALID_ARG
+    # workspace too small
+    assert lib.msa_plan_segments(FAKE, FAKE, FAKE, 4, 8, 16, 100, FAKE, 32, FAKE, FAKE, FAKE, ws - 1, NULL) == _lib.MSA_ERR_CAPACITY
+    # max_blocks * block_size overflows int32
+    assert lib.msa_plan_segments(FAKE, FAKE, FAKE, 4, 1 << 20, 1 << 12, 100, FAKE, 32, FAKE, FAKE, FAKE, ws, NULL) == _lib.MSA_ERR_INVALID_ARG
+
+
+def _decode(lib, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, P=100, bs=16, segs=FAKE, indptr=FAKE, B=2, Hq=32, Hkv=8, D=128,
+             maxctx=4096, dtype=_lib.MSA_BF16, scale=0.0, split=0, out=FAKE, lse=NULL, ws=FAKE,
+             wsb=1 << 30, stream=NULL)
+    a.update(kw)
+    return lib.msa_decode(a["q"], a["k"], a["v"], a["P"], a["bs"], a["segs"], a["indptr"], a["B"],
+                          a["Hq"], a["Hkv"], a["D"], a["maxctx"], a["dtype"], a["scale"], a["split"],
+                          a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_decode_rejects_bad_args():
+    lib = _lib.load()
+    assert _decode(lib, q=NULL) == _lib.MSA_ERR_INVALID_ARG
+    assert _decode(lib, Hq=30) == _lib.MSA_ERR_INVALID_ARG          # Hq % Hkv
+    assert _decode(lib, B=0) == _lib.MSA_ERR_INVALID_ARG
+    assert _decode(lib, split=-1) == _lib.MSA_ERR_INVALID_ARG
+    assert _decode(lib, scale=float("nan")) == _lib.MSA_ERR_INVALID_ARG
+    assert _decode(lib, bs=32) == _lib.MSA_ERR_UNSUPPORTED
+    assert _decode(lib, D=96) == _lib.MSA_ERR_UNSUPPORTED
+    assert _decode(lib, Hq=24) == _lib.MSA_ERR_UNSUPPORTED          # G = 3
+    assert _decode(lib, dtype=_lib.MSA_F32, D=128) == _lib.MSA_ERR_UNSUPPORTED
+    assert _decode(lib, dtype=7) == _lib.MSA_ERR_UNSUPPORTED
+    assert _decode(lib, split=100000) == _lib.MSA_ERR_INVALID_ARG
+    need = lib.msa_decode_workspace_size(2, 32, 8, 128, 4096, 16, 0)
+    assert need > 0
+    assert _decode(lib, wsb=need - 1) == _lib.MSA_ERR_CAPACITY
+    assert _decode(lib, ws=NULL) == _lib.MSA_ERR_CAPACITY
+
+
+def test_decode_workspace_arithmetic():
+    lib = _lib.load()
+    # one split covers the context -> no workspace at all
+    assert lib.msa_decode_workspace_size(1, 8, 2, 64, 1024, 16, 64) == 0
+    # explicit split: B*S partials of Hq*(D+2) floats (each array 256-B aligned)
+    B, Hq, D, ctx, T = 3, 32, 128, 4096, 32
+    S = -(-(ctx // 16) // T)
+    want = 0
+    for n in (B * S * Hq * D, B * S * Hq, B * S * Hq):
+        want += -(-n * 4 // 256) * 256
+    assert lib.msa_decode_workspace_size(B, Hq, 8, D, ctx, 16, T) == want
+
+
+def test_merge_rejects_bad_args():
+    lib = _lib.load()
+    assert lib.msa_merge_partials(NULL, FAKE, FAKE, FAKE, 1, 1, 1, 64, _lib.MSA_F32, FAKE, NULL, NULL) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_merge_partials(FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 64, _lib.MSA_F32, FAKE, NULL, NULL) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_merge_partials(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 9, FAKE, NULL, NULL) == _lib.MSA_ERR_UNSUPPORTED

@@ -136,11 +136,17 @@ def _place_runs_with_gaps(rng, run_sizes, pool_blocks):
 # value fill
 # ----------------------------------------------------------------------------
 
+_VALUES = {"on": True}
+
+
 def _fill_pools_and_q(rng, dtype, q_shape, P, bs, Hkv, D, live_slots):
     """Draw Q, then the K pool, then the V pool, N(0,1); poison dead slots.
 
     live_slots: bool [P, bs], True where an alive token lives.
     """
+    if not _VALUES["on"]:
+        shape = (P, bs, Hkv, D)
+        return None, np.empty((shape[0], 0), np.float32), None
     q = rng.standard_normal(q_shape, dtype=np.float32)
     pools = []
     dead = ~live_slots
@@ -156,6 +162,8 @@ def _fill_pools_and_q(rng, dtype, q_shape, P, bs, Hkv, D, live_slots):
 
 def _live_slots(P, bs, block_table, alive, ctx_len):
     live = np.zeros((P, bs), dtype=bool)
+    if not _VALUES["on"]:
+        return live
     B = block_table.shape[0]
     for b in range(B):
         nb = -(-int(ctx_len[b]) // bs)
@@ -341,11 +349,14 @@ SMALL = {
 }
 
 
-def make_workload(cfg: int, seed: int = 0, size: str = "full", **overrides) -> Workload:
+def make_workload(cfg: int, seed: int = 0, size: str = "full", values: bool = True,
+                  **overrides) -> Workload:
     """Draw workload family ``cfg`` (1..5) with ``seed``.
 
     size="full" uses the family's defining sizes, "small" the reduced ones;
-    keyword overrides change individual shape parameters.
+    keyword overrides change individual shape parameters.  values=False skips
+    the Q/K/V draw (they come last, so the tables are the same either way):
+    q and v_pool are then None and k_pool is an empty [P, 0] placeholder.
     """
     fn = _FAMILIES[cfg]
     kw = {}
@@ -355,7 +366,11 @@ def make_workload(cfg: int, seed: int = 0, size: str = "full", **overrides) -> W
         raise ValueError(size)
     kw.update(overrides)
     rng = np.random.default_rng(seed)
-    d = fn(rng, **kw)
+    _VALUES["on"] = values
+    try:
+        d = fn(rng, **kw)
+    finally:
+        _VALUES["on"] = True
     D = d["D"]
     w = Workload(name=NAMES[cfg] if size == "full" and not overrides else f"{NAMES[cfg]}[{size}]",
                  scale=1.0 / math.sqrt(D), **d)
