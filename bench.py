@@ -1,0 +1,335 @@
+#!/usr/bin/env python3
+"""Benchmark of the MSA hot path on one MI355X.
+
+One step = one pass of the whole decode hot path over one batch: the segment
+plan (msa_plan_segments) followed by decode attention with its split-K merge
+(msa_decode), on the headline decode workload (bf16, batch 32, 32 q / 8 KV
+heads, head_dim 128, 4096-token contexts, block size 16, 20% of blocks evicted
+in geometric runs).  Inputs are resident in HBM before the timed region.
+
+Printed: ONE JSON line with the decode KV GB/s (value), tokens/s, % of HBM
+peak, a roofline object for the dominant call (measured live with HIP events
+on the launch stream), the fp64 oracle timed on the host cores
+(cpu_baseline), cold-cache timing, and the chunked-prefill TFLOP/s / % of bf16
+MFMA peak on the prefill workload (bf16, batch 4, chunk 512 over 8192 cached
+tokens, 15% evicted).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "MSA decode KV GB/s (% HBM peak) + tokens/s; prefill-chunk TFLOP/s (% MFMA)"
+HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
+MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
+COUNTERS = os.path.join(ROOT, "profiles", "decode_cfg2_counters.json")
+DECODE_SOURCES = ["decode.hip", "merge.hip", "msa_internal.h"]
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--split-blocks", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for counter calibration)")
+    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
+                    help="time only one call (for profiler runs)")
+    return ap.parse_args()
+
+
+def sources_sha(names):
+    h = hashlib.sha256()
+    for n in names:
+        with open(os.path.join(ROOT, "kv_cache_attention_msa_amd", "csrc", n), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def alive_tokens_per_seq(w):
+    """Number of alive tokens per sequence (input bookkeeping for byte counts)."""
+    import numpy as np
+    out = []
+    for b in range(w.B):
+        n = int(w.ctx_len[b])
+        nb = -(-n // w.block_size)
+        tok = np.minimum(w.block_size, n - w.block_size * np.arange(nb))
+        out.append(int((tok * (w.alive[b, :nb] != 0)).sum()))
+    return out
+
+
+def visible_pairs(w):
+    """(query row, key) pairs with key position <= row position, over alive keys."""
+    import numpy as np
+    tot = 0
+    for b in range(w.B):
+        n = int(w.ctx_len[b])
+        pos = np.arange(n)
+        keep = w.alive[b, pos // w.block_size] != 0
+        kpos = pos[keep]
+        qpos = int(w.q_pos0[b]) + np.arange(w.C)
+        tot += int(np.searchsorted(kpos, qpos, side="right").sum())
+    return tot
+
+
+class Prepared:
+    """Device buffers and pre-marshalled C-ABI arguments for one workload, so
+    the timed loops make the library calls with no allocation and no
+    per-call argument building."""
+
+    def __init__(self, w, split_blocks=0):
+        import ctypes
+        import torch
+        from kv_cache_attention_msa_amd import _lib
+        from workloads.device import to_device
+        self.lib = _lib.load()
+        self.w = w
+        d = to_device(w, "cuda")
+        self.d = d
+        dev = d["q"].device
+        B, mb = w.block_table.shape
+        self.cap = B * mb
+        self.segs = torch.empty((self.cap, 6), dtype=torch.int32, device=dev)
+        self.indptr = torch.empty(B + 1, dtype=torch.int32, device=dev)
+        self.err = torch.zeros(1, dtype=torch.int32, device=dev)
+        self.pws = torch.empty(max(1, int(self.lib.msa_plan_workspace_size(B))), dtype=torch.uint8, device=dev)
+        self.out = torch.empty_like(d["q"])
+        lse_shape = (B, w.Hq) if w.kind == "decode" else (B, w.C, w.Hq)
+        self.lse = torch.empty(lse_shape, dtype=torch.float32, device=dev)
+        self.max_ctx = int(w.ctx_len.max())
+        if w.kind == "decode":
+            wsb = int(self.lib.msa_decode_workspace_size(B, w.Hq, w.Hkv, w.D, self.max_ctx, 16, split_blocks))
+        else:
+            wsb = int(self.lib.msa_prefill_workspace_size(B, w.C, w.Hq, w.Hkv, w.D, self.max_ctx, 16, split_blocks))
+        self.ws = torch.empty(max(1, wsb), dtype=torch.uint8, device=dev)
+        self.stream = torch.cuda.current_stream()
+        P = ctypes.c_void_p
+        s = P(self.stream.cuda_stream)
+        dt = _lib.MSA_BF16 if w.dtype == "bf16" else _lib.MSA_F32
+        self.plan_args = (P(d["block_table"].data_ptr()), P(d["alive"].data_ptr()), P(d["ctx_len"].data_ptr()),
+                          B, mb, w.block_size, w.num_phys_blocks, P(self.segs.data_ptr()), self.cap,
+                          P(self.indptr.data_ptr()), P(self.err.data_ptr()), P(self.pws.data_ptr()),
+                          self.pws.numel(), s)
+        if w.kind == "decode":
+            self.attn = self.lib.msa_decode
+            self.attn_args = (P(d["q"].data_ptr()), P(d["k_pool"].data_ptr()), P(d["v_pool"].data_ptr()),
+                              w.num_phys_blocks, w.block_size, P(self.segs.data_ptr()), P(self.indptr.data_ptr()),
+                              B, w.Hq, w.Hkv, w.D, self.max_ctx, dt, float(w.scale), split_blocks,
+                              P(self.out.data_ptr()), P(self.lse.data_ptr()), P(self.ws.data_ptr()),
+                              self.ws.numel(), s)
+        else:
+            self.attn = self.lib.msa_prefill_chunk
+            self.attn_args = (P(d["q"].data_ptr()), w.C, P(d["q_pos0"].data_ptr()), P(d["k_pool"].data_ptr()),
+                              P(d["v_pool"].data_ptr()), w.num_phys_blocks, w.block_size,
+                              P(self.segs.data_ptr()), P(self.indptr.data_ptr()), B, w.Hq, w.Hkv, w.D,
+                              self.max_ctx, dt, float(w.scale), split_blocks, P(self.out.data_ptr()),
+                              P(self.lse.data_ptr()), P(self.ws.data_ptr()), self.ws.numel(), s)
+
+    def plan(self):
+        st = self.lib.msa_plan_segments(*self.plan_args)
+        if st != 0:
+            raise RuntimeError(f"msa_plan_segments failed: {st}")
+
+    def attention(self):
+        st = self.attn(*self.attn_args)
+        if st != 0:
+            raise RuntimeError(f"attention call failed: {st}")
+
+    def step(self):
+        self.plan()
+        self.attention()
+
+
+def time_calls(fn, n, stream):
+    """Average duration of fn() over n back-to-back calls, from HIP events
+    recorded on the launch stream."""
+    import torch
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(n):
+        fn()
+    e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) / n * 1e-3  # seconds
+
+
+def time_cold(fn, n, stream, flush):
+    """Median duration of fn() when a 1 GiB read evicts L2 and the Infinity
+    Cache before every call (the read is outside the events; a read leaves
+    clean lines, so the call pays no write-back of the flush)."""
+    import torch
+    ts = []
+    sink = torch.empty((), dtype=torch.float32, device=flush.device)
+    for _ in range(n):
+        torch.sum(flush, dim=0, out=sink)
+        e0 = torch.cuda.Event(enable_timing=True)
+        e1 = torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        fn()
+        e1.record(stream)
+        e1.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e-3)
+    return statistics.median(ts)
+
+
+def cpu_baseline(w, bytes_per_pass, budget_s=10.0, max_reps=20):
+    """The fp64 oracle, as it stands, on the same decode workload."""
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps:
+        oracle.decode_ref(w.q, w.k_pool, w.v_pool, w.block_table, w.alive, w.ctx_len,
+                          w.block_size, w.scale)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(bytes_per_pass * reps / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle (decode_ref) over the full headline decode batch "
+                      f"({w.B} sequences x {w.Hq} heads), {reps} passes in {dt:.1f} s; "
+                      f"BLAS threads {threads}, gathering single-threaded",
+            "seconds_per_pass": round(dt / reps, 4)}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not supported "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE={world}).", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from workloads import make_workload, NAMES
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    result = {}
+    # ---------------------------------------------------------------- decode
+    if args.only in (None, "decode"):
+        w = make_workload(2, seed=args.seed)
+        prep = Prepared(w, args.split_blocks)
+        esz = 2 if w.dtype == "bf16" else 4
+        alive = alive_tokens_per_seq(w)
+        kv_bytes = sum(alive) * w.Hkv * w.D * 2 * esz
+        qo_bytes = 2 * w.B * w.Hq * w.D * esz + w.B * w.Hq * 4
+        alg_bytes = kv_bytes + qo_bytes
+        stream = prep.stream
+        for _ in range(args.warmup):
+            prep.step()
+        torch.cuda.synchronize()
+        err = int(prep.err.item())
+        nseg = int(prep.indptr[-1].item())
+        if err != 0:
+            raise RuntimeError(f"plan reported device error {err}")
+        # contract timing: K whole steps bracketed by synchronize
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(args.steps):
+            prep.step()
+        torch.cuda.synchronize()
+        step_s = (time.perf_counter() - t0) / args.steps
+        # dominant call: msa_decode (decode kernel + its split merge), HIP events
+        dec_s = time_calls(prep.attention, args.steps, stream)
+        plan_s = time_calls(prep.plan, args.steps, stream)
+        value = alg_bytes / step_s / 1e9
+        achieved = alg_bytes / dec_s / 1e9
+        traffic = None
+        if os.path.exists(COUNTERS):
+            c = json.load(open(COUNTERS))
+            if c.get("sources_sha") == sources_sha(DECODE_SOURCES) and c.get("split_blocks", 0) == args.split_blocks:
+                traffic = c.get("bytes_per_call")
+        result.update({
+            "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+            "data": "synthetic",
+            "config": {"workload": NAMES[2], "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
+                       "head_dim": w.D, "ctx_len": int(w.ctx_len[0]), "block_size": w.block_size,
+                       "evicted_fraction": round(w.meta["evicted_fraction"], 4),
+                       "alive_tokens": int(sum(alive)), "segments": nseg,
+                       "step": "msa_plan_segments + msa_decode (decode kernel + split-K merge)",
+                       "seed": args.seed, "parallelism": "single GPU"},
+            "tokens_per_s": round(w.B / step_s, 1),
+            "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
+                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                         "traffic": traffic,
+                         "kernel": "msa_decode = decode_kernel<bf16,128,4> + merge_kernel",
+                         "algorithmic_bytes_per_call": int(alg_bytes),
+                         "us_per_call": round(dec_s * 1e6, 3)},
+            "plan_us_per_call": round(plan_s * 1e6, 3),
+            "decode_tokens_per_s": round(w.B / dec_s, 1),
+        })
+        if not args.no_cold:
+            flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
+            cold_s = time_cold(prep.attention, 30, stream, flush)
+            del flush
+            result["cold"] = {"us_per_call": round(cold_s * 1e6, 3),
+                              "GB/s": round(alg_bytes / cold_s / 1e9, 2),
+                              "pct_hbm_peak": round(100 * alg_bytes / cold_s / 1e9 / HBM_PEAK_GBS, 2),
+                              "note": "msa_decode alone, a 1 GiB read evicts L2 and Infinity Cache before each call"}
+        if not args.no_cpu_baseline:
+            result["cpu_baseline"] = cpu_baseline(w, alg_bytes)
+        del prep
+        torch.cuda.empty_cache()
+
+    # --------------------------------------------------------------- prefill
+    import kv_cache_attention_msa_amd as msa
+    if args.only in (None, "prefill") and not args.no_prefill and msa.prefill_available():
+        wp = make_workload(3, seed=args.seed)
+        prep = Prepared(wp)
+        flops = 4.0 * wp.D * wp.Hq * visible_pairs(wp)
+        prep.plan()
+        for _ in range(max(3, args.warmup // 4)):
+            prep.attention()
+        torch.cuda.synchronize()
+        n = max(10, args.steps // 4)
+        pf_s = time_calls(prep.attention, n, prep.stream)
+        tfs = flops / pf_s / 1e12
+        result["prefill"] = {"workload": NAMES[3], "us_per_call": round(pf_s * 1e6, 3),
+                             "TFLOP/s": round(tfs, 2), "pct_mfma_bf16_peak": round(100 * tfs / MFMA_BF16_PEAK_TFS, 2),
+                             "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
+                                          "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                                          "traffic": None, "kernel": "msa_prefill_chunk",
+                                          "algorithmic_flops_per_call": flops},
+                             "calls": n}
+        del prep
+    if args.copy_calibration:
+        a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+        bb = torch.empty_like(a)
+        for _ in range(5):
+            bb.copy_(a)
+        torch.cuda.synchronize()
+        result["copy_calibration_bytes"] = 256 << 20
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -47,15 +47,31 @@ struct Geo {
   static constexpr int ES = sizeof(KV);
   static constexpr int ROW = D * ES;              // bytes of one head's row
   static constexpr int CH = ROW / 16;             // 16-byte chunks per row
-  static constexpr int SW = CH < 16 ? CH : 16;    // swizzle period
-  static constexpr int LPR = ROW / 4 < 64 ? ROW / 4 : 64;  // lanes per V row
-  static constexpr int BPL = ROW / LPR;           // V bytes per lane per row
-  static constexpr int RPL = kWave / LPR;         // V rows per load instruction
-  static constexpr int EPL = BPL / ES;            // V elements per lane
-  static constexpr int KLOADS = kTileTok * CH / kWave;
-  static constexpr int VLOADS = kTileTok / RPL;
-  static_assert(BPL == 4, "V lane slice must be one dword");
+  static constexpr int SW = CH < 16 ? CH : 16;    // LDS swizzle period
+  static constexpr int RPI = kWave / CH;          // rows per 16-byte load instruction
+  static constexpr int NL = kTileTok / RPI;       // load instructions per tile (K or V)
+  static constexpr int LPB = kBlk / RPI;          // load instructions per block
+  static constexpr int EPC = 16 / ES;             // elements per 16-byte chunk
+  static constexpr int NPAT = SW > RPI ? SW / RPI : 1;  // distinct swizzle patterns of K writes
+  static_assert(CH <= 16 && kBlk % RPI == 0, "row layout");
 };
+
+// Buffer resource for one KV block of one head: base = the block's first
+// row, num_records = rows that may be read * row stride.  Buffer loads
+// outside num_records return zero in hardware, so evicted blocks, blocks
+// past the split and padding rows past ctx_len need no branch and no
+// select, and can never touch memory outside the pool.
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+constexpr int kBufferFlags = 0x00020000;  // raw (untyped) dword access, gfx9 family
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, int(bytes), kBufferFlags);
+}
+
+__device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
 
 __device__ __forceinline__ float dot_chunk(uint4 q, uint4 k, float acc, uint16_t) {
   typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -79,15 +95,35 @@ __device__ __forceinline__ float dot_chunk(uint4 q, uint4 k, float acc, float) {
 }
 
 template <typename KV>
-__device__ __forceinline__ void unpack_v(uint32_t w, float* v);
+__device__ __forceinline__ void unpack_chunk(uint4 x, float* v);
 template <>
-__device__ __forceinline__ void unpack_v<uint16_t>(uint32_t w, float* v) {
-  v[0] = bf16lo_to_f32(w);
-  v[1] = bf16hi_to_f32(w);
+__device__ __forceinline__ void unpack_chunk<uint16_t>(uint4 x, float* v) {
+  v[0] = bf16lo_to_f32(x.x); v[1] = bf16hi_to_f32(x.x);
+  v[2] = bf16lo_to_f32(x.y); v[3] = bf16hi_to_f32(x.y);
+  v[4] = bf16lo_to_f32(x.z); v[5] = bf16hi_to_f32(x.z);
+  v[6] = bf16lo_to_f32(x.w); v[7] = bf16hi_to_f32(x.w);
 }
 template <>
-__device__ __forceinline__ void unpack_v<float>(uint32_t w, float* v) {
-  v[0] = __uint_as_float(w);
+__device__ __forceinline__ void unpack_chunk<float>(uint4 x, float* v) {
+  v[0] = __uint_as_float(x.x); v[1] = __uint_as_float(x.y);
+  v[2] = __uint_as_float(x.z); v[3] = __uint_as_float(x.w);
+}
+
+// G consecutive floats from LDS with the widest reads available
+template <int G>
+__device__ __forceinline__ void read_weights(const float* src, float* pw) {
+  if constexpr (G % 4 == 0) {
+#pragma unroll
+    for (int i = 0; i < G; i += 4) {
+      const float4 t = *reinterpret_cast<const float4*>(src + i);
+      pw[i] = t.x; pw[i + 1] = t.y; pw[i + 2] = t.z; pw[i + 3] = t.w;
+    }
+  } else if constexpr (G == 2) {
+    const float2 t = *reinterpret_cast<const float2*>(src);
+    pw[0] = t.x; pw[1] = t.y;
+  } else {
+    pw[0] = src[0];
+  }
 }
 
 template <typename KV>
@@ -118,8 +154,7 @@ __device__ __forceinline__ int wg_search_segment(const msa_segment* segs, int lo
 template <typename KV, int D, int G>
 __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   using GE = Geo<KV, D>;
-  constexpr int ROW = GE::ROW, CH = GE::CH, SW = GE::SW;
-  constexpr int LPR = GE::LPR, RPL = GE::RPL, EPL = GE::EPL;
+  constexpr int ROW = GE::ROW, CH = GE::CH, SW = GE::SW, EPC = GE::EPC;
 
   // K tiles; during set-up the same bytes hold the staged segment list, and
   // at the end the per-wavefront states for the cross-wave merge.
@@ -131,7 +166,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   static_assert(sizeof(k_lds) >= (kNW * G * D + 2 * kNW * G) * sizeof(float), "merge");
 
   const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int tid = threadIdx.x, lane = tid & (kWave - 1), w = tid / kWave;
+  // the wavefront index is wave-uniform; say so, or everything derived from
+  // it (tile indices, buffer descriptors) is treated as divergent
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int T = p.split_blocks;
 
   const int s0 = p.indptr[b], s1 = p.indptr[b + 1];
@@ -190,85 +228,120 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   }
   __syncthreads();
 
-  // ---- main loop: one 64-token tile per wavefront per iteration ----------
+  // ---- main loop: one 64-token tile (4 blocks) per wavefront per step ----
+  // Loads: instruction c of a tile covers rows c*RPI .. c*RPI+RPI-1 (all in
+  // block c/LPB), each lane one 16-byte chunk.  The block's base address is
+  // wave-uniform (scalar registers); the per-lane offset is fixed for the
+  // whole kernel, so no vector address arithmetic happens in the loop.
+  const size_t tok_stride = size_t(p.Hkv) * ROW;  // bytes between slots
+  const size_t blk_stride = tok_stride * kBlk;    // bytes between blocks
   const char* kbase = static_cast<const char*>(p.k_pool) + size_t(g) * ROW;
   const char* vbase = static_cast<const char*>(p.v_pool) + size_t(g) * ROW;
-  const size_t tok_stride = size_t(p.Hkv) * ROW;  // bytes between slots
+  // (rows of a block are tok_stride apart; a row's ROW bytes never cross
+  // into the next row's range, so row-granular num_records is exact)
+  const int lrow = lane / CH, lch = lane % CH;
+  // per-lane byte offsets inside a block, one per load of the block
+  uint32_t voff[GE::LPB];
+#pragma unroll
+  for (int ci = 0; ci < GE::LPB; ++ci)
+    voff[ci] = uint32_t((ci * GE::RPI + lrow) * tok_stride + lch * 16);
   uint8_t* kt = &k_lds[w][0];
+  float* pt = &p_lds[w][0][0];
+  // LDS byte offsets of this lane's K chunk, one per swizzle pattern; load c
+  // adds c*RPI*ROW on top (an immediate)
+  uint32_t kwo[GE::NPAT];
+#pragma unroll
+  for (int cm = 0; cm < GE::NPAT; ++cm) {
+    const int r = cm * GE::RPI + lrow;
+    kwo[cm] = uint32_t(lrow * ROW + ((lch ^ (r % SW)) * 16));
+  }
 
-  float m_run[G], l_lane[G], o[G][EPL];
+  float m_run[G], l_lane[G], o[G][EPC];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m_run[h] = -INFINITY;
     l_lane[h] = 0.f;
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[h][e] = 0.f;
+    for (int e = 0; e < EPC; ++e) o[h][e] = 0.f;
   }
 
   const int ntiles = (nblk + 3) / 4;
-  for (int ti = w; ti < ntiles; ti += kNW) {
-    const int jb = ti * 4;
-    // K: chunk c*64+lane of the tile = row r, 16-byte chunk ch
-    uint4 kreg[GE::KLOADS];
-#pragma unroll
-    for (int c = 0; c < GE::KLOADS; ++c) {
-      const int id = c * kWave + lane;
-      const int r = id / CH, ch = id % CH;
-      const int jj = jb + r / kBlk;
-      const int ph = jj < nblk ? blk_phys[jj] : -1;
-      kreg[c] = make_uint4(0, 0, 0, 0);
-      if (ph >= 0)
-        kreg[c] = *reinterpret_cast<const uint4*>(kbase + (size_t(ph) * kBlk + r % kBlk) * tok_stride + ch * 16);
-    }
-    // V: row t*RPL + lane/LPR, dword lane%LPR
-    uint32_t vreg[GE::VLOADS];
-#pragma unroll
-    for (int t = 0; t < GE::VLOADS; ++t) {
-      const int r = t * RPL + lane / LPR;
-      const int jj = jb + r / kBlk, slot = r % kBlk;
-      const int ph = jj < nblk ? blk_phys[jj] : -1;
-      const bool ok = ph >= 0 && (j0 + jj != nAB - 1 || slot < last_tokens);
-      uint32_t x = 0;
-      if (ph >= 0)
-        x = *reinterpret_cast<const uint32_t*>(vbase + (size_t(ph) * kBlk + slot) * tok_stride + (lane % LPR) * 4);
-      vreg[t] = ok ? x : 0u;
-    }
-#pragma unroll
-    for (int c = 0; c < GE::KLOADS; ++c) {
-      const int id = c * kWave + lane;
-      const int r = id / CH, ch = id % CH;
-      *reinterpret_cast<uint4*>(kt + r * ROW + ((ch ^ (r % SW)) * 16)) = kreg[c];
-    }
-    __builtin_amdgcn_wave_barrier();
+  const int last_local = nAB - 1 - j0;  // local index of the sequence's final block
 
-    // scores: one token per lane.  The query rows are re-read from LDS
-    // (broadcast) every tile: an opaque offset keeps the compiler from
-    // hoisting G*D loop-invariant values into registers.
+  // wave-uniform physical block ids and readable row counts of tile ti
+  auto tile_blocks = [&](int ti, int* ph, int* rows) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const int jj = ti * 4 + k;
+      ph[k] = __builtin_amdgcn_readfirstlane(jj < nblk ? blk_phys[min(jj, kMaxSplitBlocks - 1)] : -1);
+      rows[k] = ph[k] < 0 ? 0 : (jj == last_local ? last_tokens : kBlk);
+    }
+  };
+  auto load_tile = [&](const char* base, const int* ph, const int* rows, uint4* r) {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const __amdgpu_buffer_rsrc_t rs =
+          block_rsrc(base + size_t(ph[k] < 0 ? 0 : ph[k]) * blk_stride, uint32_t(rows[k] * tok_stride));
+#pragma unroll
+      for (int ci = 0; ci < GE::LPB; ++ci) r[k * GE::LPB + ci] = load16(rs, voff[ci]);
+    }
+  };
+
+  uint4 kreg[GE::NL], vreg[GE::NL];
+  int ph[4], rows[4];
+  int ti = w;
+  tile_blocks(ti, ph, rows);
+  // K strictly before V, here and in the loop: the loop top then only waits
+  // for the K loads (vmcnt counts in issue order) while V stays in flight
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(kbase, ph, rows, kreg);
+  __builtin_amdgcn_sched_barrier(0);
+  load_tile(vbase, ph, rows, vreg);
+  __builtin_amdgcn_sched_barrier(0);
+  for (; ti < ntiles; ti += kNW) {
+    // K tile -> LDS, XOR-swizzled so the one-token-per-lane reads are
+    // conflict-free
+#pragma unroll
+    for (int c = 0; c < GE::NL; ++c)
+      *reinterpret_cast<uint4*>(kt + kwo[c % GE::NPAT] + c * GE::RPI * ROW) = kreg[c];
+    __builtin_amdgcn_wave_barrier();
+    // phase fences: without them the scheduler overlaps the next tile's
+    // loads with this tile's live registers and runs out of VGPRs
+    __builtin_amdgcn_sched_barrier(0);
+    const int tn = ti + kNW;
+    int phn[4], rowsn[4];
+    tile_blocks(tn, phn, rowsn);
+    // next K in flight during this tile (past the last tile the descriptors
+    // have no readable rows: the loads return zeros and touch no memory)
+    load_tile(kbase, phn, rowsn, kreg);
+    __builtin_amdgcn_sched_barrier(0);
+
+    // token validity for the one-token-per-lane score phase
+    const int kb = lane / kBlk, slot = lane % kBlk;
+    const int rows_l = kb == 0 ? rows[0] : kb == 1 ? rows[1] : kb == 2 ? rows[2] : rows[3];
+    const bool tok_ok = slot < rows_l;
+
+    // scores.  The query rows are re-read from LDS (broadcast) every tile: an
+    // opaque offset keeps the compiler from hoisting G*D values into registers.
     int qoff = 0;
     asm volatile("" : "+v"(qoff));
     const uint8_t* qt = q_lds + qoff;
     float sc[G];
 #pragma unroll
     for (int h = 0; h < G; ++h) sc[h] = 0.f;
-    {
-      const int r = lane;
 #pragma unroll 2
-      for (int c = 0; c < CH; ++c) {
-        const uint4 kc = *reinterpret_cast<const uint4*>(kt + r * ROW + ((c ^ (r % SW)) * 16));
+    for (int c = 0; c < CH; ++c) {
+      const uint4 kc = *reinterpret_cast<const uint4*>(kt + lane * ROW + ((c ^ (lane % SW)) * 16));
 #pragma unroll
-        for (int h = 0; h < G; ++h) {
-          const uint4 qc = *reinterpret_cast<const uint4*>(qt + h * ROW + c * 16);
-          sc[h] = dot_chunk(qc, kc, sc[h], KV());
-        }
+      for (int h = 0; h < G; ++h) {
+        const uint4 qc = *reinterpret_cast<const uint4*>(qt + h * ROW + c * 16);
+        sc[h] = dot_chunk(qc, kc, sc[h], KV());
       }
-      const int jj = jb + r / kBlk, slot = r % kBlk;
-      const int ph = jj < nblk ? blk_phys[jj] : -1;
-      const bool ok = ph >= 0 && (j0 + jj != nAB - 1 || slot < last_tokens);
-#pragma unroll
-      for (int h = 0; h < G; ++h) sc[h] = ok ? sc[h] * p.scale_log2 : -INFINITY;
     }
+#pragma unroll
+    for (int h = 0; h < G; ++h) sc[h] = tok_ok ? sc[h] * p.scale_log2 : -INFINITY;
 
-    // online softmax (log2 units)
+    // online softmax (log2 units), one wavefront-wide max per head
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float m_new = fmaxf(m_run[h], wave_max(sc[h]));
@@ -280,24 +353,34 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
       m_run[h] = m_new;
       l_lane[h] = l_lane[h] * alpha + pw;
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[h][e] *= alpha;
-      p_lds[w][lane][h] = pw;
+      for (int e = 0; e < EPC; ++e) o[h][e] *= alpha;
+      pt[lane * G + h] = pw;
     }
     __builtin_amdgcn_wave_barrier();
 
-    // PV: lane owns EPL elements of D for all G heads
+    // PV: this lane's EPC elements of D for the rows its V loads covered
 #pragma unroll
-    for (int t = 0; t < GE::VLOADS; ++t) {
-      const int r = t * RPL + lane / LPR;
-      float v[EPL];
-      unpack_v<KV>(vreg[t], v);
+    for (int c = 0; c < GE::NL; ++c) {
+      const int r = c * GE::RPI + lrow;
+      float v[GE::EPC];
+      unpack_chunk<KV>(vreg[c], v);
       float pw[G];
-#pragma unroll
-      for (int h = 0; h < G; ++h) pw[h] = p_lds[w][r][h];
+      read_weights<G>(pt + r * G, pw);
 #pragma unroll
       for (int h = 0; h < G; ++h)
 #pragma unroll
-        for (int e = 0; e < EPL; ++e) o[h][e] = fmaf(pw[h], v[e], o[h][e]);
+        for (int e = 0; e < EPC; ++e) o[h][e] = fmaf(pw[h], v[e], o[h][e]);
+      // keep each chunk's weight reads and unpacking next to its FMAs;
+      // hoisting all of them would need more registers than the file has
+      if (c % 2 == 1) __builtin_amdgcn_sched_barrier(0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    load_tile(vbase, phn, rowsn, vreg);  // next V in flight during the next scores
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      ph[k] = phn[k];
+      rows[k] = rowsn[k];
     }
     __builtin_amdgcn_wave_barrier();
   }
@@ -306,21 +389,22 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   float l_w[G];
 #pragma unroll
   for (int h = 0; h < G; ++h) l_w[h] = wave_sum(l_lane[h]);
-  if constexpr (RPL == 2) {
+  // lanes with the same chunk hold partial sums over different rows
+#pragma unroll
+  for (int x = CH; x < kWave; x <<= 1)
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[h][e] += __shfl_xor(o[h][e], 32);
-  }
+      for (int e = 0; e < EPC; ++e) o[h][e] += __shfl_xor(o[h][e], x);
   __syncthreads();
   float* mo = reinterpret_cast<float*>(&k_lds[0][0]);  // [kNW][G][D]
   float* mm = mo + kNW * G * D;                        // [kNW][G]
   float* ml = mm + kNW * G;
-  if (lane < LPR) {
+  if (lrow == 0) {
 #pragma unroll
     for (int h = 0; h < G; ++h)
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) mo[(w * G + h) * D + lane * EPL + e] = o[h][e];
+      for (int e = 0; e < EPC; ++e) mo[(w * G + h) * D + lch * EPC + e] = o[h][e];
   }
   if (lane == 0) {
 #pragma unroll
@@ -393,14 +477,16 @@ SplitPlan decode_split(int32_t B, int32_t Hkv, int32_t max_ctx_len, int32_t bloc
   const int64_t nbm = (int64_t(max_ctx_len) + block_size - 1) / block_size;
   int64_t T = split_blocks;
   if (T <= 0) {
-    // aim for ~1024 workgroups (4 per CU on a 256-CU part) without splits
-    // shorter than 16 blocks (4 tiles per wavefront)
+    // Splits of at most 128 blocks (2048 tokens): long enough that the
+    // per-split set-up and partial write are small next to its 8 MB of K/V
+    // per KV head (bf16, D 128), short enough that a few long contexts in a
+    // skewed batch do not leave most CUs idle.  Short batches get shorter
+    // splits (down to 32 blocks) so the grid still covers the chip.
     const int64_t pairs = int64_t(B) * Hkv;
-    int64_t S = (1024 + pairs - 1) / pairs;
-    T = (nbm + S - 1) / S;
+    T = (nbm * pairs + 511) / 512;
     T = ((T + 15) / 16) * 16;
-    if (T < 16) T = 16;
-    if (T > kMaxSplitBlocks) T = kMaxSplitBlocks;
+    if (T < 32) T = 32;
+    if (T > 128) T = 128;
   }
   sp.split_blocks = int32_t(T);
   sp.S = int32_t(nbm == 0 ? 1 : (nbm + T - 1) / T);

@@ -1,18 +1,430 @@
-// a2 + a4: MSA chunked prefill (placeholder until the MFMA kernel lands).
+// a2 + a4: MSA chunked prefill over the alive-token stream of a segment plan.
+//
+// multi_segment_attention for a chunk of query rows (P1, "Core method 1:
+// MSA" pseudocode; P1 "3. 自适应分块调度器": prefill runs in chunks whose
+// KV is already in the pool).  Row i of sequence b sits at logical position
+// q_pos0[b] + i and sees the alive keys at logical positions <= its own.
+// This is a dense contraction, so QK^T and PV run on bf16 MFMA
+// (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.
+//
+// Workgroup = (query-position tile, KV head g, sequence b [, split s]).
+// The G query heads of KV head g are stacked: each wavefront owns one
+// 32-row tile (one head, 32 consecutive positions), so every K/V tile
+// staged in LDS is used by all G heads (GQA reuse) and by all positions of
+// the workgroup.
+//
+// Per 64-key tile and wavefront (one lane = one query row throughout):
+//   S^T[key][row] = K[key][:] . Q[row][:]     A = K from LDS (row-major,
+//                                             XOR-swizzled), B = Q in VGPRs
+//   online softmax over the lane's 32 keys + the other half-wave's 32
+//   O^T[d][row] += V^T[d][key] . P^T[key][row] A = V^T from LDS (stored
+//                                             transposed), B = P in VGPRs:
+//                                             exactly the lane's own S
+//                                             accumulators rounded to bf16
+// Keys come from the sequence's segments in logical order: the workgroup
+// expands its segments into per-block (physical id, logical id) lists in LDS,
+// 512 blocks at a time.  Blocks are loaded through buffer descriptors whose
+// num_records covers only the rows that exist, so missing blocks and padding
+// rows past ctx_len read as zero (and are masked); tiles straddling the
+// causal diagonal are masked per element by logical position.
 #include "msa_internal.h"
 
 namespace msa {
+namespace {
 
-bool prefill_supported(msa_dtype, int32_t, int32_t) { return false; }
-int32_t prefill_max_split_blocks() { return 512; }
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef unsigned int u32x4_t __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x2_t __attribute__((ext_vector_type(2)));
 
-SplitPlan prefill_split(int32_t, int32_t, int32_t, int32_t, int32_t, int32_t, int32_t split_blocks) {
+constexpr int kD = 128;            // head dim built
+constexpr int kRow = kD * 2;       // bytes per K/V row of one head (bf16)
+constexpr int kBlk = 16;           // tokens per block
+constexpr int kTK = 64;            // keys per tile (4 blocks)
+constexpr int kVtStride = kTK * 2 + 8;  // bytes per V^T row in LDS (padded, 8-aligned)
+constexpr int kChunkBlocks = 512;  // blocks expanded into LDS at a time
+constexpr int kMaxSplitBlocks = 1 << 20;
+constexpr float kLn2 = 0.69314718055994530942f;
+constexpr int kBufferFlags = 0x00020000;
+
+template <int G>
+struct PGeo {
+  static constexpr int WAVES = G <= 4 ? 4 : G;
+  static constexpr int THREADS = WAVES * kWave;
+  static constexpr int NPOS = 32 * WAVES / G;  // query positions per workgroup
+  static constexpr int KCHUNKS = kTK * (kRow / 16) / THREADS;  // K 16-B chunks per thread per tile
+  static constexpr int VPAIRS = KCHUNKS / 2;                   // V key pairs per thread per tile
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, int(bytes), kBufferFlags);
+}
+__device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+// Largest i in [lo, hi) with segs[i].alive_token_start <= x (segs[lo] does).
+template <int THREADS>
+__device__ __forceinline__ int wg_search_segment(const msa_segment* segs, int lo, int hi, int x) {
+  while (hi - lo > 1) {
+    const int step = (hi - lo + THREADS - 1) / THREADS;
+    const int idx = lo + int(threadIdx.x) * step;
+    const bool pred = idx < hi && segs[idx].alive_token_start <= x;
+    const int cnt = __syncthreads_count(pred);
+    lo = lo + (cnt - 1) * step;
+    hi = min(hi, lo + step);
+  }
+  return lo;
+}
+
+template <int G>
+__global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams p) {
+  using PG = PGeo<G>;
+  constexpr int THREADS = PG::THREADS, NPOS = PG::NPOS;
+
+  __shared__ __align__(16) uint8_t k_lds[2][kTK * kRow];
+  __shared__ __align__(16) uint8_t vt_lds[2][kD * kVtStride];
+  __shared__ int32_t blk_phys[kChunkBlocks];
+  __shared__ int32_t blk_lpos[kChunkBlocks];
+  __shared__ int32_t st_start[kChunkBlocks + 1];
+  __shared__ int32_t st_phys[kChunkBlocks + 1];
+  __shared__ int32_t st_nblk[kChunkBlocks + 1];
+  __shared__ int32_t st_lblk[kChunkBlocks + 1];
+
+  const int ptile = blockIdx.x, g = blockIdx.y;
+  const int b = blockIdx.z / p.S, s = blockIdx.z % p.S;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int hh = w % G;               // head within the group
+  const int pt = w / G;               // 32-position sub-tile of this wavefront
+  const int h = g * G + hh;           // query head
+  const int half = lane / 32, lr = lane % 32;
+  const int C = p.C;
+  const int p0 = ptile * NPOS;        // first position (row index in the chunk)
+  const int q0 = p.q_pos0[b];
+  const int my_row = p0 + pt * 32 + lr;        // this lane's row in the chunk
+  const int my_qpos = q0 + my_row;             // its logical position
+  const int wg_qmin = q0 + p0;
+  const int wg_qmax = q0 + min(p0 + NPOS, C) - 1;
+
+  // ---- this split's alive-block range -----------------------------------
+  const int s0 = p.indptr[b], s1 = p.indptr[b + 1];
+  int A = 0;
+  if (s1 > s0) {
+    const msa_segment last = p.segs[s1 - 1];
+    A = last.alive_token_start + last.num_tokens;
+  }
+  const int T = p.split_blocks;
+  const int nAB = min((A + kBlk - 1) / kBlk, p.S * T);
+  const int Sb = (nAB + T - 1) / T;
+  // a split past this sequence's keys has nothing to contribute (split 0 of
+  // a sequence without keys still writes O = 0, LSE = -inf below)
+  if (s > 0 && s >= Sb) return;
+  const int j_begin = s * T;
+  const int j_end = min(nAB, j_begin + T);
+  const int last_tokens = min(kBlk, A - kBlk * (nAB - 1));
+
+  // ---- Q of this lane's row into MFMA B-operand registers ----------------
+  // rows past the chunk read as zero (descriptor covers only existing rows)
+  uint4 qop[kD / 16];
+  {
+    const size_t row_bytes = size_t(p.Hq) * kRow;
+    const int nrows = max(0, min(NPOS, C - p0));
+    const char* qb = static_cast<const char*>(p.q) + (size_t(b) * C + p0) * row_bytes;
+    const __amdgpu_buffer_rsrc_t qr = rsrc(qb, uint32_t(nrows * row_bytes));
+    const uint32_t off = uint32_t((pt * 32 + lr) * row_bytes + size_t(h) * kRow + half * 16);
+#pragma unroll
+    for (int k = 0; k < kD / 16; ++k) qop[k] = bload16(qr, off + k * 32);
+  }
+
+  f32x16_t acc_o[kD / 32];
+#pragma unroll
+  for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc_o[dt][r] = 0.f;
+  float m_run = -INFINITY, l_lane = 0.f;
+
+  const size_t tok_stride = size_t(p.Hkv) * kRow;
+  const size_t blk_stride = tok_stride * kBlk;
+  const char* kbase = static_cast<const char*>(p.k_pool) + size_t(g) * kRow;
+  const char* vbase = static_cast<const char*>(p.v_pool) + size_t(g) * kRow;
+
+  // per-thread tile-load coordinates (fixed for the kernel)
+  // K: chunk q = tid + THREADS*it -> key row r = q/16, 16-byte chunk c = q%16
+  const int kc = tid % 16;
+  // V: key pair index rp = tid/16 + (THREADS/16)*it -> keys 2rp, 2rp+1; chunk kc
+
+  bool done = false;
+  for (int cb = j_begin; cb < j_end && !done; cb += kChunkBlocks) {
+    const int nblk = min(kChunkBlocks, j_end - cb);
+    // ---- expand the segments covering blocks [cb, cb+nblk) ---------------
+    __syncthreads();  // previous chunk's lists are no longer read
+    const int sf = wg_search_segment<THREADS>(p.segs, s0, s1, cb * kBlk);
+    const int ns = min(nblk, s1 - sf);
+    for (int i = tid; i < ns; i += THREADS) {
+      const msa_segment sg = p.segs[sf + i];
+      const bool in_pool = sg.phys_block >= 0 && sg.num_blocks >= 0 &&
+                           int64_t(sg.phys_block) + sg.num_blocks <= p.P;
+      st_start[i] = sg.alive_token_start / kBlk;
+      st_phys[i] = in_pool ? sg.phys_block : -1;
+      st_nblk[i] = in_pool ? sg.num_blocks : 0;
+      st_lblk[i] = sg.logical_block;
+    }
+    __syncthreads();
+    for (int jj = tid; jj < nblk; jj += THREADS) {
+      const int j = cb + jj;
+      int lo = 0, hi = ns;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (st_start[mid] <= j) lo = mid; else hi = mid;
+      }
+      const int off = j - st_start[lo];
+      const bool ok = st_phys[lo] >= 0 && off >= 0 && off < st_nblk[lo];
+      blk_phys[jj] = ok ? st_phys[lo] + off : -1;
+      blk_lpos[jj] = st_lblk[lo] + off;
+    }
+    __syncthreads();
+
+    const int ntiles = (nblk + 3) / 4;
+    // tile loader: global -> registers; registers -> LDS (K swizzled, V^T)
+    uint4 kreg[PG::KCHUNKS], vreg[PG::KCHUNKS];
+    auto issue_tile = [&](int ti) {
+#pragma unroll
+      for (int it = 0; it < PG::KCHUNKS; ++it) {
+        const int r = tid / 16 + (THREADS / 16) * it;  // key row in tile (K)
+        const int kb = r / kBlk, slot = r % kBlk;
+        const int jj = ti * 4 + kb;
+        const int ph = jj < nblk && ti < ntiles ? blk_phys[jj] : -1;
+        const int rows = ph < 0 ? 0 : (cb + jj == nAB - 1 ? last_tokens : kBlk);
+        const __amdgpu_buffer_rsrc_t rk =
+            rsrc(kbase + size_t(ph < 0 ? 0 : ph) * blk_stride, uint32_t(rows * tok_stride));
+        kreg[it] = bload16(rk, uint32_t(slot * tok_stride + kc * 16));
+        // V: keys 2rp, 2rp+1 with rp = tid/16 + (THREADS/16)*(it/2), chunk kc
+        const int rp = tid / 16 + (THREADS / 16) * (it / 2);
+        const int vr = 2 * rp + (it % 2);
+        const int vkb = vr / kBlk, vslot = vr % kBlk;
+        const int vjj = ti * 4 + vkb;
+        const int vph = vjj < nblk && ti < ntiles ? blk_phys[vjj] : -1;
+        const int vrows = vph < 0 ? 0 : (cb + vjj == nAB - 1 ? last_tokens : kBlk);
+        const __amdgpu_buffer_rsrc_t rv =
+            rsrc(vbase + size_t(vph < 0 ? 0 : vph) * blk_stride, uint32_t(vrows * tok_stride));
+        vreg[it] = bload16(rv, uint32_t(vslot * tok_stride + kc * 16));
+      }
+    };
+    auto store_tile = [&](int buf) {
+#pragma unroll
+      for (int it = 0; it < PG::KCHUNKS; ++it) {
+        const int r = tid / 16 + (THREADS / 16) * it;
+        *reinterpret_cast<uint4*>(&k_lds[buf][r * kRow + ((kc ^ (r % 16)) * 16)]) = kreg[it];
+      }
+#pragma unroll
+      for (int pi = 0; pi < PG::VPAIRS; ++pi) {
+        const int rp = tid / 16 + (THREADS / 16) * pi;
+        const uint4 x0 = vreg[2 * pi], x1 = vreg[2 * pi + 1];
+        const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w};
+        const uint32_t a1[4] = {x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          // (V[2rp][d], V[2rp+1][d]) for d = 8kc + 2e and 8kc + 2e + 1
+          const uint32_t lo = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
+          const uint32_t hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
+          const int d = 8 * kc + 2 * e;
+          *reinterpret_cast<uint32_t*>(&vt_lds[buf][d * kVtStride + 4 * rp]) = lo;
+          *reinterpret_cast<uint32_t*>(&vt_lds[buf][(d + 1) * kVtStride + 4 * rp]) = hi;
+        }
+      }
+    };
+
+    issue_tile(0);
+    store_tile(0);
+    __syncthreads();
+    for (int ti = 0; ti < ntiles; ++ti) {
+      const int buf = ti & 1;
+      // uniform facts about this tile
+      int lp[4], rw[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int jj = ti * 4 + k;
+        const int ph = jj < nblk ? blk_phys[jj] : -1;
+        lp[k] = jj < nblk ? blk_lpos[jj] : 0x3fffffff;
+        rw[k] = ph < 0 ? 0 : (cb + jj == nAB - 1 ? last_tokens : kBlk);
+      }
+      const int kmin = lp[0] * kBlk;
+      if (kmin > wg_qmax) {  // this and every later key is after every row
+        done = true;
+        break;
+      }
+      if (ti + 1 < ntiles) issue_tile(ti + 1);  // next tile in flight
+
+      // ---- S^T = K Q^T for 2 x 32 keys ------------------------------------
+      f32x16_t acc_s[2];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_s[kb2][r] = 0.f;
+        const int krow = kb2 * 32 + lr;
+#pragma unroll
+        for (int k = 0; k < kD / 16; ++k) {
+          const uint4 a = *reinterpret_cast<const uint4*>(
+              &k_lds[buf][krow * kRow + (((2 * k + half) ^ (krow % 16)) * 16)]);
+          acc_s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qop[k]),
+                                                               acc_s[kb2], 0, 0, 0);
+        }
+      }
+
+      // ---- mask + online softmax (lane = query row) ----------------------
+      bool full = true;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) full = full && rw[k] == kBlk;
+      const int kmax = lp[3] * kBlk + kBlk - 1;
+      const bool need_mask = !full || kmax > wg_qmin;
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          float v = acc_s[kb2][r] * p.scale_log2;
+          if (need_mask) {
+            const int key = kb2 * 32 + 8 * (r / 4) + 4 * half + (r % 4);
+            const int kblk = key / kBlk, slot = key % kBlk;
+            const int kpos = lp[kblk] * kBlk + slot;
+            const bool vis = slot < rw[kblk] && kpos <= my_qpos;
+            v = vis ? v : -INFINITY;
+          }
+          acc_s[kb2][r] = v;
+          mx = fmaxf(mx, v);
+        }
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
+      const float msub = m_new == -INFINITY ? 0.f : m_new;
+      m_run = m_new;
+      float lsum = 0.f;
+      uint4 pop[4];  // P^T operands for the 4 key steps of 16
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        float pv[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = exp2f(acc_s[t / 2][8 * (t % 2) + e] - msub);
+          lsum += pv[e];
+        }
+        pop[t] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
+                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+      }
+      l_lane = l_lane * alpha + lsum;
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+
+      // ---- O^T += V^T P^T --------------------------------------------------
+#pragma unroll
+      for (int dt = 0; dt < kD / 32; ++dt) {
+        const int d = dt * 32 + lr;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          const uint8_t* vrow = &vt_lds[buf][d * kVtStride];
+          const u32x2_t lo2 = *reinterpret_cast<const u32x2_t*>(vrow + (16 * t + 4 * half) * 2);
+          const u32x2_t hi2 = *reinterpret_cast<const u32x2_t*>(vrow + (16 * t + 8 + 4 * half) * 2);
+          const uint4 a = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pop[t]),
+                                                              acc_o[dt], 0, 0, 0);
+        }
+      }
+
+      if (ti + 1 < ntiles) store_tile(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // ---- finish: combine the two half-waves' sums, write O and LSE --------
+  const float L = l_lane + __shfl_xor(l_lane, 32);
+  if (my_row >= C) return;
+  if (Sb <= 1) {
+    const bool ok = L > 0.f;
+    const float inv = ok ? 1.f / L : 0.f;
+    uint16_t* out = static_cast<uint16_t*>(p.out) + ((size_t(b) * C + my_row) * p.Hq + h) * kD;
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = dt * 32 + 8 * i + 4 * half;
+        uint2 v;
+        v.x = pack_bf16x2(acc_o[dt][4 * i] * inv, acc_o[dt][4 * i + 1] * inv);
+        v.y = pack_bf16x2(acc_o[dt][4 * i + 2] * inv, acc_o[dt][4 * i + 3] * inv);
+        *reinterpret_cast<uint2*>(out + d) = v;
+      }
+    if (p.lse && half == 0)
+      p.lse[(size_t(b) * C + my_row) * p.Hq + h] = ok ? (m_run + log2f(L)) * kLn2 : -INFINITY;
+  } else {
+    const size_t n = size_t(b) * p.S + s;
+    const size_t row = (n * C + my_row) * p.Hq + h;
+    float* o = p.o_part + row * kD;
+#pragma unroll
+    for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int d = dt * 32 + 8 * i + 4 * half;
+        *reinterpret_cast<float4*>(o + d) =
+            make_float4(acc_o[dt][4 * i], acc_o[dt][4 * i + 1], acc_o[dt][4 * i + 2], acc_o[dt][4 * i + 3]);
+      }
+    if (half == 0) {
+      p.m_part[row] = (L > 0.f) ? m_run * kLn2 : -INFINITY;
+      p.l_part[row] = L;
+    }
+  }
+}
+
+template <int G>
+hipError_t launch_g(const PrefillParams& p, hipStream_t stream) {
+  using PG = PGeo<G>;
+  dim3 grid((p.C + PG::NPOS - 1) / PG::NPOS, p.Hkv, p.B * p.S);
+  hipLaunchKernelGGL(prefill_kernel<G>, grid, dim3(PG::THREADS), 0, stream, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool prefill_supported(msa_dtype dtype, int32_t D, int32_t G) {
+  return dtype == MSA_BF16 && D == kD && (G == 1 || G == 2 || G == 4 || G == 8);
+}
+
+int32_t prefill_max_split_blocks() { return kMaxSplitBlocks; }
+
+SplitPlan prefill_split(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t max_ctx_len,
+                        int32_t block_size, int32_t split_blocks) {
   SplitPlan sp;
-  sp.split_blocks = split_blocks;
-  sp.S = 1;
+  const int64_t nbm = (int64_t(max_ctx_len) + block_size - 1) / block_size;
+  const int G = Hkv > 0 ? Hq / Hkv : 1;
+  const int npos = G <= 4 ? 128 / (G > 0 ? G : 1) : 32;
+  const int64_t wgs = int64_t((C + npos - 1) / npos) * Hkv * B;
+  int64_t T = split_blocks;
+  if (T <= 0) {
+    // split the key stream only when the grid alone cannot fill the chip
+    // (two workgroups per CU on 256 CUs); never below 64 blocks per split
+    int64_t S = wgs >= 512 ? 1 : (512 + wgs - 1) / wgs;
+    T = nbm > 0 ? (nbm + S - 1) / S : 1;
+    if (T < 64) T = 64;
+  }
+  if (T < 1) T = 1;
+  sp.split_blocks = int32_t(T > kMaxSplitBlocks ? kMaxSplitBlocks : T);
+  sp.S = int32_t(nbm == 0 ? 1 : (nbm + sp.split_blocks - 1) / sp.split_blocks);
+  if (sp.S < 1) sp.S = 1;
   return sp;
 }
 
-hipError_t launch_prefill(const PrefillParams&, hipStream_t) { return hipErrorInvalidValue; }
+hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  switch (p.Hq / p.Hkv) {
+    case 1: return launch_g<1>(p, stream);
+    case 2: return launch_g<2>(p, stream);
+    case 4: return launch_g<4>(p, stream);
+    case 8: return launch_g<8>(p, stream);
+  }
+  return hipErrorInvalidValue;
+}
 
 }  // namespace msa
