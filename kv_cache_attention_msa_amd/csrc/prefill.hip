@@ -46,6 +46,7 @@ constexpr int kChunkBlocks = 512;  // blocks expanded into LDS at a time
 constexpr int kMaxSplitBlocks = 1 << 20;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kBufferFlags = 0x00020000;
+constexpr int kXcds = 8;  // accelerator complex dies on MI355X, one L2 each
 
 template <int G>
 struct PGeo {
@@ -65,6 +66,14 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+// two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  const f32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+}
 
 // Largest i in [lo, hi) with segs[i].alive_token_start <= x (segs[lo] does).
 template <int THREADS>
@@ -94,8 +103,22 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams
   __shared__ int32_t st_nblk[kChunkBlocks + 1];
   __shared__ int32_t st_lblk[kChunkBlocks + 1];
 
-  const int ptile = blockIdx.x, g = blockIdx.y;
-  const int b = blockIdx.z / p.S, s = blockIdx.z % p.S;
+  // XCD-aware order: consecutive workgroup ids go round-robin to the 8 XCDs
+  // (each with its own L2).  Remap so that the workgroups one XCD receives
+  // are whole runs of position tiles of the same (sequence, KV head, split):
+  // they stream the same K/V tiles, which then hit in that XCD's L2.
+  int ptile, g, bz;
+  {
+    const int gx = gridDim.x, gy = gridDim.y;
+    const int n = gx * gy * gridDim.z;
+    const int n8 = n / kXcds * kXcds;
+    const int lin = blockIdx.x + gx * (blockIdx.y + gy * blockIdx.z);
+    const int r = lin < n8 ? (lin % kXcds) * (n8 / kXcds) + lin / kXcds : lin;
+    ptile = r % gx;
+    g = (r / gx) % gy;
+    bz = r / (gx * gy);
+  }
+  const int b = bz / p.S, s = bz % p.S;
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int hh = w % G;               // head within the group
@@ -191,27 +214,28 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams
     const int ntiles = (nblk + 3) / 4;
     // tile loader: global -> registers; registers -> LDS (K swizzled, V^T)
     uint4 kreg[PG::KCHUNKS], vreg[PG::KCHUNKS];
+    // Per-block buffer descriptors must be wave-uniform: the block a load
+    // touches is derived from the (uniform) wavefront index, never from the
+    // lane id, or the compiler wraps each load in a readfirstlane loop.
+    auto block_rsrc = [&](const char* base, int ti, int kb) {
+      const int jj = ti * 4 + kb;
+      const int ph = __builtin_amdgcn_readfirstlane(
+          (jj < nblk && ti < ntiles) ? blk_phys[min(jj, kChunkBlocks - 1)] : -1);
+      const int rows = ph < 0 ? 0 : (cb + jj == nAB - 1 ? last_tokens : kBlk);
+      return rsrc(base + size_t(ph < 0 ? 0 : ph) * blk_stride, uint32_t(rows * tok_stride));
+    };
     auto issue_tile = [&](int ti) {
 #pragma unroll
       for (int it = 0; it < PG::KCHUNKS; ++it) {
-        const int r = tid / 16 + (THREADS / 16) * it;  // key row in tile (K)
-        const int kb = r / kBlk, slot = r % kBlk;
-        const int jj = ti * 4 + kb;
-        const int ph = jj < nblk && ti < ntiles ? blk_phys[jj] : -1;
-        const int rows = ph < 0 ? 0 : (cb + jj == nAB - 1 ? last_tokens : kBlk);
-        const __amdgpu_buffer_rsrc_t rk =
-            rsrc(kbase + size_t(ph < 0 ? 0 : ph) * blk_stride, uint32_t(rows * tok_stride));
-        kreg[it] = bload16(rk, uint32_t(slot * tok_stride + kc * 16));
-        // V: keys 2rp, 2rp+1 with rp = tid/16 + (THREADS/16)*(it/2), chunk kc
-        const int rp = tid / 16 + (THREADS / 16) * (it / 2);
-        const int vr = 2 * rp + (it % 2);
-        const int vkb = vr / kBlk, vslot = vr % kBlk;
-        const int vjj = ti * 4 + vkb;
-        const int vph = vjj < nblk && ti < ntiles ? blk_phys[vjj] : -1;
-        const int vrows = vph < 0 ? 0 : (cb + vjj == nAB - 1 ? last_tokens : kBlk);
-        const __amdgpu_buffer_rsrc_t rv =
-            rsrc(vbase + size_t(vph < 0 ? 0 : vph) * blk_stride, uint32_t(vrows * tok_stride));
-        vreg[it] = bload16(rv, uint32_t(vslot * tok_stride + kc * 16));
+        // K: row r = tid/16 + (THREADS/16)*it -> block w/4 + (THREADS/256)*it
+        const int kb = w / 4 + (THREADS / 256) * it;
+        const int slot = (tid / 16) % 16;
+        kreg[it] = bload16(block_rsrc(kbase, ti, kb), uint32_t(slot * tok_stride + kc * 16));
+        // V: key 2rp + it%2 with rp = tid/16 + (THREADS/16)*(it/2)
+        //    -> block w/2 + (THREADS/128)*(it/2), slot 2*((tid/16)%8) + it%2
+        const int vkb = w / 2 + (THREADS / 128) * (it / 2);
+        const int vslot = 2 * ((tid / 16) % 8) + (it % 2);
+        vreg[it] = bload16(block_rsrc(vbase, ti, vkb), uint32_t(vslot * tok_stride + kc * 16));
       }
     };
     auto store_tile = [&](int buf) {
@@ -263,44 +287,55 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams
       f32x16_t acc_s[2];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_s[kb2][r] = 0.f;
         const int krow = kb2 * 32 + lr;
+        const f32x16_t zero = {};
 #pragma unroll
         for (int k = 0; k < kD / 16; ++k) {
           const uint4 a = *reinterpret_cast<const uint4*>(
               &k_lds[buf][krow * kRow + (((2 * k + half) ^ (krow % 16)) * 16)]);
           acc_s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qop[k]),
-                                                               acc_s[kb2], 0, 0, 0);
+                                                               k == 0 ? zero : acc_s[kb2], 0, 0, 0);
         }
       }
 
       // ---- mask + online softmax (lane = query row) ----------------------
+      // Scores stay unscaled; scale*log2(e) is folded into one FMA inside
+      // the exponent (exp2 of scale*(s - m)), exact max tracking per row.
       bool full = true;
 #pragma unroll
       for (int k = 0; k < 4; ++k) full = full && rw[k] == kBlk;
       const int kmax = lp[3] * kBlk + kBlk - 1;
-      const bool need_mask = !full || kmax > wg_qmin;
-      float mx = -INFINITY;
+      if (!full || kmax > wg_qmin) {  // tile touches padding or the diagonal
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          float v = acc_s[kb2][r] * p.scale_log2;
-          if (need_mask) {
+          for (int r = 0; r < 16; ++r) {
             const int key = kb2 * 32 + 8 * (r / 4) + 4 * half + (r % 4);
             const int kblk = key / kBlk, slot = key % kBlk;
             const int kpos = lp[kblk] * kBlk + slot;
             const bool vis = slot < rw[kblk] && kpos <= my_qpos;
-            v = vis ? v : -INFINITY;
+            acc_s[kb2][r] = vis ? acc_s[kb2][r] : -INFINITY;
           }
-          acc_s[kb2][r] = v;
-          mx = fmaxf(mx, v);
-        }
+      }
+      float mx = -INFINITY;
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[kb2][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = m_new == -INFINITY ? 1.f : exp2f(m_run - m_new);
-      const float msub = m_new == -INFINITY ? 0.f : m_new;
+      const float c = p.scale_log2;
+      const float nm = m_new == -INFINITY ? 0.f : -m_new * c;
+      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
+      // rows whose max did not move keep alpha == 1: skip the rescale when
+      // that holds for the whole wavefront (the common case once the max
+      // has settled)
+      if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
+#pragma unroll
+        for (int dt = 0; dt < kD / 32; ++dt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
+      }
       m_run = m_new;
       float lsum = 0.f;
       uint4 pop[4];  // P^T operands for the 4 key steps of 16
@@ -309,17 +344,13 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = exp2f(acc_s[t / 2][8 * (t % 2) + e] - msub);
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(acc_s[t / 2][8 * (t % 2) + e], c, nm));
           lsum += pv[e];
         }
-        pop[t] = make_uint4(pack_bf16x2(pv[0], pv[1]), pack_bf16x2(pv[2], pv[3]),
-                            pack_bf16x2(pv[4], pv[5]), pack_bf16x2(pv[6], pv[7]));
+        pop[t] = make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
+                            cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7]));
       }
       l_lane = l_lane * alpha + lsum;
-#pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
 
       // ---- O^T += V^T P^T --------------------------------------------------
 #pragma unroll
@@ -354,12 +385,12 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams
       for (int i = 0; i < 4; ++i) {
         const int d = dt * 32 + 8 * i + 4 * half;
         uint2 v;
-        v.x = pack_bf16x2(acc_o[dt][4 * i] * inv, acc_o[dt][4 * i + 1] * inv);
-        v.y = pack_bf16x2(acc_o[dt][4 * i + 2] * inv, acc_o[dt][4 * i + 3] * inv);
+        v.x = cvt_pk_bf16(acc_o[dt][4 * i] * inv, acc_o[dt][4 * i + 1] * inv);
+        v.y = cvt_pk_bf16(acc_o[dt][4 * i + 2] * inv, acc_o[dt][4 * i + 3] * inv);
         *reinterpret_cast<uint2*>(out + d) = v;
       }
     if (p.lse && half == 0)
-      p.lse[(size_t(b) * C + my_row) * p.Hq + h] = ok ? (m_run + log2f(L)) * kLn2 : -INFINITY;
+      p.lse[(size_t(b) * C + my_row) * p.Hq + h] = ok ? (m_run * p.scale_log2 + log2f(L)) * kLn2 : -INFINITY;
   } else {
     const size_t n = size_t(b) * p.S + s;
     const size_t row = (n * C + my_row) * p.Hq + h;
@@ -373,7 +404,7 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams
             make_float4(acc_o[dt][4 * i], acc_o[dt][4 * i + 1], acc_o[dt][4 * i + 2], acc_o[dt][4 * i + 3]);
       }
     if (half == 0) {
-      p.m_part[row] = (L > 0.f) ? m_run * kLn2 : -INFINITY;
+      p.m_part[row] = (L > 0.f) ? m_run * p.scale_log2 * kLn2 : -INFINITY;
       p.l_part[row] = L;
     }
   }
