@@ -15,12 +15,13 @@
 //
 // Per 64-key tile and wavefront (one lane = one query row throughout):
 //   S^T[key][row] = K[key][:] . Q[row][:]     A = K from LDS (row-major,
-//                                             XOR-swizzled), B = Q in VGPRs
+//                                             row-padded), B = Q in VGPRs
 //   online softmax over the lane's 32 keys + the other half-wave's 32
-//   O^T[d][row] += V^T[d][key] . P^T[key][row] A = V^T from LDS (stored
-//                                             transposed), B = P in VGPRs:
-//                                             exactly the lane's own S
-//                                             accumulators rounded to bf16
+//   O^T[d][row] += V^T[d][key] . P^T[key][row] A = V^T read from the
+//                                             row-major V tile with the gfx950
+//                                             transpose load (ds_read_b64_tr_b16),
+//                                             B = P in VGPRs: exactly the lane's
+//                                             own S accumulators rounded to bf16
 // Keys come from the sequence's segments in logical order: the workgroup
 // expands its segments into per-block (physical id, logical id) lists in LDS,
 // 512 blocks at a time.  Blocks are loaded through buffer descriptors whose
@@ -41,8 +42,11 @@ constexpr int kD = 128;            // head dim built
 constexpr int kRow = kD * 2;       // bytes per K/V row of one head (bf16)
 constexpr int kBlk = 16;           // tokens per block
 constexpr int kTK = 64;            // keys per tile (4 blocks)
-constexpr int kVtStride = kTK * 2 + 8;  // bytes per V^T row in LDS (padded, 8-aligned)
-constexpr int kChunkBlocks = 512;  // blocks expanded into LDS at a time
+constexpr int kVStride = kRow + 32;     // bytes per V row in LDS (padded: conflict-free
+                                        // transpose reads of 4 keys x 16 d)
+constexpr int kKStride = kRow + 16;     // bytes per K row in LDS (padded: conflict-free
+                                        // column reads with immediate offsets)
+constexpr int kChunkBlocks = 256;  // blocks expanded into LDS at a time
 constexpr int kMaxSplitBlocks = 1 << 20;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kBufferFlags = 0x00020000;
@@ -54,7 +58,6 @@ struct PGeo {
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int NPOS = 32 * WAVES / G;  // query positions per workgroup
   static constexpr int KCHUNKS = kTK * (kRow / 16) / THREADS;  // K 16-B chunks per thread per tile
-  static constexpr int VPAIRS = KCHUNKS / 2;                   // V key pairs per thread per tile
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -66,6 +69,16 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+// gfx950 transpose LDS load: within each 16-lane group, lane i receives
+// element i%4 of the 8-byte words addressed by lanes i/4, i/4+4, i/4+8 and
+// i/4+12 of the group
+__device__ __forceinline__ uint2 ds_read_tr16(const uint8_t* lds_ptr) {
+  const s16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) s16x4_t*)(lds_ptr));
+  return __builtin_bit_cast(uint2, v);
+}
 
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
@@ -90,18 +103,22 @@ __device__ __forceinline__ int wg_search_segment(const msa_segment* segs, int lo
 }
 
 template <int G>
-__global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams p) {
+__global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillParams p) {
   using PG = PGeo<G>;
   constexpr int THREADS = PG::THREADS, NPOS = PG::NPOS;
 
-  __shared__ __align__(16) uint8_t k_lds[2][kTK * kRow];
-  __shared__ __align__(16) uint8_t vt_lds[2][kD * kVtStride];
-  __shared__ int32_t blk_phys[kChunkBlocks];
-  __shared__ int32_t blk_lpos[kChunkBlocks];
-  __shared__ int32_t st_start[kChunkBlocks + 1];
-  __shared__ int32_t st_phys[kChunkBlocks + 1];
-  __shared__ int32_t st_nblk[kChunkBlocks + 1];
-  __shared__ int32_t st_lblk[kChunkBlocks + 1];
+  __shared__ __align__(16) uint8_t k_lds[2][kTK * kKStride];
+  __shared__ __align__(16) uint8_t v_lds[2][kTK * kVStride];
+  __shared__ int32_t blk_rows[kChunkBlocks];  // rows present (0 = block missing)
+  __shared__ int32_t blk_lpos[kChunkBlocks];  // logical block id
+  __shared__ uint2 blk_off[kChunkBlocks];     // byte offset of the block in a pool (64-bit)
+  // segment staging for the chunk expansion; it only lives between chunks,
+  // when no K tile is in LDS, so it shares the second K buffer
+  static_assert(4 * (kChunkBlocks + 1) * sizeof(int32_t) <= sizeof(k_lds[1]), "staging");
+  int32_t* st_start = reinterpret_cast<int32_t*>(&k_lds[1][0]);
+  int32_t* st_phys = st_start + (kChunkBlocks + 1);
+  int32_t* st_nblk = st_phys + (kChunkBlocks + 1);
+  int32_t* st_lblk = st_nblk + (kChunkBlocks + 1);
 
   // XCD-aware order: consecutive workgroup ids go round-robin to the 8 XCDs
   // (each with its own L2).  Remap so that the workgroups one XCD receives
@@ -178,6 +195,10 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams
   // per-thread tile-load coordinates (fixed for the kernel)
   // K: chunk q = tid + THREADS*it -> key row r = q/16, 16-byte chunk c = q%16
   const int kc = tid % 16;
+  // transpose-load source address of this lane inside a V tile: lane 16q+j
+  // of the wavefront points at key 4*(q/2) + j/4 and d 16*(q%2) + 4*(j%4)
+  const int v_lane_off = (4 * (lane / 32) + (lane % 16) / 4) * kVStride +
+                         (16 * ((lane / 16) % 2) + 4 * (lane % 4)) * 2;
   // V: key pair index rp = tid/16 + (THREADS/16)*it -> keys 2rp, 2rp+1; chunk kc
 
   bool done = false;
@@ -206,85 +227,67 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams
       }
       const int off = j - st_start[lo];
       const bool ok = st_phys[lo] >= 0 && off >= 0 && off < st_nblk[lo];
-      blk_phys[jj] = ok ? st_phys[lo] + off : -1;
+      const uint64_t bo = ok ? uint64_t(st_phys[lo] + off) * blk_stride : 0;
+      blk_off[jj] = make_uint2(uint32_t(bo), uint32_t(bo >> 32));
       blk_lpos[jj] = st_lblk[lo] + off;
+      blk_rows[jj] = !ok ? 0 : (j == nAB - 1 ? last_tokens : kBlk);
     }
     __syncthreads();
 
     const int ntiles = (nblk + 3) / 4;
-    // tile loader: global -> registers; registers -> LDS (K swizzled, V^T)
+    // tile loaders: global -> registers; registers -> LDS (padded rows)
     uint4 kreg[PG::KCHUNKS], vreg[PG::KCHUNKS];
-    // Per-block buffer descriptors must be wave-uniform: the block a load
-    // touches is derived from the (uniform) wavefront index, never from the
-    // lane id, or the compiler wraps each load in a readfirstlane loop.
-    auto block_rsrc = [&](const char* base, int ti, int kb) {
-      const int jj = ti * 4 + kb;
-      const int ph = __builtin_amdgcn_readfirstlane(
-          (jj < nblk && ti < ntiles) ? blk_phys[min(jj, kChunkBlocks - 1)] : -1);
-      const int rows = ph < 0 ? 0 : (cb + jj == nAB - 1 ? last_tokens : kBlk);
-      return rsrc(base + size_t(ph < 0 ? 0 : ph) * blk_stride, uint32_t(rows * tok_stride));
+    // Each wavefront loads whole blocks: wave w loads rows of block
+    // (w / WPB) of the tile (WPB = waves per block), so its buffer descriptor
+    // is wave-uniform by construction and built once per tile from the
+    // per-block offset and byte count prepared above.
+    constexpr int WPB = PG::WAVES / 4;                // waves per block
+    constexpr int RPW = kBlk / WPB;                   // rows of the block per wave
+    const int my_blk = w / WPB;
+    const int row0 = (w % WPB) * RPW + lane / 16;     // first row of this lane in the block
+    auto tile_rsrc = [&](const char* base, int ti) {
+      const int jj = ti * 4 + my_blk;
+      const bool in = ti < ntiles && jj < nblk;
+      const int jc = min(jj, kChunkBlocks - 1);
+      const uint2 off = blk_off[jc];
+      const uint32_t lo = __builtin_amdgcn_readfirstlane(in ? off.x : 0u);
+      const uint32_t hi = __builtin_amdgcn_readfirstlane(in ? off.y : 0u);
+      const int rows = __builtin_amdgcn_readfirstlane(in ? blk_rows[jc] : 0);
+      return rsrc(base + ((uint64_t(hi) << 32) | lo), uint32_t(rows * tok_stride));
     };
-    auto issue_tile = [&](int ti) {
+    auto issue_k = [&](int ti) {
+      const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase, ti);
+#pragma unroll
+      for (int it = 0; it < PG::KCHUNKS; ++it)
+        kreg[it] = bload16(r, uint32_t((row0 + 4 * it) * tok_stride + kc * 16));
+    };
+    auto issue_v = [&](int ti) {
+      const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, ti);
+#pragma unroll
+      for (int it = 0; it < PG::KCHUNKS; ++it)
+        vreg[it] = bload16(r, uint32_t((row0 + 4 * it) * tok_stride + kc * 16));
+    };
+    auto store_k = [&](int buf) {
 #pragma unroll
       for (int it = 0; it < PG::KCHUNKS; ++it) {
-        // K: row r = tid/16 + (THREADS/16)*it -> block w/4 + (THREADS/256)*it
-        const int kb = w / 4 + (THREADS / 256) * it;
-        const int slot = (tid / 16) % 16;
-        kreg[it] = bload16(block_rsrc(kbase, ti, kb), uint32_t(slot * tok_stride + kc * 16));
-        // V: key 2rp + it%2 with rp = tid/16 + (THREADS/16)*(it/2)
-        //    -> block w/2 + (THREADS/128)*(it/2), slot 2*((tid/16)%8) + it%2
-        const int vkb = w / 2 + (THREADS / 128) * (it / 2);
-        const int vslot = 2 * ((tid / 16) % 8) + (it % 2);
-        vreg[it] = bload16(block_rsrc(vbase, ti, vkb), uint32_t(vslot * tok_stride + kc * 16));
+        const int r = my_blk * kBlk + row0 + 4 * it;
+        *reinterpret_cast<uint4*>(&k_lds[buf][r * kKStride + kc * 16]) = kreg[it];
       }
     };
-    auto store_tile = [&](int buf) {
+    auto store_v = [&](int buf) {
 #pragma unroll
       for (int it = 0; it < PG::KCHUNKS; ++it) {
-        const int r = tid / 16 + (THREADS / 16) * it;
-        *reinterpret_cast<uint4*>(&k_lds[buf][r * kRow + ((kc ^ (r % 16)) * 16)]) = kreg[it];
-      }
-#pragma unroll
-      for (int pi = 0; pi < PG::VPAIRS; ++pi) {
-        const int rp = tid / 16 + (THREADS / 16) * pi;
-        const uint4 x0 = vreg[2 * pi], x1 = vreg[2 * pi + 1];
-        const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w};
-        const uint32_t a1[4] = {x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          // (V[2rp][d], V[2rp+1][d]) for d = 8kc + 2e and 8kc + 2e + 1
-          const uint32_t lo = __builtin_amdgcn_perm(a1[e], a0[e], 0x05040100u);
-          const uint32_t hi = __builtin_amdgcn_perm(a1[e], a0[e], 0x07060302u);
-          const int d = 8 * kc + 2 * e;
-          *reinterpret_cast<uint32_t*>(&vt_lds[buf][d * kVtStride + 4 * rp]) = lo;
-          *reinterpret_cast<uint32_t*>(&vt_lds[buf][(d + 1) * kVtStride + 4 * rp]) = hi;
-        }
+        const int r = my_blk * kBlk + row0 + 4 * it;
+        *reinterpret_cast<uint4*>(&v_lds[buf][r * kVStride + kc * 16]) = vreg[it];
       }
     };
-
-    issue_tile(0);
-    store_tile(0);
-    __syncthreads();
-    for (int ti = 0; ti < ntiles; ++ti) {
-      const int buf = ti & 1;
-      // uniform facts about this tile
-      int lp[4], rw[4];
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int jj = ti * 4 + k;
-        const int ph = jj < nblk ? blk_phys[jj] : -1;
-        lp[k] = jj < nblk ? blk_lpos[jj] : 0x3fffffff;
-        rw[k] = ph < 0 ? 0 : (cb + jj == nAB - 1 ? last_tokens : kBlk);
-      }
-      const int kmin = lp[0] * kBlk;
-      if (kmin > wg_qmax) {  // this and every later key is after every row
-        done = true;
-        break;
-      }
-      if (ti + 1 < ntiles) issue_tile(ti + 1);  // next tile in flight
-
-      // ---- S^T = K Q^T for 2 x 32 keys ------------------------------------
-      f32x16_t acc_s[2];
+    // tile ti starts at or after every row of this workgroup: it and every
+    // later tile are fully masked
+    auto past_rows = [&](int ti) {
+      return ti >= ntiles || blk_lpos[min(ti * 4, kChunkBlocks - 1)] * kBlk > wg_qmax;
+    };
+    // S^T = K Q^T for the 2 x 32 keys of the tile in K buffer kbuf
+    auto scores = [&](int kbuf, f32x16_t* acc) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
         const int krow = kb2 * 32 + lr;
@@ -292,15 +295,47 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams
 #pragma unroll
         for (int k = 0; k < kD / 16; ++k) {
           const uint4 a = *reinterpret_cast<const uint4*>(
-              &k_lds[buf][krow * kRow + (((2 * k + half) ^ (krow % 16)) * 16)]);
-          acc_s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qop[k]),
-                                                               k == 0 ? zero : acc_s[kb2], 0, 0, 0);
+              &k_lds[kbuf][krow * kKStride + (2 * k + half) * 16]);
+          acc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qop[k]),
+                                                             k == 0 ? zero : acc[kb2], 0, 0, 0);
         }
       }
+    };
 
-      // ---- mask + online softmax (lane = query row) ----------------------
+    // Pipeline: K runs one tile ahead of V.  At the top of iteration ti the
+    // LDS holds K(ti+1) and V(ti), the registers hold S(ti), and the loads
+    // of K(ti+2) and V(ti+1) go out.  The QK MFMAs of tile ti+1 are issued
+    // next to the softmax of tile ti (independent work the MFMA and VALU
+    // pipes execute together), then PV of tile ti.
+    if (past_rows(0)) {
+      done = true;
+      continue;
+    }
+    issue_k(0);
+    issue_v(0);
+    store_k(0);
+    store_v(0);
+    issue_k(1);
+    store_k(1);
+    __syncthreads();
+    f32x16_t s_cur[2], s_nxt[2];
+    scores(0, s_cur);
+    for (int ti = 0; ti < ntiles; ++ti) {
+      const bool more = !past_rows(ti + 1);
+      issue_k(ti + 2);           // past the chunk: zero-row descriptors, no traffic
+      issue_v(ti + 1);
+      if (more) scores((ti + 1) & 1, s_nxt);
+
+      // ---- mask + online softmax of tile ti (lane = query row) -----------
       // Scores stay unscaled; scale*log2(e) is folded into one FMA inside
       // the exponent (exp2 of scale*(s - m)), exact max tracking per row.
+      int lp[4], rw[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int jj = ti * 4 + k;
+        lp[k] = jj < nblk ? blk_lpos[min(jj, kChunkBlocks - 1)] : 0x3fffffff;
+        rw[k] = jj < nblk ? blk_rows[min(jj, kChunkBlocks - 1)] : 0;
+      }
       bool full = true;
 #pragma unroll
       for (int k = 0; k < 4; ++k) full = full && rw[k] == kBlk;
@@ -314,14 +349,14 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams
             const int kblk = key / kBlk, slot = key % kBlk;
             const int kpos = lp[kblk] * kBlk + slot;
             const bool vis = slot < rw[kblk] && kpos <= my_qpos;
-            acc_s[kb2][r] = vis ? acc_s[kb2][r] : -INFINITY;
+            s_cur[kb2][r] = vis ? s_cur[kb2][r] : -INFINITY;
           }
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, acc_s[kb2][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb2][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
       const float m_new = fmaxf(m_run, mx);
       const float c = p.scale_log2;
@@ -337,39 +372,50 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS) prefill_kernel(PrefillParams
           for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
       }
       m_run = m_new;
+      // ---- P and O^T += V^T P^T for tile ti, one key step of 16 at a time --
+      // (each P operand is built right before its four MFMAs, so only one is
+      // live)
       float lsum = 0.f;
-      uint4 pop[4];  // P^T operands for the 4 key steps of 16
+      const int vb = ti & 1;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(acc_s[t / 2][8 * (t % 2) + e], c, nm));
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(s_cur[t / 2][8 * (t % 2) + e], c, nm));
           lsum += pv[e];
         }
-        pop[t] = make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
-                            cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7]));
-      }
-      l_lane = l_lane * alpha + lsum;
-
-      // ---- O^T += V^T P^T --------------------------------------------------
+        const uint4 pop = make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
+                                     cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7]));
 #pragma unroll
-      for (int dt = 0; dt < kD / 32; ++dt) {
-        const int d = dt * 32 + lr;
-#pragma unroll
-        for (int t = 0; t < 4; ++t) {
-          const uint8_t* vrow = &vt_lds[buf][d * kVtStride];
-          const u32x2_t lo2 = *reinterpret_cast<const u32x2_t*>(vrow + (16 * t + 4 * half) * 2);
-          const u32x2_t hi2 = *reinterpret_cast<const u32x2_t*>(vrow + (16 * t + 8 + 4 * half) * 2);
+        for (int dt = 0; dt < kD / 32; ++dt) {
+          // A operand (V^T, 32 d x 16 keys): two transpose loads of 4 keys x
+          // 16 d per 16-lane group; k-slots 0..3 <- keys 16t+4h+0..3, 4..7 <-
+          // keys 16t+8+4h+0..3 (the same key order as the P operand)
+          const uint8_t* vb0 = &v_lds[vb][0] + v_lane_off + (16 * t) * kVStride + dt * 64;
+          const uint2 lo2 = ds_read_tr16(vb0);
+          const uint2 hi2 = ds_read_tr16(vb0 + 8 * kVStride);
           const uint4 a = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
-          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pop[t]),
+          acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pop),
                                                               acc_o[dt], 0, 0, 0);
         }
       }
-
-      if (ti + 1 < ntiles) store_tile(buf ^ 1);
+      l_lane = l_lane * alpha + lsum;
+      if (!more) {
+        // either the chunk is exhausted (go on with the next one) or the next
+        // tile starts after every row (stop: later keys are later still)
+        done = ti + 1 < ntiles;
+        break;
+      }
+      // K(ti+2) replaces K(ti) (consumed last iteration); V(ti+1) replaces
+      // V(ti-1) (consumed last iteration); every wavefront passed the barrier
+      store_k(ti & 1);
+      store_v((ti + 1) & 1);
       __syncthreads();
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; ++kb2) s_cur[kb2] = s_nxt[kb2];
     }
+    __syncthreads();
   }
 
   // ---- finish: combine the two half-waves' sums, write O and LSE --------
