@@ -318,17 +318,17 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
     issue_k(1);
     store_k(1);
     __syncthreads();
-    f32x16_t s_cur[2], s_nxt[2];
-    scores(0, s_cur);
-    for (int ti = 0; ti < ntiles; ++ti) {
+    f32x16_t s_a[2], s_b[2];
+    scores(0, s_a);
+    // One pipeline step for tile ti: scores of ti are in sc, those of ti+1
+    // go to sn.  Returns true when this chunk is finished.
+    auto step = [&](int ti, f32x16_t* sc, f32x16_t* sn) -> bool {
       const bool more = !past_rows(ti + 1);
       issue_k(ti + 2);           // past the chunk: zero-row descriptors, no traffic
       issue_v(ti + 1);
-      if (more) scores((ti + 1) & 1, s_nxt);
+      if (more) scores((ti + 1) & 1, sn);
 
       // ---- mask + online softmax of tile ti (lane = query row) -----------
-      // Scores stay unscaled; scale*log2(e) is folded into one FMA inside
-      // the exponent (exp2 of scale*(s - m)), exact max tracking per row.
       int lp[4], rw[4];
 #pragma unroll
       for (int k = 0; k < 4; ++k) {
@@ -349,29 +349,32 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
             const int kblk = key / kBlk, slot = key % kBlk;
             const int kpos = lp[kblk] * kBlk + slot;
             const bool vis = slot < rw[kblk] && kpos <= my_qpos;
-            s_cur[kb2][r] = vis ? s_cur[kb2][r] : -INFINITY;
+            sc[kb2][r] = vis ? sc[kb2][r] : -INFINITY;
           }
       }
       float mx = -INFINITY;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, s_cur[kb2][r]);
+        for (int r = 0; r < 16; ++r) mx = fmaxf(mx, sc[kb2][r]);
       mx = fmaxf(mx, __shfl_xor(mx, 32));
-      const float m_new = fmaxf(m_run, mx);
+      // Lazy rescaling: a row keeps its reference max m_run until the true
+      // max exceeds it by more than 2^8 in the exponent; the weights are then
+      // at most 256 (harmless for fp32 sums and for bf16's relative
+      // precision) and the accumulator rescale is skipped in almost every
+      // tile.  The LSE stays exact: it is m_run*scale + log2(sum).
       const float c = p.scale_log2;
-      const float nm = m_new == -INFINITY ? 0.f : -m_new * c;
-      const float alpha = m_new == -INFINITY ? 1.f : __builtin_amdgcn_exp2f((m_run - m_new) * c);
-      // rows whose max did not move keep alpha == 1: skip the rescale when
-      // that holds for the whole wavefront (the common case once the max
-      // has settled)
-      if (__builtin_amdgcn_ballot_w64(m_new != m_run) != 0) {
+      const bool bump = (mx - m_run) * c > 8.f;  // true on the first visible key
+      const float m_use = bump ? mx : m_run;
+      const float nm = m_use == -INFINITY ? 0.f : -m_use * c;
+      const float alpha = (m_use == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_use) * c);
+      if (__builtin_amdgcn_ballot_w64(bump) != 0) {
 #pragma unroll
         for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
       }
-      m_run = m_new;
+      m_run = m_use;
       // ---- P and O^T += V^T P^T for tile ti, one key step of 16 at a time --
       // (each P operand is built right before its four MFMAs, so only one is
       // live)
@@ -382,7 +385,7 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
         float pv[8];
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          pv[e] = __builtin_amdgcn_exp2f(fmaf(s_cur[t / 2][8 * (t % 2) + e], c, nm));
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[t / 2][8 * (t % 2) + e], c, nm));
           lsum += pv[e];
         }
         const uint4 pop = make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
@@ -405,15 +408,19 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
         // either the chunk is exhausted (go on with the next one) or the next
         // tile starts after every row (stop: later keys are later still)
         done = ti + 1 < ntiles;
-        break;
+        return true;
       }
-      // K(ti+2) replaces K(ti) (consumed last iteration); V(ti+1) replaces
-      // V(ti-1) (consumed last iteration); every wavefront passed the barrier
+      // K(ti+2) replaces K(ti) (consumed last step); V(ti+1) replaces V(ti-1)
+      // (consumed last step); every wavefront passed the barrier
       store_k(ti & 1);
       store_v((ti + 1) & 1);
       __syncthreads();
-#pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) s_cur[kb2] = s_nxt[kb2];
+      return false;
+    };
+    // unrolled by two so the score registers swap roles without copies
+    for (int ti = 0;; ti += 2) {
+      if (step(ti, s_a, s_b)) break;
+      if (step(ti + 1, s_b, s_a)) break;
     }
     __syncthreads();
   }
