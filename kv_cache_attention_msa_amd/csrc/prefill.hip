@@ -326,7 +326,6 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
       const bool more = !past_rows(ti + 1);
       issue_k(ti + 2);           // past the chunk: zero-row descriptors, no traffic
       issue_v(ti + 1);
-      if (more) scores((ti + 1) & 1, sn);
 
       // ---- mask + online softmax of tile ti (lane = query row) -----------
       int lp[4], rw[4];
@@ -352,6 +351,10 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
             sc[kb2][r] = vis ? sc[kb2][r] : -INFINITY;
           }
       }
+      // QK of tile ti+1, unconditionally and in the same basic block as the
+      // softmax of tile ti so that MFMA and VALU work interleave (past the
+      // last tile the LDS holds zero rows and the result goes unused)
+      scores((ti + 1) & 1, sn);
       float mx = -INFINITY;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
