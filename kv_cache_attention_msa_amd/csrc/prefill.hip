@@ -239,20 +239,46 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
     uint4 kreg[PG::KCHUNKS], vreg[PG::KCHUNKS];
     // Each wavefront loads whole blocks: wave w loads rows of block
     // (w / WPB) of the tile (WPB = waves per block), so its buffer descriptor
-    // is wave-uniform by construction and built once per tile from the
-    // per-block offset and byte count prepared above.
+    // is wave-uniform by construction.
     constexpr int WPB = PG::WAVES / 4;                // waves per block
     constexpr int RPW = kBlk / WPB;                   // rows of the block per wave
+    static_assert(kChunkBlocks == 4 * kWave, "one tile of the chunk per lane");
     const int my_blk = w / WPB;
     const int row0 = (w % WPB) * RPW + lane / 16;     // first row of this lane in the block
+    // Per-tile bookkeeping in registers, lane t <-> tile t of the chunk: the
+    // pool offset and row count of the block this wavefront loads for tile
+    // t (read back with v_readlane, no LDS round trip in the tile loop), and
+    // two wave masks: tiles at or past the last row of the workgroup, and
+    // tiles that need the per-element mask (padding rows or the diagonal).
+    uint32_t t_off_lo, t_off_hi;
+    int t_rows;
+    uint64_t past_mask, mask_mask;
+    {
+      const int jl = lane * 4 + my_blk;
+      const bool in = jl < nblk;
+      const uint2 off = blk_off[jl];
+      t_off_lo = in ? off.x : 0u;
+      t_off_hi = in ? off.y : 0u;
+      t_rows = in ? blk_rows[jl] : 0;
+      const int jt = lane * 4;
+      bool full = jt + 3 < nblk;
+      int lp_last = 0;
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int jj = min(jt + k, nblk - 1);
+        full = full && blk_rows[jj] == kBlk;
+        lp_last = blk_lpos[jj];
+      }
+      const bool past = lane >= ntiles || blk_lpos[min(jt, nblk - 1)] * kBlk > wg_qmax;
+      const bool need = !full || lp_last * kBlk + kBlk - 1 > wg_qmin;
+      past_mask = __builtin_amdgcn_ballot_w64(past);
+      mask_mask = __builtin_amdgcn_ballot_w64(need);
+    }
     auto tile_rsrc = [&](const char* base, int ti) {
-      const int jj = ti * 4 + my_blk;
-      const bool in = ti < ntiles && jj < nblk;
-      const int jc = min(jj, kChunkBlocks - 1);
-      const uint2 off = blk_off[jc];
-      const uint32_t lo = __builtin_amdgcn_readfirstlane(in ? off.x : 0u);
-      const uint32_t hi = __builtin_amdgcn_readfirstlane(in ? off.y : 0u);
-      const int rows = __builtin_amdgcn_readfirstlane(in ? blk_rows[jc] : 0);
+      const int tl = min(ti, kWave - 1);
+      const uint32_t lo = __builtin_amdgcn_readlane(t_off_lo, tl);
+      const uint32_t hi = __builtin_amdgcn_readlane(t_off_hi, tl);
+      const int rows = ti < kWave ? __builtin_amdgcn_readlane(t_rows, tl) : 0;
       return rsrc(base + ((uint64_t(hi) << 32) | lo), uint32_t(rows * tok_stride));
     };
     auto issue_k = [&](int ti) {
@@ -283,9 +309,7 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
     };
     // tile ti starts at or after every row of this workgroup: it and every
     // later tile are fully masked
-    auto past_rows = [&](int ti) {
-      return ti >= ntiles || blk_lpos[min(ti * 4, kChunkBlocks - 1)] * kBlk > wg_qmax;
-    };
+    auto past_rows = [&](int ti) { return ti >= kWave || ((past_mask >> ti) & 1); };
     // S^T = K Q^T for the 2 x 32 keys of the tile in K buffer kbuf
     auto scores = [&](int kbuf, f32x16_t* acc) {
 #pragma unroll
@@ -328,18 +352,14 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
       issue_v(ti + 1);
 
       // ---- mask + online softmax of tile ti (lane = query row) -----------
-      int lp[4], rw[4];
+      if ((mask_mask >> ti) & 1) {  // tile touches padding or the diagonal
+        int lp[4], rw[4];
 #pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        const int jj = ti * 4 + k;
-        lp[k] = jj < nblk ? blk_lpos[min(jj, kChunkBlocks - 1)] : 0x3fffffff;
-        rw[k] = jj < nblk ? blk_rows[min(jj, kChunkBlocks - 1)] : 0;
-      }
-      bool full = true;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) full = full && rw[k] == kBlk;
-      const int kmax = lp[3] * kBlk + kBlk - 1;
-      if (!full || kmax > wg_qmin) {  // tile touches padding or the diagonal
+        for (int k = 0; k < 4; ++k) {
+          const int jj = ti * 4 + k;
+          lp[k] = jj < nblk ? blk_lpos[jj] : 0x07ffffff;
+          rw[k] = jj < nblk ? blk_rows[jj] : 0;
+        }
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
