@@ -7,11 +7,11 @@
 // This is a dense contraction, so QK^T and PV run on bf16 MFMA
 // (v_mfma_f32_32x32x16_bf16) with fp32 accumulation.
 //
-// Workgroup = (query-position tile, KV head g, sequence b [, split s]).
-// The G query heads of KV head g are stacked: each wavefront owns one
-// 32-row tile (one head, 32 consecutive positions), so every K/V tile
-// staged in LDS is used by all G heads (GQA reuse) and by all positions of
-// the workgroup.
+// Workgroup = (query-position tile, KV head g, sequence b [, split s]),
+// eight wavefronts.  The G query heads of KV head g are stacked: each
+// wavefront owns one 32-row tile (one head, 32 consecutive positions), so
+// every K/V tile staged in LDS is used by all G heads (GQA reuse) and by
+// all 256/G positions of the workgroup.
 //
 // Per 64-key tile and wavefront (one lane = one query row throughout):
 //   S^T[key][row] = K[key][:] . Q[row][:]     A = K from LDS (row-major,
@@ -52,9 +52,12 @@ constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kXcds = 8;  // accelerator complex dies on MI355X, one L2 each
 
+// Eight wavefronts per workgroup and one workgroup per CU: every K/V tile
+// staged in LDS feeds 8 x 32 query rows, which halves the global loads and
+// LDS stores per MFMA against two independent 4-wave workgroups.
 template <int G>
 struct PGeo {
-  static constexpr int WAVES = G <= 4 ? 4 : G;
+  static constexpr int WAVES = 8;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int NPOS = 32 * WAVES / G;  // query positions per workgroup
   static constexpr int KCHUNKS = kTK * (kRow / 16) / THREADS;  // K 16-B chunks per thread per tile
@@ -507,13 +510,13 @@ SplitPlan prefill_split(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t m
   SplitPlan sp;
   const int64_t nbm = (int64_t(max_ctx_len) + block_size - 1) / block_size;
   const int G = Hkv > 0 ? Hq / Hkv : 1;
-  const int npos = G <= 4 ? 128 / (G > 0 ? G : 1) : 32;
+  const int npos = 256 / (G > 0 ? G : 1);
   const int64_t wgs = int64_t((C + npos - 1) / npos) * Hkv * B;
   int64_t T = split_blocks;
   if (T <= 0) {
     // split the key stream only when the grid alone cannot fill the chip
-    // (two workgroups per CU on 256 CUs); never below 64 blocks per split
-    int64_t S = wgs >= 512 ? 1 : (512 + wgs - 1) / wgs;
+    // (one workgroup per CU on 256 CUs); never below 64 blocks per split
+    int64_t S = wgs >= 256 ? 1 : (256 + wgs - 1) / wgs;
     T = nbm > 0 ? (nbm + S - 1) / S : 1;
     if (T < 64) T = 64;
   }
