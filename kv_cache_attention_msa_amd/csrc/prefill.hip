@@ -42,10 +42,9 @@ constexpr int kD = 128;            // head dim built
 constexpr int kRow = kD * 2;       // bytes per K/V row of one head (bf16)
 constexpr int kBlk = 16;           // tokens per block
 constexpr int kTK = 64;            // keys per tile (4 blocks)
-constexpr int kVStride = kRow + 32;     // bytes per V row in LDS (padded: conflict-free
-                                        // transpose reads of 4 keys x 16 d)
-constexpr int kKStride = kRow + 16;     // bytes per K row in LDS (padded: conflict-free
-                                        // column reads with immediate offsets)
+constexpr int kTileBytes = kTK * kRow;  // one K or V tile in LDS (16 KB)
+constexpr int kUnit = 1024;             // one LDS DMA unit: 16 keys of a block x 64 B of d
+constexpr int kStages = 3;              // K and V tiles resident or in flight
 constexpr int kChunkBlocks = 256;  // blocks expanded into LDS at a time
 constexpr int kMaxSplitBlocks = 1 << 20;
 constexpr float kLn2 = 0.69314718055994530942f;
@@ -60,7 +59,6 @@ struct PGeo {
   static constexpr int WAVES = 8;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int NPOS = 32 * WAVES / G;  // query positions per workgroup
-  static constexpr int KCHUNKS = kTK * (kRow / 16) / THREADS;  // K 16-B chunks per thread per tile
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* base, uint32_t bytes) {
@@ -72,6 +70,20 @@ __device__ __forceinline__ uint4 bload16(__amdgpu_buffer_rsrc_t r, uint32_t off)
 }
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_cast(bf16x8_t, x); }
+
+// Wavefront-wide LDS DMA (gfx950 buffer_load_dwordx4 ... lds): lane i loads
+// 16 bytes at byte offset voff of the buffer and the data lands in LDS at
+// lds_addr + 16*i, without passing through VGPRs.  Lanes outside the
+// descriptor's range write zeros.  Completion is counted by vmcnt; the
+// compiler does not track these, so the tile loop waits for them itself.
+__device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t lds_addr, uint32_t voff) {
+  asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
+               :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
+}
+// LDS byte address of a pointer into __shared__ memory
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return uint32_t(size_t((const __attribute__((address_space(3))) uint8_t*)(p)));
+}
 
 typedef short s16x4_t __attribute__((ext_vector_type(4)));
 // gfx950 transpose LDS load: within each 16-lane group, lane i receives
@@ -110,13 +122,16 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
   using PG = PGeo<G>;
   constexpr int THREADS = PG::THREADS, NPOS = PG::NPOS;
 
-  __shared__ __align__(16) uint8_t k_lds[2][kTK * kKStride];
-  __shared__ __align__(16) uint8_t v_lds[2][kTK * kVStride];
+  // K and V tiles in MFMA-operand order (see the DMA unit layout below),
+  // three stages each: one being read, one landed or landing, one in flight
+  __shared__ __align__(16) uint8_t k_lds[kStages][kTileBytes];
+  __shared__ __align__(16) uint8_t v_lds[kStages][kTileBytes];
   __shared__ int32_t blk_rows[kChunkBlocks];  // rows present (0 = block missing)
   __shared__ int32_t blk_lpos[kChunkBlocks];  // logical block id
   __shared__ uint2 blk_off[kChunkBlocks];     // byte offset of the block in a pool (64-bit)
   // segment staging for the chunk expansion; it only lives between chunks,
-  // when no K tile is in LDS, so it shares the second K buffer
+  // when no K tile is in LDS and no DMA is in flight, so it shares the
+  // second K buffer
   static_assert(4 * (kChunkBlocks + 1) * sizeof(int32_t) <= sizeof(k_lds[1]), "staging");
   int32_t* st_start = reinterpret_cast<int32_t*>(&k_lds[1][0]);
   int32_t* st_phys = st_start + (kChunkBlocks + 1);
@@ -181,6 +196,12 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
     const uint32_t off = uint32_t((pt * 32 + lr) * row_bytes + size_t(h) * kRow + half * 16);
 #pragma unroll
     for (int k = 0; k < kD / 16; ++k) qop[k] = bload16(qr, off + k * 32);
+    // consume Q here: the compiler's wait for these loads then sits before
+    // the first tile DMA instead of inside the tile pipeline, where it would
+    // also wait for DMAs still in flight
+#pragma unroll
+    for (int k = 0; k < kD / 16; ++k)
+      asm volatile("" ::"v"(qop[k].x), "v"(qop[k].y), "v"(qop[k].z), "v"(qop[k].w));
   }
 
   f32x16_t acc_o[kD / 32];
@@ -195,14 +216,31 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
   const char* kbase = static_cast<const char*>(p.k_pool) + size_t(g) * kRow;
   const char* vbase = static_cast<const char*>(p.v_pool) + size_t(g) * kRow;
 
-  // per-thread tile-load coordinates (fixed for the kernel)
-  // K: chunk q = tid + THREADS*it -> key row r = q/16, 16-byte chunk c = q%16
-  const int kc = tid % 16;
-  // transpose-load source address of this lane inside a V tile: lane 16q+j
-  // of the wavefront points at key 4*(q/2) + j/4 and d 16*(q%2) + 4*(j%4)
-  const int v_lane_off = (4 * (lane / 32) + (lane % 16) / 4) * kVStride +
-                         (16 * ((lane / 16) % 2) + 4 * (lane % 4)) * 2;
-  // V: key pair index rp = tid/16 + (THREADS/16)*it -> keys 2rp, 2rp+1; chunk kc
+  // ---- LDS tile layout --------------------------------------------------
+  // A tile (64 keys = 4 blocks) is 16 DMA units of 1 KB; unit u covers block
+  // u/4 (16 keys) and a 64-byte quarter u%4 of the head dimension.  The
+  // bytes of a unit are placed so that the MFMA operand reads are lane-linear
+  // (conflict-free, immediate offsets):
+  //   K unit (block b, quarter c): slot i holds key i%16 of block b, 16-B d
+  //     chunk 4c + i/16.  The A operand of QK step (kb2, k) for lane l is key
+  //     32 kb2 + l%32, d chunk 2k + l/32, i.e. unit (2 kb2 + bit4(l), k/2),
+  //     slot l%16 + 16 (2 (k%2) + bit5(l)).
+  //   V unit (block t, quarter dt): two 512-byte halves h, one per
+  //     transpose read; 8-byte slot L of half h holds key 8h + 4(L/32) +
+  //     (L%16)/4 of block t, d = 32 dt + 16((L/16)%2) + 4(L%4) .. +3, the word
+  //     lane L of the read must point at.  DMA lane i writes slots 2(i%32)
+  //     and 2(i%32)+1 of half i/32: 8 consecutive d of one key.
+  // Wavefront w loads units 2w and 2w+1 of both K and V: all from block w/2.
+  static_assert(PG::WAVES == 8, "DMA split assumes eight wavefronts");
+  const int w2 = w % 2;
+  const uint32_t k_voff0 = uint32_t((lane % 16) * tok_stride + (8 * w2 + lane / 16) * 16);
+  const int vkey = 8 * (lane / 32) + 4 * ((lane % 32) / 16) + (lane % 8) / 2;
+  const int vd = 16 * (((lane % 32) / 8) % 2) + 8 * (lane % 2);
+  const uint32_t v_voff0 = uint32_t(vkey * tok_stride + 2 * (64 * w2 + vd));
+  const uint32_t dma_dst = uint32_t(2 * w * kUnit);
+  // operand-read offsets of this lane
+  const int k_lane_off = 4096 * ((lane >> 4) & 1) + 16 * (lane % 16) + 256 * (lane >> 5);
+  const int v_lane_off = 8 * lane;
 
   bool done = false;
   for (int cb = j_begin; cb < j_end && !done; cb += kChunkBlocks) {
@@ -238,21 +276,15 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
     __syncthreads();
 
     const int ntiles = (nblk + 3) / 4;
-    // tile loaders: global -> registers; registers -> LDS (padded rows)
-    uint4 kreg[PG::KCHUNKS], vreg[PG::KCHUNKS];
-    // Each wavefront loads whole blocks: wave w loads rows of block
-    // (w / WPB) of the tile (WPB = waves per block), so its buffer descriptor
-    // is wave-uniform by construction.
-    constexpr int WPB = PG::WAVES / 4;                // waves per block
-    constexpr int RPW = kBlk / WPB;                   // rows of the block per wave
-    static_assert(kChunkBlocks == 4 * kWave, "one tile of the chunk per lane");
-    const int my_blk = w / WPB;
-    const int row0 = (w % WPB) * RPW + lane / 16;     // first row of this lane in the block
+    // Each wavefront loads whole units of block w/2 of every tile, so its
+    // buffer descriptor is wave-uniform by construction.
+    const int my_blk = w / 2;
     // Per-tile bookkeeping in registers, lane t <-> tile t of the chunk: the
     // pool offset and row count of the block this wavefront loads for tile
     // t (read back with v_readlane, no LDS round trip in the tile loop), and
     // two wave masks: tiles at or past the last row of the workgroup, and
     // tiles that need the per-element mask (padding rows or the diagonal).
+    static_assert(kChunkBlocks == 4 * kWave, "one tile of the chunk per lane");
     uint32_t t_off_lo, t_off_hi;
     int t_rows;
     uint64_t past_mask, mask_mask;
@@ -277,82 +309,78 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
       past_mask = __builtin_amdgcn_ballot_w64(past);
       mask_mask = __builtin_amdgcn_ballot_w64(need);
     }
-    auto tile_rsrc = [&](const char* base, int ti) {
+    // buffer descriptor of this wavefront's block of tile ti; tiles past the
+    // chunk get an empty range, so their DMA writes zeros and reads nothing
+    auto tile_desc = [&](const char* base, int ti) {
       const int tl = min(ti, kWave - 1);
       const uint32_t lo = __builtin_amdgcn_readlane(t_off_lo, tl);
       const uint32_t hi = __builtin_amdgcn_readlane(t_off_hi, tl);
       const int rows = ti < kWave ? __builtin_amdgcn_readlane(t_rows, tl) : 0;
-      return rsrc(base + ((uint64_t(hi) << 32) | lo), uint32_t(rows * tok_stride));
+      const uint64_t a = reinterpret_cast<uint64_t>(base) + ((uint64_t(hi) << 32) | lo);
+      const u32x4_t r = {uint32_t(a), uint32_t(a >> 32) & 0xffffu, uint32_t(rows * tok_stride),
+                         uint32_t(kBufferFlags)};
+      return r;
     };
+    // two DMAs each: units 2w and 2w+1 of the tile into stage ti % 3
     auto issue_k = [&](int ti) {
-      const __amdgpu_buffer_rsrc_t r = tile_rsrc(kbase, ti);
-#pragma unroll
-      for (int it = 0; it < PG::KCHUNKS; ++it)
-        kreg[it] = bload16(r, uint32_t((row0 + 4 * it) * tok_stride + kc * 16));
+      const u32x4_t r = tile_desc(kbase, ti);
+      const uint32_t dst = lds_addr(&k_lds[ti % kStages][0]) + dma_dst;
+      dma16(r, dst, k_voff0);
+      dma16(r, dst + kUnit, k_voff0 + 64);
     };
     auto issue_v = [&](int ti) {
-      const __amdgpu_buffer_rsrc_t r = tile_rsrc(vbase, ti);
-#pragma unroll
-      for (int it = 0; it < PG::KCHUNKS; ++it)
-        vreg[it] = bload16(r, uint32_t((row0 + 4 * it) * tok_stride + kc * 16));
+      const u32x4_t r = tile_desc(vbase, ti);
+      const uint32_t dst = lds_addr(&v_lds[ti % kStages][0]) + dma_dst;
+      dma16(r, dst, v_voff0);
+      dma16(r, dst + kUnit, v_voff0 + 64);
     };
-    auto store_k = [&](int buf) {
-#pragma unroll
-      for (int it = 0; it < PG::KCHUNKS; ++it) {
-        const int r = my_blk * kBlk + row0 + 4 * it;
-        *reinterpret_cast<uint4*>(&k_lds[buf][r * kKStride + kc * 16]) = kreg[it];
-      }
-    };
-    auto store_v = [&](int buf) {
-#pragma unroll
-      for (int it = 0; it < PG::KCHUNKS; ++it) {
-        const int r = my_blk * kBlk + row0 + 4 * it;
-        *reinterpret_cast<uint4*>(&v_lds[buf][r * kVStride + kc * 16]) = vreg[it];
-      }
-    };
+    // the DMAs of the current step (four) may stay in flight; everything
+    // older has landed in LDS
+    auto wait_older = [] { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
     // tile ti starts at or after every row of this workgroup: it and every
     // later tile are fully masked
     auto past_rows = [&](int ti) { return ti >= kWave || ((past_mask >> ti) & 1); };
-    // S^T = K Q^T for the 2 x 32 keys of the tile in K buffer kbuf
-    auto scores = [&](int kbuf, f32x16_t* acc) {
+    // S^T = K Q^T for the 2 x 32 keys of the K tile at kt
+    auto scores = [&](const uint8_t* kt, f32x16_t* acc) {
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const int krow = kb2 * 32 + lr;
         const f32x16_t zero = {};
 #pragma unroll
         for (int k = 0; k < kD / 16; ++k) {
           const uint4 a = *reinterpret_cast<const uint4*>(
-              &k_lds[kbuf][krow * kKStride + (2 * k + half) * 16]);
+              kt + k_lane_off + 8192 * kb2 + 1024 * (k / 2) + 512 * (k % 2));
           acc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qop[k]),
                                                              k == 0 ? zero : acc[kb2], 0, 0, 0);
         }
       }
     };
 
-    // Pipeline: K runs one tile ahead of V.  At the top of iteration ti the
-    // LDS holds K(ti+1) and V(ti), the registers hold S(ti), and the loads
-    // of K(ti+2) and V(ti+1) go out.  The QK MFMAs of tile ti+1 are issued
-    // next to the softmax of tile ti (independent work the MFMA and VALU
-    // pipes execute together), then PV of tile ti.
+    // Pipeline: K runs one tile ahead of V, and the DMAs two tiles ahead of
+    // their use.  At the top of step ti the LDS holds K(ti+1) and V(ti), the
+    // registers hold S(ti), K(ti+2) and V(ti+1) are landing, and the DMAs of
+    // K(ti+3) and V(ti+2) go out into the stages read in step ti-1.  The QK
+    // MFMAs of tile ti+1 are issued next to the softmax of tile ti
+    // (independent work the MFMA and VALU pipes execute together), then PV
+    // of tile ti.
     if (past_rows(0)) {
       done = true;
       continue;
     }
     issue_k(0);
     issue_v(0);
-    store_k(0);
-    store_v(0);
     issue_k(1);
-    store_k(1);
+    issue_k(2);
+    issue_v(1);
+    wait_older();
     __syncthreads();
     f32x16_t s_a[2], s_b[2];
-    scores(0, s_a);
+    scores(&k_lds[0][0], s_a);
     // One pipeline step for tile ti: scores of ti are in sc, those of ti+1
     // go to sn.  Returns true when this chunk is finished.
     auto step = [&](int ti, f32x16_t* sc, f32x16_t* sn) -> bool {
       const bool more = !past_rows(ti + 1);
-      issue_k(ti + 2);           // past the chunk: zero-row descriptors, no traffic
-      issue_v(ti + 1);
+      issue_k(ti + 3);
+      issue_v(ti + 2);
 
       // ---- mask + online softmax of tile ti (lane = query row) -----------
       if ((mask_mask >> ti) & 1) {  // tile touches padding or the diagonal
@@ -374,10 +402,6 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
             sc[kb2][r] = vis ? sc[kb2][r] : -INFINITY;
           }
       }
-      // QK of tile ti+1, unconditionally and in the same basic block as the
-      // softmax of tile ti so that MFMA and VALU work interleave (past the
-      // last tile the LDS holds zero rows and the result goes unused)
-      scores((ti + 1) & 1, sn);
       float mx = -INFINITY;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
@@ -401,11 +425,16 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
           for (int r = 0; r < 16; ++r) acc_o[dt][r] *= alpha;
       }
       m_run = m_use;
+      // QK of tile ti+1, unconditionally and in the same basic block as the
+      // exponentials and PV of tile ti so that MFMA and VALU work interleave
+      // (past the last tile the stage holds zero rows and the result goes
+      // unused)
+      scores(&k_lds[(ti + 1) % kStages][0], sn);
       // ---- P and O^T += V^T P^T for tile ti, one key step of 16 at a time --
       // (each P operand is built right before its four MFMAs, so only one is
       // live)
       float lsum = 0.f;
-      const int vb = ti & 1;
+      const uint8_t* vt = &v_lds[ti % kStages][0] + v_lane_off;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
         float pv[8];
@@ -421,9 +450,9 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
           // A operand (V^T, 32 d x 16 keys): two transpose loads of 4 keys x
           // 16 d per 16-lane group; k-slots 0..3 <- keys 16t+4h+0..3, 4..7 <-
           // keys 16t+8+4h+0..3 (the same key order as the P operand)
-          const uint8_t* vb0 = &v_lds[vb][0] + v_lane_off + (16 * t) * kVStride + dt * 64;
+          const uint8_t* vb0 = vt + (t * 4 + dt) * kUnit;
           const uint2 lo2 = ds_read_tr16(vb0);
-          const uint2 hi2 = ds_read_tr16(vb0 + 8 * kVStride);
+          const uint2 hi2 = ds_read_tr16(vb0 + kUnit / 2);
           const uint4 a = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
           acc_o[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pop),
                                                               acc_o[dt], 0, 0, 0);
@@ -436,10 +465,8 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
         done = ti + 1 < ntiles;
         return true;
       }
-      // K(ti+2) replaces K(ti) (consumed last step); V(ti+1) replaces V(ti-1)
-      // (consumed last step); every wavefront passed the barrier
-      store_k(ti & 1);
-      store_v((ti + 1) & 1);
+      // K(ti+2) and V(ti+1) have landed once every wavefront passed here
+      wait_older();
       __syncthreads();
       return false;
     };
@@ -448,6 +475,9 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
       if (step(ti, s_a, s_b)) break;
       if (step(ti + 1, s_b, s_a)) break;
     }
+    // no DMA may still write into a stage (the next chunk's staging shares
+    // one) once the workgroup leaves this chunk
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     __syncthreads();
   }
 
