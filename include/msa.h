@@ -134,9 +134,10 @@ size_t msa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  * pseudocode; P2 Key Results: one kernel over many disjoint segments).
  *
  * The query of sequence b attends to every alive token of b (it sits after
- * all of them: no mask).  Work split: each sequence's alive-token stream is
- * cut into splits of split_blocks blocks (0 = chosen by the library from
- * B, Hkv and max_ctx_len); each (sequence, KV head, split) is one workgroup
+ * all of them: no mask).  Work split: each sequence's nA alive blocks are
+ * cut into ceil(nA / split_blocks) near-equal splits of at most split_blocks
+ * blocks (0 = chosen by the library from B, Hkv and max_ctx_len); each
+ * (sequence, KV head, split) is one workgroup
  * that walks its segments in logical order and folds them into a running
  * (max, sum-exp, unnormalised output).  When a sequence needs more than one
  * split the partials go to `workspace` and a merge kernel stitches them by
@@ -174,8 +175,9 @@ size_t msa_prefill_workspace_size(int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
  *   q       [B, C, Hq, D] bf16     q_pos0  int32 [B] (device)
  *   out     [B, C, Hq, D] bf16     lse_out [B, C, Hq] float32, may be NULL
  *   split_blocks  0 = one split per (row tile, KV head, sequence); otherwise
- *                 the alive-key stream is cut into splits of that many
- *                 blocks, merged by log-sum-exp through `workspace`.
+ *                 the alive-key stream is cut into near-equal splits of at
+ *                 most that many blocks, merged by log-sum-exp through
+ *                 `workspace`.
  * A row that sees no key gets out = 0 and lse = -inf. */
 int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const void* k_pool,
                       const void* v_pool, int32_t num_phys_blocks, int32_t block_size,

@@ -8,8 +8,9 @@
 //
 // Grid: (split s, KV head g, sequence b); 256 threads = 4 wavefronts.
 //   * The sequence's alive blocks, in logical order, are numbered
-//     0..nAB-1 (block j holds alive tokens [16j, 16j+16)); split s owns
-//     blocks [s*T, (s+1)*T).  The workgroup finds the segment holding its
+//     0..nAB-1 (block j holds alive tokens [16j, 16j+16)).  The sequence
+//     uses Sb = ceil(nAB / T) splits that share the blocks evenly: split s
+//     owns [s*nAB/Sb, (s+1)*nAB/Sb).  The workgroup finds the segment holding its
 //     first block with a workgroup-parallel search over alive_token_start,
 //     then expands its segments into a per-block physical id list in LDS.
 //     Consecutive segments are folded into one running softmax state in
@@ -68,8 +69,12 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* base, u
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<char*>(base), 0, int(bytes), kBufferFlags);
 }
 
+// K/V rows are streamed: each byte is read once per call (all G query heads
+// of a KV head share one workgroup), so the loads carry the non-temporal
+// hint and do not displace reusable lines in L2 and the Infinity Cache.
+constexpr int kStreamPolicy = 2;  // cache-policy bits: nt
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
-  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kStreamPolicy);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -191,8 +196,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
     }
     return;
   }
-  const int j0 = s * T;
-  const int nblk = min(nAB, j0 + T) - j0;
+  // the sequence's Sb splits share its nAB blocks evenly (each <= T blocks)
+  const int j0 = int(int64_t(s) * nAB / Sb);
+  const int nblk = int(int64_t(s + 1) * nAB / Sb) - j0;
   const int last_tokens = min(kBlk, A - kBlk * (nAB - 1));  // tokens in the final alive block
 
   // ---- expand this split's segments into per-block physical ids ----------

@@ -181,8 +181,9 @@ __global__ void __launch_bounds__(PGeo<G>::THREADS, 2) prefill_kernel(PrefillPar
   // a split past this sequence's keys has nothing to contribute (split 0 of
   // a sequence without keys still writes O = 0, LSE = -inf below)
   if (s > 0 && s >= Sb) return;
-  const int j_begin = s * T;
-  const int j_end = min(nAB, j_begin + T);
+  // the sequence's Sb splits share its nAB blocks evenly (each <= T blocks)
+  const int j_begin = int(int64_t(s) * nAB / Sb);
+  const int j_end = int(int64_t(s + 1) * nAB / Sb);
   const int last_tokens = min(kBlk, A - kBlk * (nAB - 1));
 
   // ---- Q of this lane's row into MFMA B-operand registers ----------------
