@@ -9,14 +9,16 @@
 // Partials are visited in their stored (logical) order, so the result is
 // deterministic run to run.
 //
-// One workgroup covers 256 consecutive (head, d) elements of one (sequence,
-// row); every thread walks the sequence's partials for its element.
+// One workgroup covers 128 consecutive (head, d) elements of one (sequence,
+// row); every thread folds the sequence's partials for its element in one
+// pass with a running maximum, eight partials' loads in flight at a time.
 #include "msa_internal.h"
 
 namespace msa {
 namespace {
 
-constexpr int kThreads = 256;
+constexpr int kThreads = 128;
+constexpr int kUnroll = 8;  // partials whose loads are issued together
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -62,22 +64,37 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
   if (e >= HD) return;
   const int h = e / a.D, d = e % a.D;
   const size_t orow = (size_t(b) * a.R + r) * a.H + h;
-  float M = -INFINITY;
-  for (int i = 0; i < n; ++i) M = fmaxf(M, a.m_part[(size_t(lo + i) * a.R + r) * a.H + h]);
-  float L = 0.f, O = 0.f;
-  if (M != -INFINITY) {
-    for (int i = 0; i < n; ++i) {
-      const size_t pr = (size_t(lo + i) * a.R + r) * a.H + h;
-      const float mi = a.m_part[pr];
-      if (mi == -INFINITY) continue;  // empty partial: its o is never read
-      const float wi = exp2f((mi - M) * kLog2e);
-      L = fmaf(wi, a.l_part[pr], L);
-      O = fmaf(wi, a.o_part[pr * a.D + d], O);
+  // running (M, L, O) in log2 units; a partial with a larger maximum rescales
+  // what was folded so far, exactly as the two-pass form would weight it
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int i0 = 0; i0 < n; i0 += kUnroll) {
+    float mi[kUnroll], li[kUnroll], oi[kUnroll];
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      const bool in = i0 + k < n;
+      const size_t pr = (size_t(lo + (in ? i0 + k : 0)) * a.R + r) * a.H + h;
+      mi[k] = in ? a.m_part[pr] : -INFINITY;
+      li[k] = in ? a.l_part[pr] : 0.f;
+      oi[k] = in ? a.o_part[pr * a.D + d] : 0.f;
+    }
+#pragma unroll
+    for (int k = 0; k < kUnroll; ++k) {
+      if (mi[k] == -INFINITY) continue;  // empty partial: its o is never used
+      const float m2 = mi[k] * kLog2e;
+      if (m2 > M) {
+        const float sc = M == -INFINITY ? 0.f : exp2f(M - m2);
+        L *= sc;
+        O *= sc;
+        M = m2;
+      }
+      const float wi = exp2f(m2 - M);
+      L = fmaf(wi, li[k], L);
+      O = fmaf(wi, oi[k], O);
     }
   }
   const bool ok = L > 0.f;
   store_o(a.out, orow * a.D + d, ok ? O / L : 0.f, a.out_dtype);
-  if (a.lse && d == 0) a.lse[orow] = ok ? M + log2f(L) * kLn2 : -INFINITY;
+  if (a.lse && d == 0) a.lse[orow] = ok ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
 
 }  // namespace
