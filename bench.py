@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--chunk-sweep", action="store_true",
+                    help="also time the prefill workload at chunk sizes 128..2048")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
@@ -189,6 +191,27 @@ def time_cold(fn, n, stream, flush):
     return statistics.median(ts)
 
 
+def prefill_leg(w, n, warm):
+    """Time msa_prefill_chunk (plus its merge when split) on workload w."""
+    import torch
+    prep = Prepared(w)
+    flops = 4.0 * w.D * w.Hq * visible_pairs(w)
+    prep.plan()
+    for _ in range(warm):
+        prep.attention()
+    torch.cuda.synchronize()
+    t = time_calls(prep.attention, n, prep.stream)
+    tfs = flops / t / 1e12
+    del prep
+    G = w.Hq // w.Hkv
+    # (256 query rows, KV head, sequence) work items: one workgroup each; the
+    # library splits the key stream too when these do not cover the 256 CUs
+    items = -(-w.C * G // 256) * w.Hkv * w.B
+    return {"us_per_call": round(t * 1e6, 3), "TFLOP/s": round(tfs, 2),
+            "pct_mfma_bf16_peak": round(100 * tfs / MFMA_BF16_PEAK_TFS, 2), "calls": n,
+            "row_tile_items": items, "flops": flops}
+
+
 def cpu_baseline(w, bytes_per_pass, budget_s=10.0, max_reps=20):
     """The fp64 oracle, as it stands, on the same decode workload."""
     import oracle
@@ -303,24 +326,32 @@ def main():
     # --------------------------------------------------------------- prefill
     import kv_cache_attention_msa_amd as msa
     if args.only in (None, "prefill") and not args.no_prefill and msa.prefill_available():
-        wp = make_workload(3, seed=args.seed)
-        prep = Prepared(wp)
-        flops = 4.0 * wp.D * wp.Hq * visible_pairs(wp)
-        prep.plan()
-        for _ in range(max(3, args.warmup // 4)):
-            prep.attention()
-        torch.cuda.synchronize()
         n = max(10, args.steps // 4)
-        pf_s = time_calls(prep.attention, n, prep.stream)
-        tfs = flops / pf_s / 1e12
-        result["prefill"] = {"workload": NAMES[3], "us_per_call": round(pf_s * 1e6, 3),
-                             "TFLOP/s": round(tfs, 2), "pct_mfma_bf16_peak": round(100 * tfs / MFMA_BF16_PEAK_TFS, 2),
-                             "roofline": {"bound": "mfma", "achieved": round(tfs, 2), "peak": MFMA_BF16_PEAK_TFS,
-                                          "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
-                                          "traffic": None, "kernel": "msa_prefill_chunk",
-                                          "algorithmic_flops_per_call": flops},
-                             "calls": n}
-        del prep
+        wp = make_workload(3, seed=args.seed)
+        leg = prefill_leg(wp, n, max(3, args.warmup // 4))
+        tfs = leg["TFLOP/s"]
+        leg["roofline"] = {"bound": "mfma", "achieved": tfs, "peak": MFMA_BF16_PEAK_TFS,
+                           "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
+                           "traffic": None, "kernel": "msa_prefill_chunk",
+                           "algorithmic_flops_per_call": leg.pop("flops")}
+        result["prefill"] = {"workload": NAMES[3], **leg}
+        del wp
+        # recompute of an evicted middle range (chunk rows in the middle of the
+        # context, later alive blocks hidden by the causal mask)
+        wr = make_workload(6, seed=args.seed)
+        leg = prefill_leg(wr, n, 3)
+        leg.pop("flops")
+        result["recompute"] = {"workload": NAMES[6], **leg}
+        del wr
+        if args.chunk_sweep:
+            sweep = []
+            for C in (128, 256, 512, 1024, 2048):
+                wc = make_workload(3, seed=args.seed, C=C)
+                leg = prefill_leg(wc, n, 3)
+                leg.pop("flops")
+                sweep.append({"C": C, **leg})
+                del wc
+            result["chunk_sweep"] = {"workload": NAMES[3] + " with chunk C varied", "points": sweep}
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         bb = torch.empty_like(a)

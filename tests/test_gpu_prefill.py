@@ -6,7 +6,9 @@ several 64-key tiles and ragged tails (partial last block, chunk lengths
 that are not a multiple of the 32-row tile), a chunk in the middle of the
 context (later alive blocks must be masked by logical position), every GQA
 group size, forced key splits merged by log-sum-exp, rows with no visible
-key, and the full-size prefill workload on sampled rows and heads.
+key, the full-size prefill workload on sampled rows and heads, and the
+recompute workload (an evicted middle range rebuilt as a chunk in fresh pool
+slots, with alive blocks after it that only the causal mask hides).
 """
 import numpy as np
 import pytest
@@ -112,3 +114,23 @@ def test_prefill_full_sampled():
     rows = np.sort(np.concatenate([[0, 31, 32, 255, 256, 480, 511], rng.choice(512, 9, replace=False)]))
     heads = sorted(rng.choice(w.Hq, size=5, replace=False).tolist())
     check(w, O, L, seqs=[0, 3], heads=heads, rows=rows)
+
+
+def test_recompute_small():
+    """Recompute of an evicted middle range: chunk rows at q_pos0 in the middle
+    of the context, alive blocks after the chunk hidden by the causal mask."""
+    for seed in (0, 1):
+        w = make_workload(6, seed=seed, size="small")
+        O, L = run_prefill(w)
+        check(w, O, L)
+        O, L = run_prefill(w, 16)
+        check(w, O, L)
+
+
+def test_recompute_full_sampled():
+    w = make_workload(6, seed=0)
+    O, L = run_prefill(w)
+    rng = np.random.default_rng(5)
+    rows = np.sort(np.concatenate([[0, 1, 63, 64, 255, 511], rng.choice(512, 8, replace=False)]))
+    heads = sorted(rng.choice(w.Hq, size=4, replace=False).tolist())
+    check(w, O, L, seqs=[1, 2], heads=heads, rows=np.unique(rows))

@@ -29,7 +29,7 @@ def _check_layout(w):
         assert np.isnan(to_f64(w.v_pool[unused[:50]])).all()
 
 
-@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5])
+@pytest.mark.parametrize("cfg", [1, 2, 3, 4, 5, 6])
 def test_small_layouts(cfg):
     w = make_workload(cfg, seed=0, size="small")
     _check_layout(w)
@@ -56,3 +56,24 @@ def test_prefill_small_has_ragged_chunk():
     w = make_workload(3, seed=1, size="small", C=70)
     assert int(w.ctx_len[0]) == 1024 + 70
     _check_layout(w)
+
+
+@pytest.mark.parametrize("size", ["small", "full"])
+def test_recompute_chunk_in_fresh_run_with_keys_after_it(size):
+    """Recompute family: the chunk's logical range is alive, sits in its own
+    physical run (not adjacent to any neighbour's slot), and alive blocks
+    follow it, so only the causal mask keeps them from the chunk rows."""
+    w = make_workload(6, seed=1, size=size, values=False)
+    bs = w.block_size
+    for b in range(w.B):
+        c0, cb = int(w.q_pos0[b]) // bs, -(-w.C // bs)
+        nb = int(w.ctx_len[b]) // bs
+        assert w.alive[b, c0:c0 + cb].all()
+        ids = w.block_table[b, c0:c0 + cb]
+        assert np.array_equal(ids, np.arange(ids[0], ids[0] + cb))
+        if c0 > 0 and w.alive[b, c0 - 1]:
+            assert w.block_table[b, c0 - 1] != ids[0] - 1
+        if w.alive[b, c0 + cb]:
+            assert w.block_table[b, c0 + cb] != ids[-1] + 1
+        assert w.alive[b, c0 + cb:nb].sum() > 0
+        assert 0 < int(w.q_pos0[b]) and int(w.q_pos0[b]) + w.C < int(w.ctx_len[b])

@@ -264,6 +264,47 @@ def _cfg3(rng, B=4, Hq=32, Hkv=8, D=128, cached=8192, C=512, mean_alive=16.0,
                 C=C, q_pos0=q_pos0)
 
 
+def _cfg6(rng, B=4, Hq=32, Hkv=8, D=128, ctx=8704, q_pos0=4096, C=512, mean_alive=16.0,
+          evict_frac=0.15, dtype="bf16"):
+    """Recompute (lossless reconstruction), bf16: an evicted range of C tokens
+    in the middle of the context, [q_pos0, q_pos0+C), is recomputed as a
+    prefill chunk.  Its K/V go into fresh pool slots (one contiguous run, like
+    a chunk) and the sequence is re-planned; the alive blocks after the chunk
+    stay in the plan and are hidden from the chunk rows by the causal mask
+    alone.  Elsewhere blocks are evicted in geometric runs as in the prefill
+    family."""
+    bs = 16
+    assert q_pos0 % bs == 0 and ctx % bs == 0 and q_pos0 + C <= ctx
+    nb = ctx // bs
+    c0, cb = q_pos0 // bs, -(-C // bs)
+    mean_dead = mean_alive * evict_frac / (1.0 - evict_frac)
+    alive = np.zeros((B, nb), dtype=np.uint8)
+    for b in range(B):
+        alive[b] = _alternating_runs(rng, nb, lambda: rng.geometric(1.0 / mean_alive),
+                                     lambda: rng.geometric(1.0 / mean_dead))
+        alive[b, c0:c0 + cb] = 1
+        alive[b, nb - 1] = 1
+    runs = []
+    for b in range(B):
+        for st, n in _runs_of(alive[b], 0, c0):
+            runs.append((b, st, n))
+        runs.append((b, c0, cb))  # the recomputed range: fresh slots, its own run
+        for st, n in _runs_of(alive[b], c0 + cb, nb):
+            runs.append((b, st, n))
+    sizes = [n for (_, _, n) in runs]
+    P = int(math.ceil(1.25 * sum(sizes)))
+    starts = _place_runs_with_gaps(rng, sizes, P)
+    table = np.full((B, nb), -1, dtype=np.int32)
+    for (b, st, n), ps in zip(runs, starts):
+        table[b, st:st + n] = np.arange(ps, ps + n, dtype=np.int32)
+    ctx_len = np.full(B, ctx, dtype=np.int32)
+    live = _live_slots(P, bs, table, alive, ctx_len)
+    q, kp, vp = _fill_pools_and_q(rng, dtype, (B, C, Hq, D), P, bs, Hkv, D, live)
+    return dict(kind="prefill", dtype=dtype, B=B, Hq=Hq, Hkv=Hkv, D=D, block_size=bs,
+                block_table=table, alive=alive, ctx_len=ctx_len, q=q, k_pool=kp, v_pool=vp,
+                C=C, q_pos0=np.full(B, q_pos0, dtype=np.int32))
+
+
 def _cfg4(rng, B=64, Hq=32, Hkv=8, D=128, median=6144, sigma=0.75, lo=2064, hi=32768,
           shared_tokens=2048, group=16, evict_frac=0.3, dtype="bf16"):
     """Multi-session decode mix: lognormal contexts, a shared prefix per group of
@@ -328,7 +369,7 @@ def _cfg5(rng, B=4, Hq=64, Hkv=8, D=128, ctx=131072, dtype="bf16"):
                 block_table=table, alive=alive, ctx_len=ctx_len, q=q, k_pool=kp, v_pool=vp)
 
 
-_FAMILIES = {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4, 5: _cfg5}
+_FAMILIES = {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4, 5: _cfg5, 6: _cfg6}
 
 NAMES = {
     1: "decode_f32_b1_h8kv2_d64_ctx1k_evict25_randperm",
@@ -336,6 +377,7 @@ NAMES = {
     3: "prefill_bf16_b4_h32kv8_d128_chunk512_cached8k_evict15",
     4: "decode_bf16_b64_h32kv8_d128_lognormal6k_shared2k_evict30",
     5: "decode_bf16_b4_h64kv8_d128_ctx128k_evict50_runs1to2",
+    6: "recompute_bf16_b4_h32kv8_d128_chunk512_at4k_ctx8704_evict15",
 }
 
 # Reduced sizes with the same recipe: several tiles and ragged tails, but small
@@ -346,12 +388,13 @@ SMALL = {
     3: dict(B=2, cached=1024, C=96),
     4: dict(B=8, median=2600, lo=2064, hi=4000, group=4),
     5: dict(B=2, ctx=4096),
+    6: dict(B=2, ctx=1536, q_pos0=512, C=96),
 }
 
 
 def make_workload(cfg: int, seed: int = 0, size: str = "full", values: bool = True,
                   **overrides) -> Workload:
-    """Draw workload family ``cfg`` (1..5) with ``seed``.
+    """Draw workload family ``cfg`` (1..6) with ``seed``.
 
     size="full" uses the family's defining sizes, "small" the reduced ones;
     keyword overrides change individual shape parameters.  values=False skips
