@@ -47,6 +47,8 @@ def parse():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cold", action="store_true")
+    ap.add_argument("--no-gather", action="store_true",
+                    help="skip the gather-then-attend baseline leg")
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="also time the prefill workload at chunk sizes 128..2048")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -155,6 +157,50 @@ class Prepared:
 
     def step(self):
         self.plan()
+        self.attention()
+
+
+class GatherBaseline:
+    """The detour MSA avoids: gather the alive blocks into dense pools
+    (msa_gather_alive), then the same decode kernel over one segment per
+    sequence.  Pre-marshalled like Prepared; uses its plan and buffers."""
+
+    def __init__(self, prep):
+        import ctypes
+        import torch
+        w, d, lib = prep.w, prep.d, prep.lib
+        self.lib = lib
+        P = ctypes.c_void_p
+        s = P(prep.stream.cuda_stream)
+        bps = -(-prep.max_ctx // w.block_size)
+        dev = d["q"].device
+        shape = (w.B * bps, w.block_size, w.Hkv, w.D)
+        self.dk = torch.empty(shape, dtype=d["k_pool"].dtype, device=dev)
+        self.dv = torch.empty_like(self.dk)
+        self.dsegs = torch.empty((w.B, 6), dtype=torch.int32, device=dev)
+        self.dind = torch.empty(w.B + 1, dtype=torch.int32, device=dev)
+        dt = 1 if w.dtype == "bf16" else 0
+        self.gather_args = (P(d["k_pool"].data_ptr()), P(d["v_pool"].data_ptr()), w.num_phys_blocks,
+                            w.block_size, P(prep.segs.data_ptr()), P(prep.indptr.data_ptr()), w.B,
+                            w.Hkv, w.D, dt, bps, P(self.dk.data_ptr()), P(self.dv.data_ptr()),
+                            P(self.dsegs.data_ptr()), P(self.dind.data_ptr()), s)
+        a = list(prep.attn_args)
+        a[1], a[2], a[3] = P(self.dk.data_ptr()), P(self.dv.data_ptr()), w.B * bps
+        a[5], a[6] = P(self.dsegs.data_ptr()), P(self.dind.data_ptr())
+        self.attn_args = tuple(a)
+
+    def gather(self):
+        st = self.lib.msa_gather_alive(*self.gather_args)
+        if st != 0:
+            raise RuntimeError(f"msa_gather_alive failed: {st}")
+
+    def attention(self):
+        st = self.lib.msa_decode(*self.attn_args)
+        if st != 0:
+            raise RuntimeError(f"msa_decode (dense) failed: {st}")
+
+    def step(self):
+        self.gather()
         self.attention()
 
 
@@ -318,6 +364,23 @@ def main():
                               "GB/s": round(alg_bytes / cold_s / 1e9, 2),
                               "pct_hbm_peak": round(100 * alg_bytes / cold_s / 1e9 / HBM_PEAK_GBS, 2),
                               "note": "msa_decode alone, a 1 GiB read evicts L2 and Infinity Cache before each call"}
+        if not args.no_gather:
+            # the gather-then-attend detour on the same inputs, same kernel
+            gb = GatherBaseline(prep)
+            for _ in range(3):
+                gb.step()
+            torch.cuda.synchronize()
+            g_step = time_calls(gb.step, max(20, args.steps // 4), stream)
+            g_copy = time_calls(gb.gather, max(20, args.steps // 4), stream)
+            g_attn = time_calls(gb.attention, max(20, args.steps // 4), stream)
+            result["gather_baseline"] = {
+                "us_per_call": round(g_step * 1e6, 3), "gather_us": round(g_copy * 1e6, 3),
+                "dense_decode_us": round(g_attn * 1e6, 3), "msa_decode_us": round(dec_s * 1e6, 3),
+                "msa_speedup": round(g_step / dec_s, 3),
+                "note": "gather alive K/V blocks into dense pools (msa_gather_alive) + msa_decode "
+                        "over one segment per sequence, vs msa_decode over the segments"}
+            del gb
+            torch.cuda.empty_cache()
         if not args.no_cpu_baseline:
             result["cpu_baseline"] = cpu_baseline(w, alg_bytes)
         del prep

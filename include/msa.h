@@ -208,6 +208,36 @@ int msa_merge_partials(const float* o_part, const float* m_part, const float* l_
                        msa_dtype out_dtype, void* out, float* lse_out, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Gather-then-attend baseline (not on the MSA path)                          */
+/* ------------------------------------------------------------------------ */
+
+/* The detour MSA avoids (P1, "Core method 1: MSA": without a multi-segment
+ * kernel, the surviving blocks are first gathered into one contiguous
+ * buffer, then a contiguous kernel runs; P2, Key Results, compares the two).
+ * Copies every sequence's alive K/V blocks, in logical order, into dense
+ * pools where alive block j of sequence b becomes block b*blocks_per_seq + j,
+ * and writes the matching plan: one segment per sequence
+ *   {b, logical_block 0, phys_block b*blocks_per_seq, nA_b, A_b, 0}
+ * (nA_b = alive blocks, A_b = alive tokens, both cut at blocks_per_seq) and
+ * dense_indptr = 0, 1, ..., B.  msa_decode over (dense pools, dense plan)
+ * then computes the same attention with a single segment per sequence.
+ * Logical positions are renumbered, so the dense plan suits decode only.
+ *
+ *   k_pool, v_pool   [P, 16, Hkv, D] dtype (device, read)
+ *   segs, seg_indptr a plan of those pools (device)
+ *   dense_k, dense_v [B * blocks_per_seq, 16, Hkv, D] dtype (device, written)
+ *   dense_segs       [B] msa_segment (device, written)
+ *   dense_indptr     [B + 1] int32 (device, written)
+ * Dense blocks past a sequence's alive blocks are left untouched.
+ * Returns INVALID_ARG for null pointers or non-positive sizes, UNSUPPORTED
+ * for other dtypes or block sizes, DEVICE on a launch error. */
+int msa_gather_alive(const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
+                     int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr,
+                     int32_t B, int32_t Hkv, int32_t D, msa_dtype dtype, int32_t blocks_per_seq,
+                     void* dense_k, void* dense_v, msa_segment* dense_segs,
+                     int32_t* dense_indptr, void* stream);
+
+/* ------------------------------------------------------------------------ */
 
 /* 1 if the attention kernels were built for this shape, else 0.
  * prefill = 0 asks about msa_decode, 1 about msa_prefill_chunk;

@@ -1,6 +1,6 @@
 """Multi-Segment Attention (MSA) on MI355X: thin PyTorch binding of libmsa.
 
-The four calls mirror the C ABI in include/msa.h one to one; this module
+The calls mirror the C ABI in include/msa.h one to one; this module
 only checks tensor shapes/dtypes/devices, allocates outputs and workspaces
 with torch (device memory plumbing), and passes raw pointers plus the
 current HIP stream.  Every step of the computation runs in libmsa's HIP
@@ -10,6 +10,7 @@ kernels; there is no CPU or PyTorch fallback, and a missing library raises.
   msa_decode          decode attention over the segments (a2, a3, a5)
   msa_prefill_chunk   chunked-prefill attention over the segments (a2, a4, a5)
   msa_merge_partials  log-sum-exp merge of (m, l, o) partials (a5)
+  msa_gather_alive    gather-then-attend baseline: alive blocks -> dense pools
 """
 from __future__ import annotations
 
@@ -245,3 +246,44 @@ def msa_merge_partials(o_part: torch.Tensor, m_part: torch.Tensor, l_part: torch
                                 _dev_ptr(lse, "lse"), _stream(stream, dev))
     _lib.check(st, "msa_merge_partials")
     return out, lse
+
+
+# ---------------------------------------------------------------------------
+# gather-then-attend baseline (the detour MSA avoids; not on the MSA path)
+# ---------------------------------------------------------------------------
+
+def msa_gather_alive(k_pool: torch.Tensor, v_pool: torch.Tensor, segs: torch.Tensor,
+                     seg_indptr: torch.Tensor, blocks_per_seq: int,
+                     dense_k: torch.Tensor | None = None, dense_v: torch.Tensor | None = None,
+                     dense_segs: torch.Tensor | None = None,
+                     dense_indptr: torch.Tensor | None = None, stream=None):
+    """Copy each sequence's alive blocks, in logical order, into dense pools
+    [B * blocks_per_seq, 16, Hkv, D] and write the one-segment-per-sequence
+    plan of those pools.  Returns (dense_k, dense_v, dense_segs [B, 6],
+    dense_indptr [B + 1])."""
+    lib = _lib_handle()
+    if k_pool.dim() != 4 or v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
+        raise ValueError("k_pool/v_pool must be [P,bs,Hkv,D] of equal shape and dtype")
+    _expect(segs, torch.int32, "segs", 2)
+    _expect(seg_indptr, torch.int32, "seg_indptr", 1)
+    P, bs, Hkv, D = k_pool.shape
+    B = seg_indptr.shape[0] - 1
+    dev = k_pool.device
+    shape = (B * int(blocks_per_seq), bs, Hkv, D)
+    if dense_k is None:
+        dense_k = torch.empty(shape, dtype=k_pool.dtype, device=dev)
+    if dense_v is None:
+        dense_v = torch.empty(shape, dtype=k_pool.dtype, device=dev)
+    if tuple(dense_k.shape) != shape or tuple(dense_v.shape) != shape:
+        raise ValueError(f"dense pools must be {shape}")
+    if dense_segs is None:
+        dense_segs = torch.empty((B, 6), dtype=torch.int32, device=dev)
+    if dense_indptr is None:
+        dense_indptr = torch.empty(B + 1, dtype=torch.int32, device=dev)
+    st = lib.msa_gather_alive(_dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"), P, bs,
+                              _dev_ptr(segs, "segs"), _dev_ptr(seg_indptr, "seg_indptr"), B, Hkv, D,
+                              _dtype_enum(k_pool), int(blocks_per_seq), _dev_ptr(dense_k, "dense_k"),
+                              _dev_ptr(dense_v, "dense_v"), _dev_ptr(dense_segs, "dense_segs"),
+                              _dev_ptr(dense_indptr, "dense_indptr"), _stream(stream, dev))
+    _lib.check(st, "msa_gather_alive")
+    return dense_k, dense_v, dense_segs, dense_indptr

@@ -43,6 +43,8 @@ SIGNATURES = {
     "msa_prefill_chunk": (ctypes.c_int, [_p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32,
                                          _i32, _i32, ctypes.c_int, _f, _i32, _p, _p, _p, _sz, _p]),
     "msa_merge_partials": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _p, _p]),
+    "msa_gather_alive": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, ctypes.c_int, _i32,
+                                        _p, _p, _p, _p, _p]),
 }
 
 _LIB = None

@@ -244,4 +244,37 @@ int msa_merge_partials(const float* o_part, const float* m_part, const float* l_
                                       out, lse_out, as_stream(stream)));
 }
 
+int msa_gather_alive(const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
+                     int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr,
+                     int32_t B, int32_t Hkv, int32_t D, msa_dtype dtype, int32_t blocks_per_seq,
+                     void* dense_k, void* dense_v, msa_segment* dense_segs,
+                     int32_t* dense_indptr, void* stream) {
+  if (!k_pool || !v_pool || !segs || !seg_indptr || !dense_k || !dense_v || !dense_segs ||
+      !dense_indptr)
+    return MSA_ERR_INVALID_ARG;
+  if (B <= 0 || Hkv <= 0 || D <= 0 || num_phys_blocks <= 0 || blocks_per_seq <= 0)
+    return MSA_ERR_INVALID_ARG;
+  if (dtype != MSA_F32 && dtype != MSA_BF16) return MSA_ERR_UNSUPPORTED;
+  if (block_size != 16) return MSA_ERR_UNSUPPORTED;
+  if (B > 65535) return MSA_ERR_UNSUPPORTED;
+  const size_t esz = dtype == MSA_BF16 ? 2 : 4;
+  const size_t block_bytes = size_t(block_size) * size_t(Hkv) * size_t(D) * esz;
+  if (block_bytes % 16 != 0) return MSA_ERR_UNSUPPORTED;
+  if (int64_t(B) * blocks_per_seq > INT32_MAX) return MSA_ERR_INVALID_ARG;
+  GatherParams p;
+  p.k_pool = k_pool;
+  p.v_pool = v_pool;
+  p.P = num_phys_blocks;
+  p.segs = segs;
+  p.indptr = seg_indptr;
+  p.B = B;
+  p.blocks_per_seq = blocks_per_seq;
+  p.block_bytes = block_bytes;
+  p.dense_k = dense_k;
+  p.dense_v = dense_v;
+  p.dense_segs = dense_segs;
+  p.dense_indptr = dense_indptr;
+  return from_hip(launch_gather(p, as_stream(stream)));
+}
+
 }  // extern "C"

@@ -120,6 +120,21 @@ struct PrefillParams {
   float* l_part;
 };
 
+struct GatherParams {
+  const void* k_pool;
+  const void* v_pool;
+  int32_t P;
+  const msa_segment* segs;
+  const int32_t* indptr;
+  int32_t B;
+  int32_t blocks_per_seq;  // dense blocks reserved per sequence
+  size_t block_bytes;      // bytes of one pool block (16 * Hkv * D * element size)
+  void* dense_k;
+  void* dense_v;
+  msa_segment* dense_segs;  // [B]
+  int32_t* dense_indptr;    // [B+1]
+};
+
 // Decode/prefill work split, shared by the workspace-size functions and the
 // launches so both always agree.
 struct SplitPlan {
@@ -139,6 +154,7 @@ bool prefill_supported(msa_dtype dtype, int32_t D, int32_t G);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
+hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
 // Merge of decode/prefill split partials; the partial count of each sequence
 // is derived from the plan (same rule as the attention launch).
 hipError_t launch_merge_from_plan(const float* o_part, const float* m_part, const float* l_part,
