@@ -49,6 +49,8 @@ def parse():
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--no-gather", action="store_true",
                     help="skip the gather-then-attend baseline leg")
+    ap.add_argument("--latency-model", action="store_true",
+                    help="fit the decode latency model used by the eviction scorer")
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="also time the prefill workload at chunk sizes 128..2048")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -258,6 +260,62 @@ def prefill_leg(w, n, warm):
             "row_tile_items": items, "flops": flops}
 
 
+def latency_model_leg(args):
+    """Fit msa_decode time = c0 + c_tok * alive tokens + c_seg * segments over
+    decode batches that vary the context length (alive tokens) and the mean
+    alive-run length (segments at a given token count), then use the fitted
+    model in the kernel-aware eviction scorer on the headline batch and
+    check its prediction against the measured time after eviction."""
+    import numpy as np
+    import torch
+    from workloads import make_workload
+    from kv_cache_attention_msa_amd.evict import (DecodeLatencyModel, choose_evictions,
+                                                  recompute_cost_us)
+    pts = []
+    for ctx in (2048, 4096, 8192):
+        for run in (1.0, 4.0, 32.0):
+            w = make_workload(2, seed=args.seed, ctx=ctx, mean_alive=run, mean_dead=max(1.0, run / 4),
+                              pool_factor=2.5)
+            prep = Prepared(w)
+            prep.plan()
+            for _ in range(5):
+                prep.attention()
+            torch.cuda.synchronize()
+            t = time_calls(prep.attention, 30, prep.stream)
+            pts.append({"ctx": ctx, "mean_alive_run": run, "alive_tokens": int(sum(alive_tokens_per_seq(w))),
+                        "segments": int(prep.indptr[-1].item()), "us": round(t * 1e6, 3)})
+            del prep, w
+    m = DecodeLatencyModel.fit([p["alive_tokens"] for p in pts], [p["segments"] for p in pts],
+                               [p["us"] for p in pts])
+    pred = m.predict([p["alive_tokens"] for p in pts], [p["segments"] for p in pts])
+    meas = np.array([p["us"] for p in pts])
+    r2 = 1.0 - float(((meas - pred) ** 2).sum() / ((meas - meas.mean()) ** 2).sum())
+    # the scorer on the headline batch: evict a further 10% of the blocks
+    w = make_workload(2, seed=args.seed)
+    rng = np.random.default_rng(args.seed + 7)
+    hit = rng.random(w.alive.shape)
+    rec = [recompute_cost_us(w.alive[b], w.ctx_len[b], 16, w.D, w.Hq, 800.0) for b in range(w.B)]
+    n_ev = int(0.1 * w.alive.sum())
+    al, _ = choose_evictions(w.block_table, w.alive, w.ctx_len, 16, n_ev, hit, rec, m,
+                             alpha=float(np.mean([r.mean() for r in rec])), beta=1.0, gamma=1000.0,
+                             batch_seqs=w.B)
+    w.alive = al
+    prep = Prepared(w)
+    prep.plan()
+    for _ in range(5):
+        prep.attention()
+    torch.cuda.synchronize()
+    t_after = time_calls(prep.attention, 30, prep.stream)
+    segs_after = int(prep.indptr[-1].item())
+    tok_after = int(sum(alive_tokens_per_seq(w)))
+    del prep
+    return {"c0_us": round(m.c0, 3), "c_tok_us": m.c_tok, "c_seg_us": m.c_seg, "r2": round(r2, 4),
+            "points": pts,
+            "eviction_check": {"evicted_blocks": n_ev, "alive_tokens": tok_after, "segments": segs_after,
+                               "predicted_us": round(float(m.predict(tok_after, segs_after)), 3),
+                               "measured_us": round(t_after * 1e6, 3)}}
+
+
 def cpu_baseline(w, bytes_per_pass, budget_s=10.0, max_reps=20):
     """The fp64 oracle, as it stands, on the same decode workload."""
     import oracle
@@ -385,6 +443,10 @@ def main():
             result["cpu_baseline"] = cpu_baseline(w, alg_bytes)
         del prep
         torch.cuda.empty_cache()
+
+    # ------------------------------------------- decode latency model (next)
+    if args.latency_model:
+        result["latency_model"] = latency_model_leg(args)
 
     # --------------------------------------------------------------- prefill
     import kv_cache_attention_msa_amd as msa

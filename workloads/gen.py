@@ -233,11 +233,11 @@ def _geom_runs_layout(rng, B, nb_cached, mean_alive, mean_dead, chunk_blocks, po
 
 
 def _cfg2(rng, B=32, Hq=32, Hkv=8, D=128, ctx=4096, mean_alive=8.0, mean_dead=2.0,
-          dtype="bf16"):
+          dtype="bf16", pool_factor=1.25):
     """Decode, bf16: alternating alive ~ Geom(mean 8) / evicted ~ Geom(mean 2) runs."""
     bs = 16
     nb = -(-ctx // bs)
-    alive, table, P = _geom_runs_layout(rng, B, nb, mean_alive, mean_dead, 0, 1.25)
+    alive, table, P = _geom_runs_layout(rng, B, nb, mean_alive, mean_dead, 0, pool_factor)
     ctx_len = np.full(B, ctx, dtype=np.int32)
     live = _live_slots(P, bs, table, alive, ctx_len)
     q, kp, vp = _fill_pools_and_q(rng, dtype, (B, Hq, D), P, bs, Hkv, D, live)
