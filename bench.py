@@ -35,6 +35,8 @@ HBM_PEAK_GBS = 8000.0       # MI355X HBM3E, published
 MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
 COUNTERS = os.path.join(ROOT, "profiles", "decode_cfg2_counters.json")
 DECODE_SOURCES = ["decode.hip", "merge.hip", "msa_internal.h"]
+PF_COUNTERS = os.path.join(ROOT, "profiles", "prefill_cfg3_counters.json")
+PREFILL_SOURCES = ["prefill.hip", "msa_internal.h"]
 
 
 def parse():
@@ -49,6 +51,8 @@ def parse():
     ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--no-gather", action="store_true",
                     help="skip the gather-then-attend baseline leg")
+    ap.add_argument("--no-recompute", action="store_true",
+                    help="skip the recompute (middle chunk) prefill leg")
     ap.add_argument("--latency-model", action="store_true",
                     help="fit the decode latency model used by the eviction scorer")
     ap.add_argument("--chunk-sweep", action="store_true",
@@ -407,7 +411,7 @@ def main():
             "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": traffic,
+                         "traffic": traffic, "traffic_unit": "bytes per call",
                          "kernel": "msa_decode = decode_kernel<bf16,128,4> + merge_kernel",
                          "algorithmic_bytes_per_call": int(alg_bytes),
                          "us_per_call": round(dec_s * 1e6, 3)},
@@ -455,19 +459,26 @@ def main():
         wp = make_workload(3, seed=args.seed)
         leg = prefill_leg(wp, n, max(3, args.warmup // 4))
         tfs = leg["TFLOP/s"]
+        pf_traffic = None
+        if os.path.exists(PF_COUNTERS):
+            c = json.load(open(PF_COUNTERS))
+            if c.get("sources_sha") == sources_sha(PREFILL_SOURCES):
+                pf_traffic = c.get("bytes_per_call")
         leg["roofline"] = {"bound": "mfma", "achieved": tfs, "peak": MFMA_BF16_PEAK_TFS,
                            "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
-                           "traffic": None, "kernel": "msa_prefill_chunk",
+                           "traffic": pf_traffic, "traffic_unit": "bytes per call",
+                           "kernel": "msa_prefill_chunk",
                            "algorithmic_flops_per_call": leg.pop("flops")}
         result["prefill"] = {"workload": NAMES[3], **leg}
         del wp
         # recompute of an evicted middle range (chunk rows in the middle of the
         # context, later alive blocks hidden by the causal mask)
-        wr = make_workload(6, seed=args.seed)
-        leg = prefill_leg(wr, n, 3)
-        leg.pop("flops")
-        result["recompute"] = {"workload": NAMES[6], **leg}
-        del wr
+        if not args.no_recompute:
+            wr = make_workload(6, seed=args.seed)
+            leg = prefill_leg(wr, n, 3)
+            leg.pop("flops")
+            result["recompute"] = {"workload": NAMES[6], **leg}
+            del wr
         if args.chunk_sweep:
             sweep = []
             for C in (128, 256, 512, 1024, 2048):

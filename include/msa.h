@@ -41,9 +41,10 @@
  *   prefill O   [B, C, Hq, D]             dtype;  LSE [B, C, Hq] float32
  *   Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
  *
- * Supported kernels: block_size 16; D in {64, 128}; Hq/Hkv in {1, 2, 4, 8};
- * decode in float32 or bfloat16; prefill in bfloat16.  Anything else
- * returns MSA_ERR_UNSUPPORTED.  The plan itself accepts any block_size >= 1.
+ * Supported kernels: block_size 16; Hq/Hkv in {1, 2, 4, 8}; decode in
+ * bfloat16 with D 64 or 128, or float32 with D 64; prefill in bfloat16 with
+ * D 128.  Anything else returns MSA_ERR_UNSUPPORTED (msa_attention_supported
+ * answers without launching).  The plan accepts any block_size >= 1.
  */
 #ifndef MSA_H
 #define MSA_H
