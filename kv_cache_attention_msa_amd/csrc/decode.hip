@@ -31,6 +31,8 @@
 //   * At the end the 4 wavefront states are merged in LDS; a sequence with
 //     one split writes O and LSE directly, otherwise the split writes its
 //     (m, l, o) partial for the merge kernel.
+#include <type_traits>
+
 #include "msa_internal.h"
 
 namespace msa {
@@ -75,6 +77,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t block_rsrc(const char* base, u
 constexpr int kStreamPolicy = 2;  // cache-policy bits: nt
 __device__ __forceinline__ uint4 load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, kStreamPolicy);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+
+__device__ __forceinline__ uint4 load16_cached(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(r, int(off), 0, 0);
   return make_uint4(v.x, v.y, v.z, v.w);
 }
 
@@ -450,10 +457,357 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Grouped-query bf16 decode with D 128 and G in {4, 8}: the G query heads of a
+// KV head against the keys of a tile form a real [G x 128] x [128 x 64]
+// contraction, and so does P x V.  On the VALU these cost 2G multiply-adds
+// per K/V element, which at G 8 limits the kernel well below the HBM stream;
+// on v_mfma_f32_16x16x32_bf16 (heads padded to 16 rows) they are a few
+// hundred cycles per 32 KB tile, so the loads set the pace.  Same grid,
+// split rule, segment walk and cross-wavefront merge as decode_kernel.
+//
+// Per wavefront and 64-token tile (4 blocks):
+//   S[key][head] = K Q^T: A = K rows straight from HBM into VGPRs (lane l:
+//     key l%16 of block kg, d 32 ds + 8(l/16) .. +7: 16 keys x 64 B per
+//     load), B = Q^T (lane l: head l%16, same d), C: lane l holds head l%16
+//     for keys 16 kg + 4(l/16) + r.
+//   online softmax per head over those 16 values x the 4 lanes of the head
+//   O[head][d] += P V: A = P, exactly the lane's own weights (k-slots are
+//     keys 16(2ks + s/4) + 4(l/16) + s%4), B = V from LDS with the gfx950
+//     transpose read (4 keys x 1 d per lane per read); V reaches the
+//     wavefront's LDS tile by DMA in an order that makes those reads
+//     lane-linear.
+// K(t+1) is loaded during softmax and PV of tile t, V(t+1) during QK(t+1).
+
+typedef __bf16 mbf16x8_t __attribute__((ext_vector_type(8)));
+typedef float mf32x4_t __attribute__((ext_vector_type(4)));
+typedef short ms16x4_t __attribute__((ext_vector_type(4)));
+typedef float mf32x2_t __attribute__((ext_vector_type(2)));
+typedef __bf16 mbf16x2_t __attribute__((ext_vector_type(2)));
+
+constexpr int kMD = 128, kMRow = 256;
+constexpr int kMTile = kTileTok * kMRow;  // bytes of a K or V tile (16 KB)
+constexpr int kMUnit = 1024;              // one V DMA unit: 16 keys x 64 B of d
+
+__device__ __forceinline__ mbf16x8_t m_as_bf16x8(uint4 x) { return __builtin_bit_cast(mbf16x8_t, x); }
+__device__ __forceinline__ uint32_t m_cvt_pk_bf16(float a, float b) {
+  const mf32x2_t v = {a, b};
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, mbf16x2_t));
+}
+// gfx950 transpose LDS load: within each 16-lane group, lane i receives
+// element i%4 of the 8-byte words addressed by lanes i/4, i/4+4, i/4+8 and
+// i/4+12 of the group
+__device__ __forceinline__ uint2 m_read_tr16(const uint8_t* lds_ptr) {
+  const ms16x4_t v = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) ms16x4_t*)(lds_ptr));
+  return __builtin_bit_cast(uint2, v);
+}
+
+template <int G>
+__global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p) {
+  static_assert(G == 4 || G == 8, "heads padded to 16 MFMA rows");
+  constexpr int D = kMD;
+  // per-wavefront V tile; during set-up the same bytes hold the staged
+  // segment list, and at the end the per-wavefront states for the merge
+  __shared__ __align__(16) uint8_t v_lds[kNW][kMTile];
+  __shared__ __align__(16) int32_t blk_phys[kMaxSplitBlocks];
+  static_assert(sizeof(v_lds) >= 3 * (kMaxSplitBlocks + 1) * sizeof(int32_t), "staging");
+  static_assert(sizeof(v_lds) >= (kNW * G * D + 2 * kNW * G) * sizeof(float), "merge");
+
+  const int s = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
+  const int T = p.split_blocks;
+
+  const int s0 = p.indptr[b], s1 = p.indptr[b + 1];
+  int A = 0;
+  if (s1 > s0) {
+    const msa_segment last = p.segs[s1 - 1];
+    A = last.alive_token_start + last.num_tokens;
+  }
+  const int nAB = min((A + kBlk - 1) / kBlk, p.S * T);
+  const int Sb = (nAB + T - 1) / T;
+  if (s >= Sb) {
+    if (s == 0 && p.S == 1) {  // no alive token at all: O = 0, LSE = -inf
+      for (int i = tid; i < G * D; i += kThreads) {
+        const int h = g * G + i / D;
+        store_out<uint16_t>(p.out, (size_t(b) * p.Hq + h) * D + i % D, 0.f);
+        if (p.lse && i % D == 0) p.lse[size_t(b) * p.Hq + h] = -INFINITY;
+      }
+    }
+    return;
+  }
+  const int j0 = int(int64_t(s) * nAB / Sb);
+  const int nblk = int(int64_t(s + 1) * nAB / Sb) - j0;
+  const int last_tokens = min(kBlk, A - kBlk * (nAB - 1));
+
+  // ---- expand this split's segments into per-block physical ids ----------
+  {
+    const int sf = wg_search_segment(p.segs, s0, s1, j0 * kBlk);
+    const int ns = min(nblk, s1 - sf);
+    int32_t* st_start = reinterpret_cast<int32_t*>(&v_lds[0][0]);
+    int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
+    int32_t* st_nblk = st_phys + kMaxSplitBlocks + 1;
+    for (int i = tid; i < ns; i += kThreads) {
+      const msa_segment sg = p.segs[sf + i];
+      st_start[i] = sg.alive_token_start / kBlk;
+      const bool in_pool = sg.phys_block >= 0 && sg.num_blocks >= 0 &&
+                           int64_t(sg.phys_block) + sg.num_blocks <= p.P;
+      st_phys[i] = in_pool ? sg.phys_block : -1;
+      st_nblk[i] = in_pool ? sg.num_blocks : 0;
+    }
+    __syncthreads();
+    for (int jj = tid; jj < nblk; jj += kThreads) {
+      const int j = j0 + jj;
+      int lo = 0, hi = ns;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (st_start[mid] <= j) lo = mid; else hi = mid;
+      }
+      const int off = j - st_start[lo];
+      blk_phys[jj] = (st_phys[lo] >= 0 && off >= 0 && off < st_nblk[lo]) ? st_phys[lo] + off : -1;
+    }
+    __syncthreads();  // staging dead from here on: the V tiles may overwrite it
+  }
+
+  const int hl = lane % 16, q4 = lane / 16;
+  // Q^T operand: lane l holds head l%16 (zero past G), d 32 ds + 8(l/16)
+  uint4 qop[4];
+  {
+    const uint8_t* qsrc = static_cast<const uint8_t*>(p.q) + (size_t(b) * p.Hq + size_t(g) * G + hl) * kMRow;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      qop[ds] = hl < G ? *reinterpret_cast<const uint4*>(qsrc + (4 * ds + q4) * 16) : make_uint4(0, 0, 0, 0);
+  }
+
+  const size_t tok_stride = size_t(p.Hkv) * kMRow;
+  const size_t blk_stride = tok_stride * kBlk;
+  const char* kbase = static_cast<const char*>(p.k_pool) + size_t(g) * kMRow;
+  const char* vbase = static_cast<const char*>(p.v_pool) + size_t(g) * kMRow;
+  // K operand loads: lane offset inside a block for d step ds (adds 64 B each)
+  const uint32_t k_voff = uint32_t(hl * tok_stride + q4 * 16);
+  // V DMA unit (block, quarter dq of d): lane i writes 16 B at 16 i holding
+  // key 4(m/8) + (m%8)/2, d 32 dq + 16 e + 8(m%2) .. +7 (m = i%32, e = i/32):
+  // the transpose reads' words for lanes 2m and 2m+1 of half e
+  const int m32 = lane % 32, e2 = lane / 32;
+  const uint32_t v_voff = uint32_t((4 * (m32 / 8) + (m32 % 8) / 2) * tok_stride +
+                                   2 * (16 * e2 + 8 * (m32 % 2)));
+  uint8_t* vt = &v_lds[w][0];
+
+  mf32x4_t o[8];
+#pragma unroll
+  for (int dg = 0; dg < 8; ++dg) o[dg] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+  const float c = p.scale_log2;
+
+  const int ntiles = (nblk + 3) / 4;
+  const int last_local = nAB - 1 - j0;
+  // wave-uniform physical ids and readable row counts of tile ti's 4 blocks
+  // (one 16-byte LDS read; tiles past the split get empty ranges)
+  auto tile_blocks = [&](int ti, int* ph, int* rows) {
+    int4 v = make_int4(-1, -1, -1, -1);
+    if (ti < ntiles) v = *reinterpret_cast<const int4*>(&blk_phys[min(ti * 4, kMaxSplitBlocks - 4)]);
+    const int pv[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const int jj = ti * 4 + kg;
+      ph[kg] = __builtin_amdgcn_readfirstlane(jj < nblk ? pv[kg] : -1);
+      rows[kg] = ph[kg] < 0 ? 0 : (jj == last_local ? last_tokens : kBlk);
+    }
+  };
+  auto rsrc_of = [&](const char* base, int ph, int rows) {
+    return block_rsrc(base + size_t(ph < 0 ? 0 : ph) * blk_stride, uint32_t(rows * tok_stride));
+  };
+  uint4 kreg[4][4];
+  auto issue_k = [&](const int* ph, const int* rows) {
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const __amdgpu_buffer_rsrc_t r = rsrc_of(kbase, ph[kg], rows[kg]);
+      // (default cache policy: each 256-byte key row arrives as four 64-byte
+      // pieces from four loads, which must meet in the cache; measured 79 us
+      // against 99 us with the streaming hint on these loads)
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds) kreg[kg][ds] = load16_cached(r, k_voff + ds * 64);
+    }
+  };
+  auto issue_v = [&](const int* ph, const int* rows) {
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      const __amdgpu_buffer_rsrc_t r = rsrc_of(vbase, ph[kg], rows[kg]);
+#pragma unroll
+      for (int dq = 0; dq < 4; ++dq)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            r, (__attribute__((address_space(3))) void*)(vt + (kg * 4 + dq) * kMUnit), 16,
+            v_voff + dq * 64, 0, 0, kStreamPolicy);
+    }
+  };
+
+  int ti = w;
+  int ph[4], rows[4], phn[4], rowsn[4];
+  tile_blocks(ti, ph, rows);
+  issue_k(ph, rows);
+  issue_v(ph, rows);
+  for (; ti < ntiles; ti += kNW) {
+    // ---- S = K Q^T for the tile's 4 blocks ------------------------------
+    mf32x4_t sc[4];
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      sc[kg] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ds = 0; ds < 4; ++ds)
+        sc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(kreg[kg][ds]),
+                                                         m_as_bf16x8(qop[ds]), sc[kg], 0, 0, 0);
+    }
+    // next tile's K is in flight during softmax and PV of this one
+    tile_blocks(ti + kNW, phn, rowsn);
+    issue_k(phn, rowsn);
+
+    // ---- mask rows that do not exist (padding past ctx_len, missing blocks)
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      if (rows[kg] < kBlk) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) sc[kg][r] = 4 * q4 + r < rows[kg] ? sc[kg][r] : -INFINITY;
+      }
+    }
+    // ---- online softmax per head (lane l%16), lazy rescale ----------------
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) mx = fmaxf(mx, sc[kg][r]);
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool bump = (mx - m_run) * c > 8.f;
+    const float m_use = bump ? mx : m_run;
+    const float nm = m_use == -INFINITY ? 0.f : -m_use * c;
+    const float alpha = (m_use == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_use) * c);
+    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+      // O rows are heads 4(l/16) + r: fetch those heads' factors
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r);
+#pragma unroll
+      for (int dg = 0; dg < 8; ++dg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[dg][r] *= ar[r];
+    }
+    m_run = m_use;
+    float pw[4][4];
+    float lsum = 0.f;
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        pw[kg][r] = __builtin_amdgcn_exp2f(fmaf(sc[kg][r], c, nm));
+        lsum += pw[kg][r];
+      }
+    l_lane = l_lane * alpha + lsum;
+
+    // ---- O += P V ----------------------------------------------------------
+    // V(t) has landed once at most the 16 K loads of the next tile are still
+    // in flight.  Written out: the compiler's own tracking of LDS DMA was
+    // seen to let a transpose read run ahead of this wait.
+    asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint4 pop = make_uint4(m_cvt_pk_bf16(pw[2 * ks][0], pw[2 * ks][1]),
+                                   m_cvt_pk_bf16(pw[2 * ks][2], pw[2 * ks][3]),
+                                   m_cvt_pk_bf16(pw[2 * ks + 1][0], pw[2 * ks + 1][1]),
+                                   m_cvt_pk_bf16(pw[2 * ks + 1][2], pw[2 * ks + 1][3]));
+#pragma unroll
+      for (int dg = 0; dg < 8; ++dg) {
+        // k-slots 0..3: block 2ks, rows 4(l/16)+0..3; 4..7: block 2ks+1
+        const uint8_t* u0 = vt + ((2 * ks) * 4 + dg / 2) * kMUnit + (dg % 2) * (kMUnit / 2) + lane * 8;
+        const uint2 lo2 = m_read_tr16(u0);
+        const uint2 hi2 = m_read_tr16(u0 + 4 * kMUnit);
+        const uint4 vop = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+        o[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(pop), m_as_bf16x8(vop), o[dg],
+                                                        0, 0, 0);
+      }
+    }
+    // the V tile is free once its transpose reads have returned: next V in
+    // flight during the next QK
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    issue_v(phn, rowsn);
+#pragma unroll
+    for (int kg = 0; kg < 4; ++kg) {
+      ph[kg] = phn[kg];
+      rows[kg] = rowsn[kg];
+    }
+  }
+
+  // ---- merge the 4 wavefront states --------------------------------------
+  const float l_w = l_lane + __shfl_xor(l_lane, 16);
+  const float l_h = l_w + __shfl_xor(l_w, 32);
+  // no DMA may land in the V tiles once they hold the merge states
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+  __syncthreads();
+  float* mo = reinterpret_cast<float*>(&v_lds[0][0]);  // [kNW][G][D]
+  float* mm = mo + kNW * G * D;                        // [kNW][G]
+  float* ml = mm + kNW * G;
+#pragma unroll
+  for (int dg = 0; dg < 8; ++dg)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int h = 4 * q4 + r;
+      if (h < G) mo[(w * G + h) * D + dg * 16 + hl] = o[dg][r];
+    }
+  if (q4 == 0 && hl < G) {
+    mm[w * G + hl] = m_run;
+    ml[w * G + hl] = l_h;
+  }
+  __syncthreads();
+  for (int i = tid; i < G * D; i += kThreads) {
+    const int hh = i / D, d = i % D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int k = 0; k < kNW; ++k) M = fmaxf(M, mm[k * G + hh]);
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int k = 0; k < kNW; ++k) {
+        const float mk = mm[k * G + hh];
+        const float wt = mk == -INFINITY ? 0.f : exp2f((mk - M) * c);
+        L = fmaf(wt, ml[k * G + hh], L);
+        O = fmaf(wt, mo[(k * G + hh) * D + d], O);
+      }
+    }
+    const int h = g * G + hh;
+    const float Mc = M * c;  // log2 units
+    if (Sb == 1) {
+      store_out<uint16_t>(p.out, (size_t(b) * p.Hq + h) * D + d, L > 0.f ? O / L : 0.f);
+      if (p.lse && d == 0) p.lse[size_t(b) * p.Hq + h] = L > 0.f ? (Mc + log2f(L)) * kLn2 : -INFINITY;
+    } else {
+      const size_t n = size_t(b) * p.S + s;
+      p.o_part[(n * p.Hq + h) * D + d] = O;
+      if (d == 0) {
+        p.m_part[n * p.Hq + h] = M == -INFINITY ? -INFINITY : Mc * kLn2;
+        p.l_part[n * p.Hq + h] = L;
+      }
+    }
+  }
+}
+
 template <typename KV, int D, int G>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   dim3 grid(p.S, p.Hkv, p.B);
-  hipLaunchKernelGGL((decode_kernel<KV, D, G>), grid, dim3(kThreads), 0, stream, p);
+  // MFMA kernel: always for G 8 (the VALU kernel is compute-bound there:
+  // 119 against 81 us on the 32 x 4k batch with 64 query heads, 366 against
+  // 284 us on the 131k-token batch); for G 4 when each sequence takes at most
+  // four splits (79 against 84 us on the 32 x 4k batch), while on long,
+  // many-split contexts the VALU kernel's full-row loads measured faster
+  // (289 against 298 us on the lognormal batch, 241 against 274 us on the
+  // 131k-token layout with 32 query heads).
+  bool mfma = false;
+  if constexpr (std::is_same<KV, uint16_t>::value && D == kMD && (G == 4 || G == 8))
+    mfma = G == 8 || p.S <= 4;
+  if (mfma) {
+    if constexpr (std::is_same<KV, uint16_t>::value && D == kMD && (G == 4 || G == 8))
+      hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(kThreads), 0, stream, p);
+  } else {
+    hipLaunchKernelGGL((decode_kernel<KV, D, G>), grid, dim3(kThreads), 0, stream, p);
+  }
   return hipGetLastError();
 }
 

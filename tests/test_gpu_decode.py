@@ -126,6 +126,17 @@ def test_decode_determinism():
     assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
 
 
+def test_decode_determinism_full():
+    """Full-size headline batch, three calls: identical bits every time (the
+    tile pipeline must never read a V tile before its copy has landed)."""
+    w = make_workload(2, seed=0)
+    d = to_device(w, DEV)
+    O1, L1 = run_decode(w, 0, d)
+    for _ in range(2):
+        O2, L2 = run_decode(w, 0, d)
+        assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
 def test_decode_relayout_invariance():
     """The same alive content under a packed layout (few long segments) and
     under one block per segment gives the same output within tolerance."""
