@@ -847,6 +847,10 @@ SplitPlan decode_split(int32_t B, int32_t Hkv, int32_t max_ctx_len, int32_t bloc
     T = ((T + 15) / 16) * 16;
     if (T < 32) T = 32;
     if (T > 128) T = 128;
+    // When the (sequence, KV head) pairs alone fill the 256 CUs and no
+    // context exceeds 256 blocks, one split per pair needs no merge at all
+    // (77 against 81 us with two splits on the 32 x 4k batch).
+    if (pairs >= 256 && nbm <= 256) T = nbm > 0 ? nbm : 1;
   }
   sp.split_blocks = int32_t(T);
   sp.S = int32_t(nbm == 0 ? 1 : (nbm + T - 1) / T);
