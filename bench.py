@@ -412,7 +412,7 @@ def main():
             "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
                          "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                          "traffic": traffic, "traffic_unit": "bytes per call",
-                         "kernel": "msa_decode = decode_kernel<bf16,128,4> + merge_kernel",
+                         "kernel": "msa_decode (decode kernel, plus the split merge when a sequence has several splits)",
                          "algorithmic_bytes_per_call": int(alg_bytes),
                          "us_per_call": round(dec_s * 1e6, 3)},
             "plan_us_per_call": round(plan_s * 1e6, 3),
