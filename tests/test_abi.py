@@ -107,3 +107,48 @@ def test_merge_rejects_bad_args():
     assert lib.msa_merge_partials(NULL, FAKE, FAKE, FAKE, 1, 1, 1, 64, _lib.MSA_F32, FAKE, NULL, NULL) == _lib.MSA_ERR_INVALID_ARG
     assert lib.msa_merge_partials(FAKE, FAKE, FAKE, FAKE, 0, 1, 1, 64, _lib.MSA_F32, FAKE, NULL, NULL) == _lib.MSA_ERR_INVALID_ARG
     assert lib.msa_merge_partials(FAKE, FAKE, FAKE, FAKE, 1, 1, 1, 64, 9, FAKE, NULL, NULL) == _lib.MSA_ERR_UNSUPPORTED
+
+
+def _splits_from_workspace(lib, B, Hq, Hkv, D, ctx):
+    """Number of key splits the automatic rule picks, read back from the
+    decode workspace size (B*S partials of Hq*(D+2) floats, 256-B aligned)."""
+    ws = lib.msa_decode_workspace_size(B, Hq, Hkv, D, ctx, 16, 0)
+    if ws == 0:
+        return 1
+    for S in range(2, 100000):
+        want = sum(-(-n * 4 // 256) * 256 for n in (B * S * Hq * D, B * S * Hq, B * S * Hq))
+        if want == ws:
+            return S
+    raise AssertionError(ws)
+
+
+def test_decode_automatic_split_rule():
+    lib = _lib.load()
+    # the (sequence, KV head) pairs fill the 256 CUs and contexts are short:
+    # one split, no merge workspace
+    assert _splits_from_workspace(lib, 32, 32, 8, 128, 4096) == 1
+    # long contexts: splits of at most 128 blocks, never a multiple of 8
+    for B, Hq, ctx in ((4, 64, 131072), (64, 32, 32768), (4, 32, 65536), (2, 16, 20000)):
+        S = _splits_from_workspace(lib, B, Hq, 8, 128, ctx)
+        nbm = -(-ctx // 16)
+        assert S > 1 and S % 8 != 0
+        assert -(-nbm // S) <= 128
+
+
+def test_gather_rejects_bad_args():
+    lib = _lib.load()
+
+    def g(**kw):
+        a = dict(k=FAKE, v=FAKE, P=100, bs=16, segs=FAKE, indptr=FAKE, B=2, Hkv=8, D=128,
+                 dtype=_lib.MSA_BF16, bps=16, dk=FAKE, dv=FAKE, dsegs=FAKE, dind=FAKE)
+        a.update(kw)
+        return lib.msa_gather_alive(a["k"], a["v"], a["P"], a["bs"], a["segs"], a["indptr"], a["B"],
+                                    a["Hkv"], a["D"], a["dtype"], a["bps"], a["dk"], a["dv"],
+                                    a["dsegs"], a["dind"], NULL)
+
+    assert g(k=NULL) == _lib.MSA_ERR_INVALID_ARG
+    assert g(dind=NULL) == _lib.MSA_ERR_INVALID_ARG
+    assert g(B=0) == _lib.MSA_ERR_INVALID_ARG
+    assert g(bps=0) == _lib.MSA_ERR_INVALID_ARG
+    assert g(bs=32) == _lib.MSA_ERR_UNSUPPORTED
+    assert g(dtype=5) == _lib.MSA_ERR_UNSUPPORTED
