@@ -149,7 +149,10 @@ size_t msa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *   max_ctx_len  >= every sequence's number of alive tokens (sizes the grid)
  *   scale        softmax scale; <= 0 selects 1/sqrt(D)
  *   out          [B, Hq, D] dtype           lse_out  [B, Hq] float32, may be NULL
- * A sequence with no alive token gets out = 0 and lse = -inf. */
+ * A sequence with no alive token gets out = 0 and lse = -inf.  Accumulation
+ * is float32 throughout; for bf16 with D 128 and Hq/Hkv 4 or 8 the scores
+ * and the output run on bf16 matrix cores, so the softmax weights are rounded
+ * to bf16 for the P x V product (as in msa_prefill_chunk). */
 int msa_decode(const void* q, const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
                int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr, int32_t B,
                int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype,
