@@ -3,8 +3,12 @@
 // multi_segment_attention for one decode query per sequence (P1, "Core
 // method 1: MSA" pseudocode; P2, Key Results: one kernel over many disjoint
 // KV segments).  Decode is bandwidth-bound (it reads every resident K/V
-// row once per generated token; P3, "解决什么真问题", item 2), so this is a
-// VALU kernel built around the HBM stream, not a matrix-core kernel.
+// row once per generated token; P3, "解决什么真问题", item 2), so both
+// kernels here are built around the HBM stream: decode_kernel on the VALU,
+// and, for grouped-query bf16 with G 4 or 8, decode_mfma_kernel (further
+// below), which moves the G-head contractions onto matrix cores so that
+// the VALU does not cap the stream.  This comment describes decode_kernel;
+// the frame (grid, split rule, segment walk, merge) is shared.
 //
 // Grid: (split s, KV head g, sequence b); 256 threads = 4 wavefronts.
 //   * The sequence's alive blocks, in logical order, are numbered
@@ -25,9 +29,10 @@
 //   * Online softmax per wavefront: wave max by DPP + cross-row shuffles,
 //     exp2 with the scale folded into log2 units; the weights go through
 //     LDS and are broadcast to the PV loop, in which each lane owns a slice
-//     of D and accumulates fp32 for all G heads.  V rows of masked tokens
-//     (padding past ctx_len, blocks outside the split) are zeroed by a
-//     select, never multiplied by 0, so NaN-poisoned slots cannot leak.
+//     of D and accumulates fp32 for all G heads.  K/V rows of masked tokens
+//     (padding past ctx_len, blocks outside the split) lie outside their
+//     block's buffer descriptor and read as zero, so NaN-poisoned slots
+//     cannot leak into a product.
 //   * At the end the 4 wavefront states are merged in LDS; a sequence with
 //     one split writes O and LSE directly, otherwise the split writes its
 //     (m, l, o) partial for the merge kernel.

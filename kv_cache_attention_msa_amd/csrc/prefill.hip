@@ -14,19 +14,20 @@
 // all 256/G positions of the workgroup.
 //
 // Per 64-key tile and wavefront (one lane = one query row throughout):
-//   S^T[key][row] = K[key][:] . Q[row][:]     A = K from LDS (row-major,
-//                                             row-padded), B = Q in VGPRs
+//   S^T[key][row] = K[key][:] . Q[row][:]     A = K from LDS (operand-order
+//                                             DMA units), B = Q in VGPRs
 //   online softmax over the lane's 32 keys + the other half-wave's 32
-//   O^T[d][row] += V^T[d][key] . P^T[key][row] A = V^T read from the
-//                                             row-major V tile with the gfx950
-//                                             transpose load (ds_read_b64_tr_b16),
-//                                             B = P in VGPRs: exactly the lane's
-//                                             own S accumulators rounded to bf16
+//   O^T[d][row] += V^T[d][key] . P^T[key][row] A = V^T read from the V tile
+//                                             with the gfx950 transpose load
+//                                             (ds_read_b64_tr_b16), B = P in
+//                                             VGPRs: exactly the lane's own S
+//                                             accumulators rounded to bf16
 // Keys come from the sequence's segments in logical order: the workgroup
-// expands its segments into per-block (physical id, logical id) lists in LDS,
-// 512 blocks at a time.  Blocks are loaded through buffer descriptors whose
+// expands its segments into per-block (physical offset, logical id, rows)
+// lists in LDS, 256 blocks (64 tiles) at a time.  Tiles reach LDS by DMA
+// (buffer_load ... lds) through per-block buffer descriptors whose
 // num_records covers only the rows that exist, so missing blocks and padding
-// rows past ctx_len read as zero (and are masked); tiles straddling the
+// rows past ctx_len land as zeros (and are masked); tiles straddling the
 // causal diagonal are masked per element by logical position.
 #include "msa_internal.h"
 
