@@ -405,6 +405,9 @@ __global__ void __launch_bounds__((PGeo<G, RT>::THREADS), (PGeo<G, RT>::WAVES / 
     __syncthreads();
     f32x16_t s_a[RT][2], s_b[RT][2];
     scores(&k_lds[0][0], s_a);
+    // every wavefront has read K(0) before the first step's DMA rewrites
+    // its stage
+    __syncthreads();
     // One pipeline step for tile ti: scores of ti are in sc, those of ti+1
     // go to sn.  Returns true when this chunk is finished.
     auto step = [&](int ti, f32x16_t (*sc)[2], f32x16_t (*sn)[2]) -> bool {
