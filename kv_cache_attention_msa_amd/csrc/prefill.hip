@@ -97,6 +97,15 @@ __device__ __forceinline__ uint2 ds_read_tr16(const uint8_t* lds_ptr) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// max of x over lanes l and l ^ 32: gfx950's v_permlane32_swap exchanges the
+// two halves of the wavefront in one VALU instruction, keeping the LDS
+// permute unit's latency out of the per-tile softmax chain
+__device__ __forceinline__ float max_halves(float x) {
+  const uint32_t u = __builtin_bit_cast(uint32_t, x);
+  const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+  return fmaxf(__builtin_bit_cast(float, uint32_t(r[0])), __builtin_bit_cast(float, uint32_t(r[1])));
+}
+
 typedef float f32x2_t __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // two floats -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32)
@@ -446,7 +455,7 @@ __global__ void __launch_bounds__((PGeo<G, RT>::THREADS), (PGeo<G, RT>::WAVES / 
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
         for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[r][kb2][i]);
-      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      mx = max_halves(mx);
       // Lazy rescaling: a row keeps its reference max m_run until the true
       // max exceeds it by more than 2^8 in the exponent; the weights are then
       // at most 256 (harmless for fp32 sums and for bf16's relative
@@ -472,9 +481,12 @@ __global__ void __launch_bounds__((PGeo<G, RT>::THREADS), (PGeo<G, RT>::WAVES / 
       // ---- P and O^T += V^T P^T for tile ti, one key step of 16 at a time --
       // (each P operand is built right before its four MFMAs, so only one is
       // live)
-      float lsum[RT];
+      // four partial sums per row keep the additions out of one long chain
+      float lsum[RT][4];
 #pragma unroll
-      for (int r = 0; r < RT; ++r) lsum[r] = 0.f;
+      for (int r = 0; r < RT; ++r)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) lsum[r][e] = 0.f;
       const uint8_t* vt = &v_lds[ti % kStages][0] + v_lane_off;
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
@@ -485,7 +497,7 @@ __global__ void __launch_bounds__((PGeo<G, RT>::THREADS), (PGeo<G, RT>::WAVES / 
 #pragma unroll
           for (int e = 0; e < 8; ++e) {
             pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[r][t / 2][8 * (t % 2) + e], c, nm[r]));
-            lsum[r] += pv[e];
+            lsum[r][e % 4] += pv[e];
           }
           pop[r] = make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
                               cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7]));
@@ -506,7 +518,8 @@ __global__ void __launch_bounds__((PGeo<G, RT>::THREADS), (PGeo<G, RT>::WAVES / 
         }
       }
 #pragma unroll
-      for (int r = 0; r < RT; ++r) l_lane[r] = l_lane[r] * alpha[r] + lsum[r];
+      for (int r = 0; r < RT; ++r)
+        l_lane[r] = l_lane[r] * alpha[r] + ((lsum[r][0] + lsum[r][1]) + (lsum[r][2] + lsum[r][3]));
       if (!more) {
         // either the chunk is exhausted (go on with the next one) or the next
         // tile starts after every row (stop: later keys are later still)

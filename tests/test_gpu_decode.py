@@ -94,6 +94,17 @@ def test_decode_cfg2_full():
     check(w, O, L)
 
 
+@pytest.mark.parametrize("split_blocks", [64, 16])
+def test_decode_cfg2_full_forced_splits(split_blocks):
+    """The headline batch needs no merge under the automatic split rule; forced
+    splits of 64 blocks (4 per sequence, matrix-core kernel + merge) and 16
+    blocks (16 per sequence, vector kernel + merge) cover those paths at full
+    size."""
+    w = make_workload(2, seed=0)
+    O, L = run_decode(w, split_blocks)
+    check(w, O, L)
+
+
 @pytest.mark.parametrize("cfg", [4, 5])
 def test_decode_full_sampled(cfg):
     w = make_workload(cfg, seed=0)
