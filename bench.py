@@ -57,6 +57,9 @@ def parse():
                     help="fit the decode latency model used by the eviction scorer")
     ap.add_argument("--chunk-sweep", action="store_true",
                     help="also time the prefill workload at chunk sizes 128..2048")
+    ap.add_argument("--more-decode", action="store_true",
+                    help="also time msa_decode on the lognormal shared-prefix batch and the "
+                         "131k-token fragmented batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
@@ -82,6 +85,21 @@ def alive_tokens_per_seq(w):
         tok = np.minimum(w.block_size, n - w.block_size * np.arange(nb))
         out.append(int((tok * (w.alive[b, :nb] != 0)).sum()))
     return out
+
+
+def unique_alive_bytes(w):
+    """K+V bytes of the distinct alive pool blocks (a block shared by several
+    sequences, such as a common prefix, counted once)."""
+    import numpy as np
+    tok = {}
+    for b in range(w.B):
+        n = int(w.ctx_len[b])
+        nb = -(-n // w.block_size)
+        for l in np.nonzero(w.alive[b, :nb])[0]:
+            t = min(w.block_size, n - w.block_size * int(l))
+            ph = int(w.block_table[b, l])
+            tok[ph] = max(tok.get(ph, 0), t)
+    return sum(tok.values()) * w.Hkv * w.D * (2 if w.dtype == "bf16" else 4) * 2
 
 
 def visible_pairs(w):
@@ -451,6 +469,29 @@ def main():
     # ------------------------------------------- decode latency model (next)
     if args.latency_model:
         result["latency_model"] = latency_model_leg(args)
+
+    # ------------------------- decode on the other two decode families
+    if args.more_decode and args.only in (None, "decode"):
+        legs = []
+        for fam in (4, 5):
+            wf = make_workload(fam, seed=args.seed)
+            prep = Prepared(wf, args.split_blocks)
+            prep.plan()
+            for _ in range(3):
+                prep.attention()
+            torch.cuda.synchronize()
+            t = time_calls(prep.attention, max(10, args.steps // 10), prep.stream)
+            logical = sum(alive_tokens_per_seq(wf)) * wf.Hkv * wf.D * (2 if wf.dtype == "bf16" else 4) * 2
+            unique = unique_alive_bytes(wf)
+            legs.append({"workload": NAMES[fam], "us_per_call": round(t * 1e6, 3),
+                         "logical_bytes": logical, "unique_bytes": unique,
+                         "GB/s_logical": round(logical / t / 1e9, 1),
+                         "GB/s_unique": round(unique / t / 1e9, 1),
+                         "pct_hbm_peak_unique": round(100 * unique / t / 1e9 / HBM_PEAK_GBS, 2),
+                         "tokens_per_s": round(wf.B / t, 1)})
+            del prep, wf
+            torch.cuda.empty_cache()
+        result["more_decode"] = legs
 
     # --------------------------------------------------------------- prefill
     import kv_cache_attention_msa_amd as msa
