@@ -198,3 +198,32 @@ def test_merge_partials_parity():
         fin = np.isfinite(Lr)
         assert np.max(np.abs(Lg[fin] - Lr[fin])) <= 1e-5
         assert np.all(np.isneginf(Lg[~fin]))
+
+
+def test_merge_partials_many_and_ragged():
+    """Sequences with 0..37 partials (the four-way split of the partial list
+    gets empty, short and uneven quarters), head x dim not a multiple of the
+    64-element workgroup, and an all-empty quarter."""
+    rng = np.random.default_rng(11)
+    B, R, H, D = 5, 2, 3, 40
+    counts = [37, 1, 2, 0, 5]
+    ind = np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
+    N = int(ind[-1])
+    o = rng.standard_normal((N, R, H, D)).astype(np.float32)
+    m = (rng.standard_normal((N, R, H)) * 4).astype(np.float32)
+    l = rng.uniform(0.5, 20, size=(N, R, H)).astype(np.float32)
+    m[0:9, 1, 2] = -np.inf      # the first quarter of sequence 0 empty for one row/head
+    l[0:9, 1, 2] = 0
+    o[0:9, 1, 2] = np.nan
+    m[30, 0, 0] = 40.0          # a late partial with a much larger maximum
+    for dt, tol in ((torch.float32, 1e-5), (torch.bfloat16, 2e-2)):
+        out, lse = msa.msa_merge_partials(tensor(o, DEV), tensor(m, DEV), tensor(l, DEV),
+                                          tensor(ind, DEV), out_dtype=dt)
+        torch.cuda.synchronize()
+        Or, Lr = oracle.merge_ref(o, m, l, ind)
+        Og = from_device(out)
+        Lg = lse.cpu().numpy().astype(np.float64)
+        assert np.max(np.abs(Og - Or)) <= tol
+        fin = np.isfinite(Lr)
+        assert np.max(np.abs(Lg[fin] - Lr[fin])) <= 1e-5
+        assert np.all(np.isneginf(Lg[~fin]))
