@@ -102,16 +102,18 @@ def unique_alive_bytes(w):
     return sum(tok.values()) * w.Hkv * w.D * (2 if w.dtype == "bf16" else 4) * 2
 
 
-def visible_pairs(w):
-    """(query row, key) pairs with key position <= row position, over alive keys."""
+def visible_pairs(w, rows=None):
+    """(query row, key) pairs with key position <= row position, over alive
+    keys (all chunk rows, or only the given row indices)."""
     import numpy as np
+    rows = np.arange(w.C) if rows is None else np.asarray(rows)
     tot = 0
     for b in range(w.B):
         n = int(w.ctx_len[b])
         pos = np.arange(n)
         keep = w.alive[b, pos // w.block_size] != 0
         kpos = pos[keep]
-        qpos = int(w.q_pos0[b]) + np.arange(w.C)
+        qpos = int(w.q_pos0[b]) + rows
         tot += int(np.searchsorted(kpos, qpos, side="right").sum())
     return tot
 
@@ -369,6 +371,35 @@ def cpu_baseline(w, bytes_per_pass, budget_s=10.0, max_reps=20):
             "seconds_per_pass": round(dt / reps, 4)}
 
 
+def prefill_cpu_baseline(w, row_step=16, budget_s=10.0, max_reps=5):
+    """The fp64 oracle, as it stands, on a row sample of the prefill workload:
+    every row_step-th chunk row of every sequence and head, over all the keys
+    each row sees."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    rows = np.arange(0, w.C, row_step)
+    flops = 4.0 * w.D * w.Hq * visible_pairs(w, rows)
+    reps, t0 = 0, time.perf_counter()
+    while reps < max_reps:
+        oracle.prefill_ref(w.q, w.q_pos0, w.k_pool, w.v_pool, w.block_table, w.alive, w.ctx_len,
+                           w.block_size, w.scale, rows=rows)
+        reps += 1
+        if time.perf_counter() - t0 >= budget_s:
+            break
+    dt = time.perf_counter() - t0
+    return {"value": round(flops * reps / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"fp64 numpy oracle (prefill_ref) on every {row_step}th chunk row "
+                      f"({len(rows)} of {w.C}) of all {w.B} sequences x {w.Hq} heads, visible keys "
+                      f"only; {reps} passes in {dt:.1f} s; BLAS threads {threads}",
+            "seconds_per_pass": round(dt / reps, 4)}
+
+
 def main():
     args = parse()
     world = int(os.environ.get("WORLD_SIZE", "1"))
@@ -517,6 +548,8 @@ def main():
                            "traffic": pf_traffic, "traffic_unit": "bytes per call",
                            "kernel": "msa_prefill_chunk",
                            "algorithmic_flops_per_call": leg.pop("flops")}
+        if not args.no_cpu_baseline:
+            leg["cpu_baseline"] = prefill_cpu_baseline(wp)
         result["prefill"] = {"workload": NAMES[3], **leg}
         del wp
         # recompute of an evicted middle range (chunk rows in the middle of the
