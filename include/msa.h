@@ -178,11 +178,18 @@ size_t msa_prefill_workspace_size(int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
  *
  *   q       [B, C, Hq, D] bf16     q_pos0  int32 [B] (device)
  *   out     [B, C, Hq, D] bf16     lse_out [B, C, Hq] float32, may be NULL
- *   split_blocks  0 = one split per (row tile, KV head, sequence); otherwise
- *                 the alive-key stream is cut into near-equal splits of at
- *                 most that many blocks, merged by log-sum-exp through
- *                 `workspace`.
- * A row that sees no key gets out = 0 and lse = -inf. */
+ *   split_blocks  0 = automatic: the alive-key stream is split only when the
+ *                 (row tile, KV head, sequence) work items do not cover the
+ *                 chip's 256 CUs; otherwise it is cut into near-equal splits
+ *                 of at most that many blocks.  Splits are merged by
+ *                 log-sum-exp through `workspace`.
+ * A row that sees no key gets out = 0 and lse = -inf.
+ * Errors (returned before any launch): MSA_ERR_INVALID_ARG for null
+ * pointers, C <= 0 or bad shapes; MSA_ERR_UNSUPPORTED for shapes not built
+ * (msa_attention_supported) and when B x splits > 65535 or, with more than
+ * one split, C > 65535 (launch-grid limits); MSA_ERR_CAPACITY when a split
+ * is needed and the workspace is missing or smaller than
+ * msa_prefill_workspace_size. */
 int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const void* k_pool,
                       const void* v_pool, int32_t num_phys_blocks, int32_t block_size,
                       const msa_segment* segs, const int32_t* seg_indptr, int32_t B, int32_t Hq,

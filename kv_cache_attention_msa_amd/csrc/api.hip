@@ -191,6 +191,8 @@ int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const voi
   if (!prefill_supported(dtype, D, Hq / Hkv)) return MSA_ERR_UNSUPPORTED;
   if (split_blocks > prefill_max_split_blocks()) return MSA_ERR_INVALID_ARG;
   const SplitPlan sp = prefill_split(B, C, Hq, Hkv, max_ctx_len, block_size, split_blocks);
+  // grid z is (sequence, split); the split merge's grid y is the chunk row
+  if (int64_t(B) * sp.S > 65535 || (sp.S > 1 && C > 65535)) return MSA_ERR_UNSUPPORTED;
   const size_t need =
       msa_prefill_workspace_size(B, C, Hq, Hkv, D, max_ctx_len, block_size, split_blocks);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MSA_ERR_CAPACITY;

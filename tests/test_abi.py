@@ -152,3 +152,48 @@ def test_gather_rejects_bad_args():
     assert g(bps=0) == _lib.MSA_ERR_INVALID_ARG
     assert g(bs=32) == _lib.MSA_ERR_UNSUPPORTED
     assert g(dtype=5) == _lib.MSA_ERR_UNSUPPORTED
+
+
+def _prefill(lib, **kw):
+    a = dict(q=FAKE, C=512, qpos=FAKE, k=FAKE, v=FAKE, P=100, bs=16, segs=FAKE, indptr=FAKE, B=4,
+             Hq=32, Hkv=8, D=128, maxctx=8704, dtype=_lib.MSA_BF16, scale=0.0, split=0, out=FAKE,
+             lse=NULL, ws=FAKE, wsb=1 << 30, stream=NULL)
+    a.update(kw)
+    return lib.msa_prefill_chunk(a["q"], a["C"], a["qpos"], a["k"], a["v"], a["P"], a["bs"], a["segs"],
+                                 a["indptr"], a["B"], a["Hq"], a["Hkv"], a["D"], a["maxctx"], a["dtype"],
+                                 a["scale"], a["split"], a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+
+
+def test_prefill_rejects_bad_args():
+    lib = _lib.load()
+    assert _prefill(lib, q=NULL) == _lib.MSA_ERR_INVALID_ARG
+    assert _prefill(lib, qpos=NULL) == _lib.MSA_ERR_INVALID_ARG
+    assert _prefill(lib, C=0) == _lib.MSA_ERR_INVALID_ARG
+    assert _prefill(lib, Hq=30) == _lib.MSA_ERR_INVALID_ARG        # Hq % Hkv
+    assert _prefill(lib, scale=float("inf")) == _lib.MSA_ERR_INVALID_ARG
+    assert _prefill(lib, dtype=_lib.MSA_F32) == _lib.MSA_ERR_UNSUPPORTED
+    assert _prefill(lib, D=64) == _lib.MSA_ERR_UNSUPPORTED
+    assert _prefill(lib, Hq=24) == _lib.MSA_ERR_UNSUPPORTED        # G = 3
+    assert _prefill(lib, Hq=128, Hkv=8) == _lib.MSA_ERR_UNSUPPORTED  # G = 16
+    # a small chunk splits the key stream: the workspace must hold the partials
+    need = lib.msa_prefill_workspace_size(1, 16, 32, 8, 128, 8192, 16, 0)
+    assert need > 0
+    assert _prefill(lib, B=1, C=16, maxctx=8192, wsb=need - 1) == _lib.MSA_ERR_CAPACITY
+    assert _prefill(lib, B=1, C=16, maxctx=8192, ws=NULL) == _lib.MSA_ERR_CAPACITY
+    # launch-grid limits: (sequence, split) pairs above 65535, or a split chunk
+    # with more rows than the merge grid takes
+    assert _prefill(lib, B=40000, C=16, maxctx=1 << 20, split=64) == _lib.MSA_ERR_UNSUPPORTED
+    assert _prefill(lib, B=1, C=70000, maxctx=1 << 20, split=64) == _lib.MSA_ERR_UNSUPPORTED
+
+
+def test_header_compiles_as_c_and_cpp(tmp_path):
+    import shutil
+    import subprocess
+    for cc, lang, std in (("gcc", "c", "-std=c99"), ("g++", "c++", "-std=c++11")):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not available")
+        src = tmp_path / f"use.{lang[0]}"
+        src.write_text('#include "msa.h"\nint use(void) { return msa_version(); }\n')
+        r = subprocess.run([cc, "-x", lang, std, "-Wall", "-Werror", "-pedantic", "-fsyntax-only",
+                            "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
