@@ -846,12 +846,18 @@ SplitPlan decode_split(int32_t B, int32_t Hkv, int32_t max_ctx_len, int32_t bloc
     // per-split set-up and partial write are small next to its 8 MB of K/V
     // per KV head (bf16, D 128), short enough that a few long contexts in a
     // skewed batch do not leave most CUs idle.  Short batches get shorter
-    // splits (down to 32 blocks) so the grid still covers the chip.
+    // splits (down to 32 blocks) so the grid still covers the chip.  When
+    // the (sequence, KV head) pairs alone cover the 256 CUs the cap is 192
+    // blocks: the grid is sized by the longest context, so shorter splits
+    // mostly add workgroups with nothing to do and partials to merge (the
+    // 64-sequence lognormal batch: 249 against 261 us at 120 blocks; the
+    // 4-sequence 131k batch, 32 pairs, is best at 120-136 blocks).
     const int64_t pairs = int64_t(B) * Hkv;
+    const int64_t cap = pairs >= 256 ? 192 : 128;
     T = (nbm * pairs + 511) / 512;
     T = ((T + 15) / 16) * 16;
     if (T < 32) T = 32;
-    if (T > 128) T = 128;
+    if (T > cap) T = cap;
     // When the (sequence, KV head) pairs alone fill the 256 CUs and no
     // context exceeds 256 blocks, one split per pair needs no merge at all
     // (77 against 81 us with two splits on the 32 x 4k batch).

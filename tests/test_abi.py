@@ -127,12 +127,17 @@ def test_decode_automatic_split_rule():
     # the (sequence, KV head) pairs fill the 256 CUs and contexts are short:
     # one split, no merge workspace
     assert _splits_from_workspace(lib, 32, 32, 8, 128, 4096) == 1
-    # long contexts: splits of at most 128 blocks, never a multiple of 8
+    # long contexts: splits of at most 128 blocks (192 when the pairs alone
+    # cover the 256 CUs), never a multiple of 8
     for B, Hq, ctx in ((4, 64, 131072), (64, 32, 32768), (4, 32, 65536), (2, 16, 20000)):
         S = _splits_from_workspace(lib, B, Hq, 8, 128, ctx)
         nbm = -(-ctx // 16)
         assert S > 1 and S % 8 != 0
-        assert -(-nbm // S) <= 128
+        assert -(-nbm // S) <= (192 if B * 8 >= 256 else 128)
+    # the 64-sequence batch with contexts up to 32k: 192-block splits
+    assert _splits_from_workspace(lib, 64, 32, 8, 128, 32768) == 11
+    # the 4-sequence 131k batch keeps 120-block splits (128 would give 64 splits)
+    assert _splits_from_workspace(lib, 4, 64, 8, 128, 131072) == 69
 
 
 def test_gather_rejects_bad_args():
