@@ -178,7 +178,7 @@ def _live_slots(P, bs, block_table, alive, ctx_len):
 # the five workload families
 # ----------------------------------------------------------------------------
 
-def _cfg1(rng, B=1, Hq=8, Hkv=2, D=64, nb=64, pool=256, n_evict=16, dtype="f32"):
+def _decode_fp32_permuted(rng, B=1, Hq=8, Hkv=2, D=64, nb=64, pool=256, n_evict=16, dtype="f32"):
     """Decode, fp32: table = first nb entries of a random permutation of the pool;
     exactly n_evict of the first nb-1 blocks evicted uniformly."""
     bs = 16
@@ -232,7 +232,7 @@ def _geom_runs_layout(rng, B, nb_cached, mean_alive, mean_dead, chunk_blocks, po
     return alive, table, P
 
 
-def _cfg2(rng, B=32, Hq=32, Hkv=8, D=128, ctx=4096, mean_alive=8.0, mean_dead=2.0,
+def _decode_geometric_runs(rng, B=32, Hq=32, Hkv=8, D=128, ctx=4096, mean_alive=8.0, mean_dead=2.0,
           dtype="bf16", pool_factor=1.25):
     """Decode, bf16: alternating alive ~ Geom(mean 8) / evicted ~ Geom(mean 2) runs."""
     bs = 16
@@ -245,7 +245,7 @@ def _cfg2(rng, B=32, Hq=32, Hkv=8, D=128, ctx=4096, mean_alive=8.0, mean_dead=2.
                 block_table=table, alive=alive, ctx_len=ctx_len, q=q, k_pool=kp, v_pool=vp)
 
 
-def _cfg3(rng, B=4, Hq=32, Hkv=8, D=128, cached=8192, C=512, mean_alive=16.0,
+def _prefill_chunk(rng, B=4, Hq=32, Hkv=8, D=128, cached=8192, C=512, mean_alive=16.0,
           evict_frac=0.15, dtype="bf16"):
     """Chunked prefill, bf16: C query rows at positions [cached, cached+C) over
     the alive cached blocks plus the chunk's own blocks (causal)."""
@@ -264,7 +264,7 @@ def _cfg3(rng, B=4, Hq=32, Hkv=8, D=128, cached=8192, C=512, mean_alive=16.0,
                 C=C, q_pos0=q_pos0)
 
 
-def _cfg6(rng, B=4, Hq=32, Hkv=8, D=128, ctx=8704, q_pos0=4096, C=512, mean_alive=16.0,
+def _prefill_recompute_middle(rng, B=4, Hq=32, Hkv=8, D=128, ctx=8704, q_pos0=4096, C=512, mean_alive=16.0,
           evict_frac=0.15, dtype="bf16"):
     """Recompute (lossless reconstruction), bf16: an evicted range of C tokens
     in the middle of the context, [q_pos0, q_pos0+C), is recomputed as a
@@ -305,7 +305,7 @@ def _cfg6(rng, B=4, Hq=32, Hkv=8, D=128, ctx=8704, q_pos0=4096, C=512, mean_aliv
                 C=C, q_pos0=np.full(B, q_pos0, dtype=np.int32))
 
 
-def _cfg4(rng, B=64, Hq=32, Hkv=8, D=128, median=6144, sigma=0.75, lo=2064, hi=32768,
+def _decode_lognormal_shared_prefix(rng, B=64, Hq=32, Hkv=8, D=128, median=6144, sigma=0.75, lo=2064, hi=32768,
           shared_tokens=2048, group=16, evict_frac=0.3, dtype="bf16"):
     """Multi-session decode mix: lognormal contexts, a shared prefix per group of
     sequences (one contiguous run, never evicted), a fraction of each sequence's
@@ -347,7 +347,7 @@ def _cfg4(rng, B=64, Hq=32, Hkv=8, D=128, median=6144, sigma=0.75, lo=2064, hi=3
                 block_table=table, alive=alive, ctx_len=ctx_len, q=q, k_pool=kp, v_pool=vp)
 
 
-def _cfg5(rng, B=4, Hq=64, Hkv=8, D=128, ctx=131072, dtype="bf16"):
+def _decode_long_fragmented(rng, B=4, Hq=64, Hkv=8, D=128, ctx=131072, dtype="bf16"):
     """Long-context fragmented decode: alive/evicted runs of 1-2 blocks each;
     every alive block at its own random pool slot."""
     bs = 16
@@ -369,7 +369,7 @@ def _cfg5(rng, B=4, Hq=64, Hkv=8, D=128, ctx=131072, dtype="bf16"):
                 block_table=table, alive=alive, ctx_len=ctx_len, q=q, k_pool=kp, v_pool=vp)
 
 
-_FAMILIES = {1: _cfg1, 2: _cfg2, 3: _cfg3, 4: _cfg4, 5: _cfg5, 6: _cfg6}
+_FAMILIES = {1: _decode_fp32_permuted, 2: _decode_geometric_runs, 3: _prefill_chunk, 4: _decode_lognormal_shared_prefix, 5: _decode_long_fragmented, 6: _prefill_recompute_middle}
 
 NAMES = {
     1: "decode_f32_b1_h8kv2_d64_ctx1k_evict25_randperm",
@@ -392,19 +392,19 @@ SMALL = {
 }
 
 
-def make_workload(cfg: int, seed: int = 0, size: str = "full", values: bool = True,
+def make_workload(family: int, seed: int = 0, size: str = "full", values: bool = True,
                   **overrides) -> Workload:
-    """Draw workload family ``cfg`` (1..6) with ``seed``.
+    """Draw workload family ``family`` (1..6) with ``seed``.
 
     size="full" uses the family's defining sizes, "small" the reduced ones;
     keyword overrides change individual shape parameters.  values=False skips
     the Q/K/V draw (they come last, so the tables are the same either way):
     q and v_pool are then None and k_pool is an empty [P, 0] placeholder.
     """
-    fn = _FAMILIES[cfg]
+    fn = _FAMILIES[family]
     kw = {}
     if size == "small":
-        kw.update(SMALL[cfg])
+        kw.update(SMALL[family])
     elif size != "full":
         raise ValueError(size)
     kw.update(overrides)
@@ -415,13 +415,13 @@ def make_workload(cfg: int, seed: int = 0, size: str = "full", values: bool = Tr
     finally:
         _VALUES["on"] = True
     D = d["D"]
-    w = Workload(name=NAMES[cfg] if size == "full" and not overrides else f"{NAMES[cfg]}[{size}]",
+    w = Workload(name=NAMES[family] if size == "full" and not overrides else f"{NAMES[family]}[{size}]",
                  scale=1.0 / math.sqrt(D), **d)
     bs = w.block_size
     nb = -(-w.ctx_len.astype(np.int64) // bs)
     tot = int(nb.sum())
     alive_blocks = int(sum(int(w.alive[b, :nb[b]].sum()) for b in range(w.B)))
-    w.meta = dict(seed=seed, cfg=cfg, size=size, pool_blocks=w.num_phys_blocks,
+    w.meta = dict(seed=seed, family=family, size=size, pool_blocks=w.num_phys_blocks,
                   logical_blocks=tot, alive_blocks=alive_blocks,
                   evicted_fraction=1.0 - alive_blocks / max(tot, 1))
     return w
