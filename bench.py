@@ -244,6 +244,21 @@ def time_calls(fn, n, stream):
     return e0.elapsed_time(e1) / n * 1e-3  # seconds
 
 
+def call_percentiles(fn, n, stream):
+    """p10 / median / p90 of single-call durations (us), each call between
+    its own pair of HIP events on the launch stream, calls back to back."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
+    for a, b in ev:
+        a.record(stream)
+        fn()
+        b.record(stream)
+    ev[-1][1].synchronize()
+    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
+    q = lambda f: us[min(n - 1, int(round(f * (n - 1))))]
+    return {"p10": round(q(0.1), 3), "p50": round(q(0.5), 3), "p90": round(q(0.9), 3), "calls": n}
+
+
 def time_cold(fn, n, stream, flush):
     """Median duration of fn() when a 1 GiB read evicts L2 and the Infinity
     Cache before every call (the read is outside the events; a read leaves
@@ -280,6 +295,7 @@ def prefill_leg(w, n, warm):
             prep.attention()
         torch.cuda.synchronize()
     t = time_calls(prep.attention, n, prep.stream)
+    dist = call_percentiles(prep.attention, n, prep.stream)
     tfs = flops / t / 1e12
     del prep
     G = w.Hq // w.Hkv
@@ -288,6 +304,7 @@ def prefill_leg(w, n, warm):
     items = -(-w.C * G // 256) * w.Hkv * w.B
     return {"us_per_call": round(t * 1e6, 3), "TFLOP/s": round(tfs, 2),
             "pct_mfma_bf16_peak": round(100 * tfs / MFMA_BF16_PEAK_TFS, 2), "calls": n,
+            "call_us": dist,
             "row_tile_items": items, "flops": flops}
 
 
@@ -444,6 +461,7 @@ def main():
         step_s = (time.perf_counter() - t0) / args.steps
         # dominant call: msa_decode (decode kernel + its split merge), HIP events
         dec_s = time_calls(prep.attention, args.steps, stream)
+        dec_dist = call_percentiles(prep.attention, args.steps, stream)
         plan_s = time_calls(prep.plan, args.steps, stream)
         value = alg_bytes / step_s / 1e9
         achieved = alg_bytes / dec_s / 1e9
@@ -473,6 +491,7 @@ def main():
                          "us_per_call": round(dec_s * 1e6, 3)},
             "plan_us_per_call": round(plan_s * 1e6, 3),
             "decode_tokens_per_s": round(w.B / dec_s, 1),
+            "decode_call_us": dec_dist,
         })
         if not args.no_cold:
             flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
