@@ -278,6 +278,27 @@ def time_cold(fn, n, stream, flush):
     return statistics.median(ts)
 
 
+def realised(w, prep):
+    """What the seeded draw actually produced: eviction fraction, segment
+    count (from the device plan) and context lengths."""
+    import numpy as np
+    ctx = np.asarray(w.ctx_len)
+    return {"evicted_fraction": round(float(w.meta["evicted_fraction"]), 4),
+            "segments": int(prep.indptr[-1].item()),
+            "ctx_len": {"min": int(ctx.min()), "median": int(np.median(ctx)), "max": int(ctx.max())}}
+
+
+def warm_for(fn, seconds=0.25):
+    """Run fn in bursts for a while: the first milliseconds of a burst run at
+    a lower clock."""
+    import torch
+    t_end = time.perf_counter() + seconds
+    while time.perf_counter() < t_end:
+        for _ in range(10):
+            fn()
+        torch.cuda.synchronize()
+
+
 def prefill_leg(w, n, warm):
     """Time msa_prefill_chunk (plus its merge when split) on workload w."""
     import torch
@@ -289,14 +310,11 @@ def prefill_leg(w, n, warm):
     torch.cuda.synchronize()
     # keep the matrix cores busy for a quarter second before timing: the
     # first milliseconds of a burst run at a lower clock (about 10% slower)
-    t_end = time.perf_counter() + 0.25
-    while time.perf_counter() < t_end:
-        for _ in range(10):
-            prep.attention()
-        torch.cuda.synchronize()
+    warm_for(prep.attention)
     t = time_calls(prep.attention, n, prep.stream)
     dist = call_percentiles(prep.attention, n, prep.stream)
     tfs = flops / t / 1e12
+    stats = realised(w, prep)
     del prep
     G = w.Hq // w.Hkv
     # (256 query rows, KV head, sequence) work items: one workgroup each; the
@@ -304,7 +322,7 @@ def prefill_leg(w, n, warm):
     items = -(-w.C * G // 256) * w.Hkv * w.B
     return {"us_per_call": round(t * 1e6, 3), "TFLOP/s": round(tfs, 2),
             "pct_mfma_bf16_peak": round(100 * tfs / MFMA_BF16_PEAK_TFS, 2), "calls": n,
-            "call_us": dist,
+            "call_us": dist, **stats,
             "row_tile_items": items, "flops": flops}
 
 
@@ -534,9 +552,7 @@ def main():
             wf = make_workload(fam, seed=args.seed)
             prep = Prepared(wf, args.split_blocks)
             prep.plan()
-            for _ in range(3):
-                prep.attention()
-            torch.cuda.synchronize()
+            warm_for(prep.attention)
             t = time_calls(prep.attention, max(10, args.steps // 10), prep.stream)
             logical = sum(alive_tokens_per_seq(wf)) * wf.Hkv * wf.D * (2 if wf.dtype == "bf16" else 4) * 2
             unique = unique_alive_bytes(wf)
@@ -545,7 +561,7 @@ def main():
                          "GB/s_logical": round(logical / t / 1e9, 1),
                          "GB/s_unique": round(unique / t / 1e9, 1),
                          "pct_hbm_peak_unique": round(100 * unique / t / 1e9 / HBM_PEAK_GBS, 2),
-                         "tokens_per_s": round(wf.B / t, 1)})
+                         "tokens_per_s": round(wf.B / t, 1), **realised(wf, prep)})
             del prep, wf
             torch.cuda.empty_cache()
         result["more_decode"] = legs
