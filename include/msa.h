@@ -146,7 +146,11 @@ size_t msa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *
  *   q            [B, Hq, D] dtype           k_pool, v_pool  [P, 16, Hkv, D] dtype
  *   segs, seg_indptr   a plan from msa_plan_segments over the same pool
- *   max_ctx_len  >= every sequence's number of alive tokens (sizes the grid)
+ *   max_ctx_len  >= every sequence's number of alive tokens (sizes the grid;
+ *                a sequence with more alive tokens is cut to its first
+ *                ceil(ceil(max_ctx_len/16) / split_blocks) x split_blocks
+ *                alive blocks in logical order -- memory-safe, but the
+ *                result then covers only those keys)
  *   scale        softmax scale; <= 0 selects 1/sqrt(D)
  *   out          [B, Hq, D] dtype           lse_out  [B, Hq] float32, may be NULL
  * A sequence with no alive token gets out = 0 and lse = -inf.  Accumulation

@@ -227,3 +227,35 @@ def test_merge_partials_many_and_ragged():
         fin = np.isfinite(Lr)
         assert np.max(np.abs(Lg[fin] - Lr[fin])) <= 1e-5
         assert np.all(np.isneginf(Lg[~fin]))
+
+
+@pytest.mark.parametrize("cfg", [1, 2])
+def test_decode_understated_max_ctx_len_truncates_safely(cfg):
+    """max_ctx_len sizes the grid; a caller that understates it gets each
+    sequence cut to the grid's capacity (its first splits x split_blocks
+    alive blocks, in logical order) -- never an access outside the plan or
+    the pool.  The result must equal the oracle over that prefix."""
+    w = make_workload(cfg, seed=3, size="small")
+    T, max_ctx = 16, 512  # 32 blocks of 16 tokens -> two splits of 16
+    cap_blocks = -(-max_ctx // 16)
+    d = to_device(w, DEV)
+    segs, indptr, err = msa.msa_plan_segments(d["block_table"], d["alive"], d["ctx_len"],
+                                              w.block_size, w.num_phys_blocks)
+    out, lse = msa.msa_decode(d["q"], d["k_pool"], d["v_pool"], segs, indptr,
+                              max_ctx_len=max_ctx, scale=w.scale, split_blocks=T)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    kept = w.alive.copy()
+    cut_any = False
+    for b in range(w.B):
+        nb = -(-int(w.ctx_len[b]) // w.block_size)
+        idx = [l for l in range(nb) if w.alive[b, l]]
+        for l in idx[cap_blocks:]:
+            kept[b, l] = 0
+        cut_any |= len(idx) > cap_blocks
+    assert cut_any, "the workload must have a sequence longer than the grid"
+    Or, Lr = oracle.decode_ref(w.q, w.k_pool, w.v_pool, w.block_table, kept, w.ctx_len,
+                               w.block_size, w.scale)
+    tol = TOL[w.dtype]
+    assert np.max(np.abs(from_device(out) - Or)) <= tol
+    assert np.max(np.abs(lse.cpu().numpy().astype(np.float64) - Lr)) <= tol
