@@ -182,6 +182,9 @@ size_t msa_prefill_workspace_size(int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
  *
  *   q       [B, C, Hq, D] bf16     q_pos0  int32 [B] (device)
  *   out     [B, C, Hq, D] bf16     lse_out [B, C, Hq] float32, may be NULL
+ *   max_ctx_len  as for msa_decode: bounds every sequence's alive tokens
+ *                (the chunk's included) and sizes the grid; a longer
+ *                sequence is cut the same way
  *   split_blocks  0 = automatic: the alive-key stream is split only when the
  *                 (row tile, KV head, sequence) work items do not cover the
  *                 chip's 256 CUs; otherwise it is cut into near-equal splits

@@ -144,3 +144,31 @@ def test_recompute_full_sampled():
     rows = np.sort(np.concatenate([[0, 1, 63, 64, 255, 511], rng.choice(512, 8, replace=False)]))
     heads = sorted(rng.choice(w.Hq, size=4, replace=False).tolist())
     check(w, O, L, seqs=[1, 2], heads=heads, rows=np.unique(rows))
+
+
+def test_prefill_understated_max_ctx_len_truncates_safely():
+    """As for decode: an understated max_ctx_len cuts each sequence to the
+    grid's capacity (its first splits x split_blocks alive blocks in logical
+    order) without touching anything outside the plan or the pool; the rows
+    then see only those keys (here every kept key precedes every row)."""
+    w = make_workload(3, seed=5, size="small")
+    T, max_ctx = 16, 512
+    cap_blocks = -(-max_ctx // 16)
+    d = to_device(w, DEV)
+    segs, indptr, err = msa.msa_plan_segments(d["block_table"], d["alive"], d["ctx_len"],
+                                              w.block_size, w.num_phys_blocks)
+    out, lse = msa.msa_prefill_chunk(d["q"], d["q_pos0"], d["k_pool"], d["v_pool"], segs, indptr,
+                                     max_ctx_len=max_ctx, scale=w.scale, split_blocks=T)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    kept = w.alive.copy()
+    for b in range(w.B):
+        nb = -(-int(w.ctx_len[b]) // w.block_size)
+        idx = [l for l in range(nb) if w.alive[b, l]]
+        assert len(idx) > cap_blocks
+        for l in idx[cap_blocks:]:
+            kept[b, l] = 0
+    Or, Lr = oracle.prefill_ref(w.q, w.q_pos0, w.k_pool, w.v_pool, w.block_table, kept, w.ctx_len,
+                                w.block_size, w.scale)
+    assert np.max(np.abs(from_device(out) - Or)) <= TOL
+    assert np.max(np.abs(lse.cpu().numpy().astype(np.float64) - Lr)) <= TOL
