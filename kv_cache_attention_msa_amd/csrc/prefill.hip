@@ -29,6 +29,15 @@
 // num_records covers only the rows that exist, so missing blocks and padding
 // rows past ctx_len land as zeros (and are masked); tiles straddling the
 // causal diagonal are masked per element by logical position.
+//
+// Schedule: wavefronts w and w+4 share a SIMD, and one wavefront cannot
+// overlap its own exponentials with its own MFMAs, while two wavefronts
+// overlap them almost fully.  So the two halves of the workgroup alternate:
+// while wavefronts 0-3 run the matrix half of a step (QK of the next tile,
+// PV of this one), wavefronts 4-7 run the softmax half, and the other way
+// round in the next half-step; a barrier ends every half-step.  The lone
+// matrix-half wavefront of a SIMD is kept fed by reading half of its V
+// operands during its preceding softmax half.  Four K/V stages in LDS.
 #include "msa_internal.h"
 
 namespace msa {
@@ -45,19 +54,19 @@ constexpr int kBlk = 16;           // tokens per block
 constexpr int kTK = 64;            // keys per tile (4 blocks)
 constexpr int kTileBytes = kTK * kRow;  // one K or V tile in LDS (16 KB)
 constexpr int kUnit = 1024;             // one LDS DMA unit: 16 keys of a block x 64 B of d
-constexpr int kStages = 3;              // K and V tiles resident or in flight
+constexpr int kStages = 4;              // K and V tiles resident or in flight
 constexpr int kChunkBlocks = 256;  // blocks expanded into LDS at a time
 constexpr int kMaxSplitBlocks = 1 << 20;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kBufferFlags = 0x00020000;
 constexpr int kXcds = 8;  // accelerator complex dies on MI355X, one L2 each
 
-// Eight wavefronts per workgroup and one workgroup per CU: every K/V tile
-// staged in LDS feeds 8 x 32 query rows, which halves the global loads and
-// LDS stores per MFMA against two independent 4-wave workgroups.
-template <int G, int RT>
+// Eight wavefronts per workgroup (two per SIMD) and one workgroup per CU:
+// every K/V tile staged in LDS feeds 8 x 32 query rows, one 32-row tile per
+// wavefront.
+template <int G>
 struct PGeo {
-  static constexpr int WAVES = 8 / RT;          // RT 32-row tiles per wavefront
+  static constexpr int WAVES = 8;
   static constexpr int THREADS = WAVES * kWave;
   static constexpr int NPOS = 256 / G;          // query positions per workgroup
   static constexpr int UPW = 16 / WAVES;        // DMA units of a K (and a V) tile per wavefront
@@ -128,10 +137,11 @@ __device__ __forceinline__ int wg_search_segment(const msa_segment* segs, int lo
   return lo;
 }
 
-template <int G, int RT>
-__global__ void __launch_bounds__((PGeo<G, RT>::THREADS), (PGeo<G, RT>::WAVES / 4))
+template <int G>
+__global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
     prefill_kernel(PrefillParams p) {
-  using PG = PGeo<G, RT>;
+  using PG = PGeo<G>;
+  constexpr int RT = 1;  // 32-row tiles per wavefront
   constexpr int THREADS = PG::THREADS, NPOS = PG::NPOS;
 
   // K and V tiles in MFMA-operand order (see the DMA unit layout below),
@@ -262,7 +272,7 @@ __global__ void __launch_bounds__((PGeo<G, RT>::THREADS), (PGeo<G, RT>::WAVES / 
   // Wavefront w loads units UPW*w .. UPW*w+UPW-1 of both K and V, all from
   // block UPW*w/4; quarter q of a block adds 64 bytes to both global offsets.
   constexpr int UPW = PG::UPW;
-  static_assert(UPW == 2 || UPW == 4, "DMA split");
+  static_assert(UPW == 2, "DMA split: two units of each tile per wavefront");
   const int u0 = UPW * w, q0u = u0 % 4;
   const uint32_t k_voff0 = uint32_t((lane % 16) * tok_stride + (4 * q0u + lane / 16) * 16);
   const int vkey = 8 * (lane / 32) + 4 * ((lane % 32) / 16) + (lane % 8) / 2;
@@ -365,177 +375,208 @@ __global__ void __launch_bounds__((PGeo<G, RT>::THREADS), (PGeo<G, RT>::WAVES / 
 #pragma unroll
       for (int i = 0; i < UPW; ++i) dma16(r, dst + i * kUnit, v_voff0 + 64 * i);
     };
-    // the DMAs of the current step (2*UPW) may stay in flight; everything
-    // older has landed in LDS
-    auto wait_older = [] {
-      if constexpr (UPW == 2)
-        asm volatile("s_waitcnt vmcnt(4)" ::: "memory");
-      else
-        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    // the DMAs of this wavefront's last two loop iterations (2 x 2*UPW) may
+    // stay in flight; everything older has landed in LDS
+    auto wait_older = [] { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); };
+    // The matrix half of a step: S^T = K Q^T for the 2 x 32 keys of the K
+    // tile at kt (QK of the next tile) and O^T += V^T P^T for the V tile at
+    // vt0 (PV of this tile).  The first eight PV MFMAs use the V operands
+    // the softmax half already read (vpre); their 256+ cycles cover the K
+    // operand reads, which then run two MFMAs ahead, followed by the other
+    // half of the V reads.  One wavefront per SIMD issues these MFMAs while
+    // the other runs its softmax, so this half runs at raised priority.
+    auto mphase = [&](const uint8_t* kt, const uint8_t* vt0, f32x16_t* sacc, const uint4* pp,
+                      const uint2* vpre) {
+      __builtin_amdgcn_s_setprio(1);
+      uint4 ka[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kb2 = j / 8, k = j % 8;
+        ka[j] = *reinterpret_cast<const uint4*>(kt + k_lane_off + 8192 * kb2 + 1024 * (k / 2) + 512 * (k % 2));
+      }
+      uint2 va[16];
+      const uint8_t* vt = vt0 + v_lane_off;
+#pragma unroll
+      for (int j = 8; j < 16; ++j) {
+        const int t = j / 4, dt = j % 4;
+        const uint8_t* vb0 = vt + (t * 4 + dt) * kUnit;
+        va[2 * (j - 8)] = ds_read_tr16(vb0);
+        va[2 * (j - 8) + 1] = ds_read_tr16(vb0 + kUnit / 2);
+      }
+      // PV steps 0..7 on the V operands read during the softmax half
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int t = j / 4, dt = j % 4;
+        const uint4 a = make_uint4(vpre[2 * j].x, vpre[2 * j].y, vpre[2 * j + 1].x, vpre[2 * j + 1].y);
+        acc_o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pp[t]), acc_o[0][dt], 0, 0, 0);
+      }
+      const f32x16_t zero = {};
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int kb2 = j / 8, k = j % 8;
+        sacc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(ka[j]), as_bf16x8(qop[0][k]),
+                                                            k == 0 ? zero : sacc[kb2], 0, 0, 0);
+      }
+#pragma unroll
+      for (int j = 8; j < 16; ++j) {
+        const int t = j / 4, dt = j % 4;
+        const uint4 a = make_uint4(va[2 * (j - 8)].x, va[2 * (j - 8)].y, va[2 * (j - 8) + 1].x, va[2 * (j - 8) + 1].y);
+        acc_o[0][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pp[t]), acc_o[0][dt], 0, 0, 0);
+      }
+      // order: 2 K reads; then each of 30 MFMAs (PV 0..7, QK 0..15, PV 8..13)
+      // followed by one read (K 2..15, then the 16 halves of V steps 8..15);
+      // PV 14..15
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);
+#pragma unroll
+      for (int i = 0; i < 30; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
+      }
+      __builtin_amdgcn_sched_group_barrier(0x008, 2, 0);
+      __builtin_amdgcn_s_setprio(0);
     };
-    // tile ti starts at or after every row of this workgroup: it and every
-    // later tile are fully masked
-    auto past_rows = [&](int ti) { return ti >= kWave || ((past_mask >> ti) & 1); };
-    // S^T = K Q^T for the 2 x 32 keys of the K tile at kt, for each row
-    // tile (one K operand read feeds all RT of them)
-    auto scores = [&](const uint8_t* kt, f32x16_t (*acc)[2]) {
+
+    // The softmax half of a step for tile j: the V operands of PV steps
+    // 0..7 of tile j are read into vpre first (the LDS is otherwise idle for
+    // this wavefront here), then mask (padding or diagonal tiles), running
+    // max with lazy rescaling, weights rounded to bf16 into the P operand,
+    // row sums.
+    auto softmax = [&](int j, f32x16_t* sc, uint4* pp, uint2* vpre) {
+      {
+        const uint8_t* vt = &v_lds[j % kStages][0] + v_lane_off;
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; ++kb2) {
-        const f32x16_t zero = {};
-#pragma unroll
-        for (int k = 0; k < kD / 16; ++k) {
-          const uint4 a = *reinterpret_cast<const uint4*>(
-              kt + k_lane_off + 8192 * kb2 + 1024 * (k / 2) + 512 * (k % 2));
-#pragma unroll
-          for (int r = 0; r < RT; ++r)
-            acc[r][kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                as_bf16x8(a), as_bf16x8(qop[r][k]), k == 0 ? zero : acc[r][kb2], 0, 0, 0);
+        for (int i = 0; i < 8; ++i) {
+          const int t = i / 4, dt = i % 4;
+          const uint8_t* vb0 = vt + (t * 4 + dt) * kUnit;
+          vpre[2 * i] = ds_read_tr16(vb0);
+          vpre[2 * i + 1] = ds_read_tr16(vb0 + kUnit / 2);
         }
       }
-    };
-
-    // Pipeline: K runs one tile ahead of V, and the DMAs two tiles ahead of
-    // their use.  At the top of step ti the LDS holds K(ti+1) and V(ti), the
-    // registers hold S(ti), K(ti+2) and V(ti+1) are landing, and the DMAs of
-    // K(ti+3) and V(ti+2) go out into the stages read in step ti-1.  The QK
-    // MFMAs of tile ti+1 are issued next to the softmax of tile ti
-    // (independent work the MFMA and VALU pipes execute together), then PV
-    // of tile ti.
-    if (past_rows(0)) {
-      done = true;
-      continue;
-    }
-    issue_k(0);
-    issue_v(0);
-    issue_k(1);
-    issue_k(2);
-    issue_v(1);
-    wait_older();
-    __syncthreads();
-    f32x16_t s_a[RT][2], s_b[RT][2];
-    scores(&k_lds[0][0], s_a);
-    // every wavefront has read K(0) before the first step's DMA rewrites
-    // its stage
-    __syncthreads();
-    // One pipeline step for tile ti: scores of ti are in sc, those of ti+1
-    // go to sn.  Returns true when this chunk is finished.
-    auto step = [&](int ti, f32x16_t (*sc)[2], f32x16_t (*sn)[2]) -> bool {
-      const bool more = !past_rows(ti + 1);
-      issue_k(ti + 3);
-      issue_v(ti + 2);
-
-      // ---- mask + online softmax of tile ti (lane = query row) -----------
-      if ((mask_mask >> ti) & 1) {  // tile touches padding or the diagonal
+      if ((mask_mask >> j) & 1) {
         int lp[4], rw[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-          const int jj = ti * 4 + k;
+          const int jj = j * 4 + k;
           lp[k] = jj < nblk ? blk_lpos[jj] : 0x07ffffff;
           rw[k] = jj < nblk ? blk_rows[jj] : 0;
         }
 #pragma unroll
-        for (int r = 0; r < RT; ++r)
+        for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-          for (int kb2 = 0; kb2 < 2; ++kb2)
-#pragma unroll
-            for (int i = 0; i < 16; ++i) {
-              const int key = kb2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
-              const int kblk = key / kBlk, slot = key % kBlk;
-              const int kpos = lp[kblk] * kBlk + slot;
-              const bool vis = slot < rw[kblk] && kpos <= my_qpos[r];
-              sc[r][kb2][i] = vis ? sc[r][kb2][i] : -INFINITY;
-            }
+          for (int i = 0; i < 16; ++i) {
+            const int key = kb2 * 32 + 8 * (i / 4) + 4 * half + (i % 4);
+            const int kblk = key / kBlk, slot = key % kBlk;
+            const int kpos = lp[kblk] * kBlk + slot;
+            const bool vis = slot < rw[kblk] && kpos <= my_qpos[0];
+            sc[kb2][i] = vis ? sc[kb2][i] : -INFINITY;
+          }
       }
       const float c = p.scale_log2;
-      float nm[RT], alpha[RT];
-#pragma unroll
-      for (int r = 0; r < RT; ++r) {
       float mx = -INFINITY;
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[r][kb2][i]);
+        for (int i = 0; i < 16; ++i) mx = fmaxf(mx, sc[kb2][i]);
       mx = max_halves(mx);
       // Lazy rescaling: a row keeps its reference max m_run until the true
       // max exceeds it by more than 2^8 in the exponent; the weights are then
       // at most 256 (harmless for fp32 sums and for bf16's relative
       // precision) and the accumulator rescale is skipped in almost every
       // tile.  The LSE stays exact: it is m_run*scale + log2(sum).
-      const bool bump = (mx - m_run[r]) * c > 8.f;  // true on the first visible key
-      const float m_use = bump ? mx : m_run[r];
-      nm[r] = m_use == -INFINITY ? 0.f : -m_use * c;
-      alpha[r] = (m_use == m_run[r]) ? 1.f : __builtin_amdgcn_exp2f((m_run[r] - m_use) * c);
+      const bool bump = (mx - m_run[0]) * c > 8.f;  // true on the first visible key
+      const float m_use = bump ? mx : m_run[0];
+      const float nm = m_use == -INFINITY ? 0.f : -m_use * c;
+      const float alpha = (m_use == m_run[0]) ? 1.f : __builtin_amdgcn_exp2f((m_run[0] - m_use) * c);
       if (__builtin_amdgcn_ballot_w64(bump) != 0) {
 #pragma unroll
         for (int dt = 0; dt < kD / 32; ++dt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) acc_o[r][dt][i] *= alpha[r];
+          for (int i = 0; i < 16; ++i) acc_o[0][dt][i] *= alpha;
       }
-      m_run[r] = m_use;
-      }
-      // QK of tile ti+1, unconditionally and in the same basic block as the
-      // exponentials and PV of tile ti so that MFMA and VALU work interleave
-      // (past the last tile the stage holds zero rows and the result goes
-      // unused)
-      scores(&k_lds[(ti + 1) % kStages][0], sn);
-      // ---- P and O^T += V^T P^T for tile ti, one key step of 16 at a time --
-      // (each P operand is built right before its four MFMAs, so only one is
-      // live)
+      m_run[0] = m_use;
       // four partial sums per row keep the additions out of one long chain
-      float lsum[RT][4];
-#pragma unroll
-      for (int r = 0; r < RT; ++r)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) lsum[r][e] = 0.f;
-      const uint8_t* vt = &v_lds[ti % kStages][0] + v_lane_off;
+      float lsum[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        uint4 pop[RT];
+        float pv[8];
 #pragma unroll
-        for (int r = 0; r < RT; ++r) {
-          float pv[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[r][t / 2][8 * (t % 2) + e], c, nm[r]));
-            lsum[r][e % 4] += pv[e];
-          }
-          pop[r] = make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
-                              cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7]));
+        for (int e = 0; e < 8; ++e) {
+          pv[e] = __builtin_amdgcn_exp2f(fmaf(sc[t / 2][8 * (t % 2) + e], c, nm));
+          lsum[e % 4] += pv[e];
         }
+        pp[t] = make_uint4(cvt_pk_bf16(pv[0], pv[1]), cvt_pk_bf16(pv[2], pv[3]),
+                           cvt_pk_bf16(pv[4], pv[5]), cvt_pk_bf16(pv[6], pv[7]));
+      }
+      l_lane[0] = l_lane[0] * alpha + ((lsum[0] + lsum[1]) + (lsum[2] + lsum[3]));
+    };
+
+    // Ping-pong schedule.  Wavefronts w and w+4 share a SIMD; group A
+    // (w < 4) and group B (w >= 4) alternate between the matrix half of a
+    // step (QK of tile k+1 and PV of tile k, MFMA only) and the softmax half
+    // (VALU only), so that each SIMD's matrix core runs one wavefront's
+    // MFMAs while its VALU runs the other's exponentials.  A barrier ends
+    // every half-step; B runs the same loop as A one half-step later:
+    //   half-step 2k:   A: QK(k+1) + PV(k)    B: softmax(k)
+    //   half-step 2k+1: A: softmax(k+1)       B: QK(k+1) + PV(k)
+    // K(k+1) and V(k) are read in half-steps 2k and 2k+1.  Iteration k
+    // sends the DMAs of K(k+4) and V(k+3) into the stages of K(k) and V(k-1),
+    // last read in half-step 2k-1; before each barrier a wavefront waits for
+    // all but its last two iterations' DMAs, so K(k+1) and V(k) have landed
+    // before half-step 2k for both groups, and V(k+1) (iteration k-2) before
+    // the softmax half of tile k+1 reads half of its operands in advance.
+    // Tiles past the workgroup's last row are never processed.
+    const int n_eff = past_mask == 0 ? kWave : min(ntiles, int(__builtin_ctzll(past_mask)));
+    if (n_eff == 0) {
+      done = true;
+      continue;
+    }
+    done = n_eff < ntiles;
+    const bool grp_b = w >= 4;
+    issue_k(0);
+    issue_v(0);
+    issue_k(1);
+    issue_k(2);
+    issue_v(1);
+    issue_k(3);
+    issue_v(2);
+    wait_older();  // K(0), V(0), K(1) have landed
+    __syncthreads();
+    f32x16_t sc[2];
+    uint4 pp[4];
+    uint2 vpre[16];
+    {
+      const f32x16_t zero = {};
 #pragma unroll
-        for (int dt = 0; dt < kD / 32; ++dt) {
-          // A operand (V^T, 32 d x 16 keys): two transpose loads of 4 keys x
-          // 16 d per 16-lane group; k-slots 0..3 <- keys 16t+4h+0..3, 4..7 <-
-          // keys 16t+8+4h+0..3 (the same key order as the P operand)
-          const uint8_t* vb0 = vt + (t * 4 + dt) * kUnit;
-          const uint2 lo2 = ds_read_tr16(vb0);
-          const uint2 hi2 = ds_read_tr16(vb0 + kUnit / 2);
-          const uint4 a = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
+      for (int kb2 = 0; kb2 < 2; ++kb2)
 #pragma unroll
-          for (int r = 0; r < RT; ++r)
-            acc_o[r][dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(pop[r]),
-                                                                   acc_o[r][dt], 0, 0, 0);
+        for (int k = 0; k < kD / 16; ++k) {
+          const uint4 a = *reinterpret_cast<const uint4*>(
+              &k_lds[0][0] + k_lane_off + 8192 * kb2 + 1024 * (k / 2) + 512 * (k % 2));
+          sc[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(qop[0][k]),
+                                                            k == 0 ? zero : sc[kb2], 0, 0, 0);
         }
-      }
-#pragma unroll
-      for (int r = 0; r < RT; ++r)
-        l_lane[r] = l_lane[r] * alpha[r] + ((lsum[r][0] + lsum[r][1]) + (lsum[r][2] + lsum[r][3]));
-      if (!more) {
-        // either the chunk is exhausted (go on with the next one) or the next
-        // tile starts after every row (stop: later keys are later still)
-        done = ti + 1 < ntiles;
-        return true;
-      }
-      // K(ti+2) and V(ti+1) have landed once every wavefront passed here
+    }
+    // A: softmax(0), barrier.  B: barrier, softmax(0), barrier.  Every
+    // wavefront has read K(0) before the first DMA rewrites its stage.
+    if (grp_b) __syncthreads();
+    softmax(0, sc, pp, vpre);
+    __builtin_amdgcn_sched_barrier(0);
+    __syncthreads();
+    for (int k = 0; k < n_eff; ++k) {
+      issue_k(k + 4);
+      issue_v(k + 3);
+      mphase(&k_lds[(k + 1) % kStages][0], &v_lds[k % kStages][0], sc, pp, vpre);
+      // keep the matrix half's MFMAs on this side of the barrier
+      __builtin_amdgcn_sched_barrier(0);
       wait_older();
       __syncthreads();
-      return false;
-    };
-    // unrolled by two so the score registers swap roles without copies
-    for (int ti = 0;; ti += 2) {
-      if (step(ti, s_a, s_b)) break;
-      if (step(ti + 1, s_b, s_a)) break;
+      if (k + 1 < n_eff) softmax(k + 1, sc, pp, vpre);
+      __builtin_amdgcn_sched_barrier(0);
+      wait_older();
+      __syncthreads();
     }
+    // A ends one half-step earlier: its last barrier pairs with B's last
+    if (!grp_b) __syncthreads();
     // no DMA may still write into a stage (the next chunk's staging shares
     // one) once the workgroup leaves this chunk
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
@@ -584,17 +625,11 @@ __global__ void __launch_bounds__((PGeo<G, RT>::THREADS), (PGeo<G, RT>::WAVES / 
   }
 }
 
-// row tiles per wavefront: 1 (eight wavefronts, two per SIMD) or 2 (four
-// wavefronts, one per SIMD, each K/V operand read feeding two MFMAs).  On
-// the 4 x 512-row chunk over 8k cached tokens: 294 us with 1, 370 us with 2
-// (one wavefront per SIMD leaves the MFMA pipe idle during its own waits).
-constexpr int kRowTiles = 1;
-
 template <int G>
 hipError_t launch_g(const PrefillParams& p, hipStream_t stream) {
-  using PG = PGeo<G, kRowTiles>;
+  using PG = PGeo<G>;
   dim3 grid((p.C + PG::NPOS - 1) / PG::NPOS, p.Hkv, p.B * p.S);
-  hipLaunchKernelGGL((prefill_kernel<G, kRowTiles>), grid, dim3(PG::THREADS), 0, stream, p);
+  hipLaunchKernelGGL((prefill_kernel<G>), grid, dim3(PG::THREADS), 0, stream, p);
   return hipGetLastError();
 }
 
