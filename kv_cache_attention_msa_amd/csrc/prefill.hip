@@ -145,7 +145,8 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
   constexpr int THREADS = PG::THREADS, NPOS = PG::NPOS;
 
   // K and V tiles in MFMA-operand order (see the DMA unit layout below),
-  // three stages each: one being read, one landed or landing, one in flight
+  // four stages each: K(k+1) and V(k) being read by the two halves of the
+  // workgroup, the later tiles landing or in flight
   __shared__ __align__(16) uint8_t k_lds[kStages][kTileBytes];
   __shared__ __align__(16) uint8_t v_lds[kStages][kTileBytes];
   __shared__ int32_t blk_rows[kChunkBlocks];  // rows present (0 = block missing)
