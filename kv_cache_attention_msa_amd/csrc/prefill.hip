@@ -379,6 +379,8 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
     // the DMAs of this wavefront's last two loop iterations (2 x 2*UPW) may
     // stay in flight; everything older has landed in LDS
     auto wait_older = [] { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); };
+    // only the DMAs of this wavefront's last loop iteration may stay in flight
+    auto wait_last = [] { asm volatile("s_waitcnt vmcnt(4)" ::: "memory"); };
     // The matrix half of a step: S^T = K Q^T for the 2 x 32 keys of the K
     // tile at kt (QK of the next tile) and O^T += V^T P^T for the V tile at
     // vt0 (PV of this tile).  The first eight PV MFMAs use the V operands
@@ -519,13 +521,18 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
     // every half-step; B runs the same loop as A one half-step later:
     //   half-step 2k:   A: QK(k+1) + PV(k)    B: softmax(k)
     //   half-step 2k+1: A: softmax(k+1)       B: QK(k+1) + PV(k)
-    // K(k+1) and V(k) are read in half-steps 2k and 2k+1.  Iteration k
-    // sends the DMAs of K(k+4) and V(k+3) into the stages of K(k) and V(k-1),
-    // last read in half-step 2k-1; before each barrier a wavefront waits for
-    // all but its last two iterations' DMAs, so K(k+1) and V(k) have landed
-    // before half-step 2k for both groups, and V(k+1) (iteration k-2) before
-    // the softmax half of tile k+1 reads half of its operands in advance.
-    // Tiles past the workgroup's last row are never processed.
+    // K(k+1) and V(k) are read in half-steps 2k and 2k+1, and half of V(k+1)
+    // in advance by A's softmax half in 2k+1.  Iteration k sends the DMAs of
+    // K(k+4) and V(k+3) into the stages of K(k) and V(k-1), last read in
+    // half-step 2k-1 (A issues them at the start of 2k, B of 2k+1).  Every
+    // tile needs all eight wavefronts' DMA units, so the waits are set by
+    // the other group's barriers: before the barrier that ends its matrix
+    // half a wavefront waits for all but its last two iterations' DMAs,
+    // before the one that ends its softmax half for all but its last one.
+    // Then K(k+1) and V(k) (iteration k-3) have landed for every wavefront
+    // before half-step 2k, and V(k+1) (iteration k-2) before 2k+1: B passes
+    // that barrier at the end of its iteration k-1, A in the middle of its
+    // iteration k.  Tiles past the workgroup's last row are never processed.
     const int n_eff = past_mask == 0 ? kWave : min(ntiles, int(__builtin_ctzll(past_mask)));
     if (n_eff == 0) {
       done = true;
@@ -562,6 +569,7 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
     if (grp_b) __syncthreads();
     softmax(0, sc, pp, vpre);
     __builtin_amdgcn_sched_barrier(0);
+    wait_last();  // B: the prologue's V(1), which A reads in half-step 1
     __syncthreads();
     for (int k = 0; k < n_eff; ++k) {
       issue_k(k + 4);
@@ -573,7 +581,7 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
       __syncthreads();
       if (k + 1 < n_eff) softmax(k + 1, sc, pp, vpre);
       __builtin_amdgcn_sched_barrier(0);
-      wait_older();
+      wait_last();
       __syncthreads();
     }
     // A ends one half-step earlier: its last barrier pairs with B's last
