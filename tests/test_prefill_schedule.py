@@ -62,10 +62,6 @@ class Group:
     def wait(self, outstanding):
         self.landed = max(self.landed, len(self.issued) - outstanding)
 
-    def has(self, kind, tile):
-        want = [i for i, d in enumerate(self.issued) if d == (kind, tile)]
-        return len(want) == self.upw and max(want) < self.landed
-
 
 def replay(c, n, w_end=None):
     """Replay the kernel's timeline for n tiles; return a list of violations."""
