@@ -126,6 +126,18 @@ def test_prefill_full_sampled():
     check(w, O, L, seqs=[0, 3], heads=heads, rows=rows)
 
 
+def test_prefill_full_forced_split_sampled():
+    """Full-size chunk with the key stream cut into splits of 128 blocks
+    (five per sequence, 1280 workgroups in five waves over the CUs): the
+    ping-pong kernel writes partials and the merge stitches them."""
+    w = make_workload(3, seed=1)
+    O, L = run_prefill(w, split_blocks=128)
+    rng = np.random.default_rng(5)
+    rows = np.sort(np.concatenate([[0, 63, 64, 300, 511], rng.choice(512, 7, replace=False)]))
+    heads = sorted(rng.choice(w.Hq, size=4, replace=False).tolist())
+    check(w, O, L, seqs=[1, 2], heads=heads, rows=rows)
+
+
 def test_recompute_small():
     """Recompute of an evicted middle range: chunk rows at q_pos0 in the middle
     of the context, alive blocks after the chunk hidden by the causal mask."""
