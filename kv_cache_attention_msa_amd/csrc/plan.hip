@@ -44,16 +44,32 @@ __device__ __forceinline__ SeqView seq_view(const PlanParams& p, int b, int& fla
   return v;
 }
 
-// alive-and-valid predicate; phys is meaningful only when it returns true
-__device__ __forceinline__ bool live(const PlanParams& p, const SeqView& v, int l, int32_t& phys,
-                                     int& flags) {
-  if (l < 0 || l >= v.nb || v.arow[l] == 0) return false;
-  const int32_t ph = v.trow[l];
-  if (ph < 0 || ph >= p.P) {
+// a block's alive flag and table entry, read together whatever their
+// values (the row pointers do not depend on ctx_len, so these loads need not
+// wait for it); blocks outside the row read as dead
+struct Raw {
+  uint8_t a;
+  int32_t ph;
+};
+__device__ __forceinline__ Raw load_raw(const PlanParams& p, const SeqView& v, int l) {
+  Raw r = {0, -1};
+  if (l >= 0 && l < p.max_blocks) {
+    r.a = v.arow[l];
+    r.ph = v.trow[l];
+  }
+  return r;
+}
+
+// alive-and-valid predicate on block l's raw values; phys is meaningful only
+// when it returns true
+__device__ __forceinline__ bool live(const PlanParams& p, const SeqView& v, int l, Raw r,
+                                     int32_t& phys, int& flags) {
+  if (l < 0 || l >= v.nb || r.a == 0) return false;
+  if (r.ph < 0 || r.ph >= p.P) {
     flags |= MSA_DEVERR_PHYS_RANGE;
     return false;
   }
-  phys = ph;
+  phys = r.ph;
   return true;
 }
 
@@ -86,11 +102,15 @@ __global__ void __launch_bounds__(kPlanThreads) plan_count_kernel(PlanParams p) 
   int flags = 0;
   const SeqView v = seq_view(p, b, flags);
   int starts = 0;
-  for (int l = threadIdx.x; l < v.nb; l += kPlanThreads) {
+  // the raw loads come before the test against nb, so the first ones go out
+  // together with the ctx_len load
+  for (int l = threadIdx.x; l < p.max_blocks; l += kPlanThreads) {
+    const Raw r = load_raw(p, v, l), rp = load_raw(p, v, l - 1);
+    if (l >= v.nb) break;
     int32_t ph = 0, pp = 0;
-    if (live(p, v, l, ph, flags)) {
+    if (live(p, v, l, r, ph, flags)) {
       int dummy = 0;  // the previous block's flags are counted by its own thread
-      const bool cont = live(p, v, l - 1, pp, dummy) && pp + 1 == ph;
+      const bool cont = live(p, v, l - 1, rp, pp, dummy) && pp + 1 == ph;
       starts += cont ? 0 : 1;
     }
   }
@@ -150,6 +170,15 @@ __global__ void __launch_bounds__(kPlanThreads) plan_write_kernel(PlanParams p) 
   __shared__ Scan3 scan_lds[kPlanThreads / kWave];
   const int b = blockIdx.x;
 
+  // this thread's first blocks (and their neighbours): loaded before the
+  // offset reduction below, so the two memory round trips overlap
+  int dummy = 0;  // flags were gathered by the count pass
+  const SeqView v = seq_view(p, b, dummy);
+  Raw r0[kPerThread + 2];
+#pragma unroll
+  for (int k = 0; k < kPerThread + 2; ++k)
+    r0[k] = load_raw(p, v, threadIdx.x * kPerThread - 1 + k);
+
   // offset of this sequence's records; workgroup 0 also publishes the totals
   int before = 0, all = 0, fl = 0;
   for (int i = threadIdx.x; i < p.B; i += kPlanThreads) {
@@ -170,23 +199,24 @@ __global__ void __launch_bounds__(kPlanThreads) plan_write_kernel(PlanParams p) 
     }
   }
 
-  int dummy = 0;  // flags were gathered by the count pass
-  const SeqView v = seq_view(p, b, dummy);
   Scan3 carry = {0, 0, -1};
   for (int base = 0; base < v.nb; base += kChunk) {
     const int l0 = base + threadIdx.x * kPerThread;
+    Raw r[kPerThread + 2];  // blocks l0-1 .. l0+kPerThread
+#pragma unroll
+    for (int k = 0; k < kPerThread + 2; ++k) r[k] = base == 0 ? r0[k] : load_raw(p, v, l0 - 1 + k);
     bool a[kPerThread];
     int32_t ph[kPerThread];
     int tok[kPerThread];
     bool st[kPerThread];
     int32_t prev_ph = 0;
-    bool prev_a = live(p, v, l0 - 1, prev_ph, dummy);
+    bool prev_a = live(p, v, l0 - 1, r[0], prev_ph, dummy);
     Scan3 mine = {0, 0, -1};
 #pragma unroll
     for (int k = 0; k < kPerThread; ++k) {
       const int l = l0 + k;
       ph[k] = 0;
-      a[k] = live(p, v, l, ph[k], dummy);
+      a[k] = live(p, v, l, r[k + 1], ph[k], dummy);
       st[k] = a[k] && !(prev_a && prev_ph + 1 == ph[k]);
       tok[k] = a[k] ? min(p.bs, v.n_tok - l * p.bs) : 0;
       mine.a += st[k] ? 1 : 0;
@@ -196,7 +226,7 @@ __global__ void __launch_bounds__(kPlanThreads) plan_write_kernel(PlanParams p) 
       prev_ph = ph[k];
     }
     int32_t next_ph = 0;
-    const bool next_a = live(p, v, l0 + kPerThread, next_ph, dummy);
+    const bool next_a = live(p, v, l0 + kPerThread, r[kPerThread + 1], next_ph, dummy);
 
     Scan3 total;
     const Scan3 ex = block_exclusive_scan3(mine, scan_lds, total);
