@@ -80,6 +80,34 @@ def _expect(t, dtype, name, ndim=None):
         raise ValueError(f"{name} must have {ndim} dims, got shape {tuple(t.shape)}")
 
 
+def _expect_shape(t, shape, dtype, name):
+    """A caller-supplied buffer must be exactly what the kernels will write:
+    the library trusts the sizes it is given, so a short buffer would be
+    written past its end on the device."""
+    if t is None:
+        return
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(t.shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {t.dtype}")
+
+
+def _same_device(dev, **tensors):
+    for name, t in tensors.items():
+        if t is not None and t.device != dev:
+            raise ValueError(f"{name} is on {t.device}, expected {dev}")
+
+
+def _segs_table(segs):
+    _expect(segs, torch.int32, "segs", 2)
+    if segs.shape[1] != 6:
+        raise ValueError(f"segs must be [N, 6] int32 records, got shape {tuple(segs.shape)}")
+
+
+def _nbytes(t):
+    return 0 if t is None else t.numel() * t.element_size()
+
+
 # ---------------------------------------------------------------------------
 # a1: plan
 # ---------------------------------------------------------------------------
@@ -103,7 +131,17 @@ def msa_plan_segments(block_table: torch.Tensor, alive: torch.Tensor, ctx_len: t
     if tuple(alive.shape) != (B, max_blocks) or ctx_len.shape[0] != B:
         raise ValueError("block_table, alive and ctx_len disagree on shape")
     dev = block_table.device
+    if segs is not None:
+        _segs_table(segs)
+        if seg_capacity is None:
+            seg_capacity = segs.shape[0]
+        elif int(seg_capacity) > segs.shape[0]:
+            raise ValueError(f"seg_capacity {seg_capacity} exceeds the {segs.shape[0]} rows of segs")
     cap = B * max_blocks if seg_capacity is None else int(seg_capacity)
+    _expect_shape(seg_indptr, (B + 1,), torch.int32, "seg_indptr")
+    _expect_shape(dev_error, (1,), torch.int32, "dev_error")
+    _same_device(dev, alive=alive, ctx_len=ctx_len, segs=segs, seg_indptr=seg_indptr,
+                 dev_error=dev_error, workspace=workspace)
     if segs is None:
         segs = torch.empty((max(cap, 1), 6), dtype=torch.int32, device=dev)
     if seg_indptr is None:
@@ -117,7 +155,7 @@ def msa_plan_segments(block_table: torch.Tensor, alive: torch.Tensor, ctx_len: t
                                _dev_ptr(ctx_len, "ctx_len"), B, max_blocks, block_size,
                                num_phys_blocks, _dev_ptr(segs, "segs"), cap,
                                _dev_ptr(seg_indptr, "seg_indptr"), _dev_ptr(dev_error, "dev_error"),
-                               _dev_ptr(workspace, "workspace"), workspace.numel(),
+                               _dev_ptr(workspace, "workspace"), _nbytes(workspace),
                                _stream(stream, dev))
     _lib.check(st, "msa_plan_segments")
     return segs, seg_indptr, dev_error
@@ -144,13 +182,17 @@ def msa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs
         raise ValueError("q must be [B,Hq,D]; k_pool/v_pool [P,bs,Hkv,D] of equal shape")
     if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
         raise ValueError("q, k_pool and v_pool must share a dtype")
-    _expect(segs, torch.int32, "segs", 2)
+    _segs_table(segs)
     _expect(seg_indptr, torch.int32, "seg_indptr", 1)
     B, Hq, D = q.shape
     P, bs, Hkv, Dk = k_pool.shape
     if Dk != D or seg_indptr.shape[0] != B + 1:
         raise ValueError("shape mismatch between q, pools and seg_indptr")
     dev = q.device
+    _expect_shape(out, (B, Hq, D), q.dtype, "out")
+    _expect_shape(lse, (B, Hq), torch.float32, "lse")
+    _same_device(dev, k_pool=k_pool, v_pool=v_pool, segs=segs, seg_indptr=seg_indptr, out=out,
+                 lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -162,8 +204,7 @@ def msa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs
                         P, bs, _dev_ptr(segs, "segs"), _dev_ptr(seg_indptr, "seg_indptr"),
                         B, Hq, Hkv, D, int(max_ctx_len), _dtype_enum(q), float(scale),
                         int(split_blocks), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
-                        _dev_ptr(workspace, "workspace"),
-                        0 if workspace is None else workspace.numel() * workspace.element_size(),
+                        _dev_ptr(workspace, "workspace"), _nbytes(workspace),
                         _stream(stream, dev))
     _lib.check(st, "msa_decode")
     return out, lse
@@ -191,13 +232,17 @@ def msa_prefill_chunk(q: torch.Tensor, q_pos0: torch.Tensor, k_pool: torch.Tenso
     if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
         raise ValueError("q, k_pool and v_pool must share a dtype")
     _expect(q_pos0, torch.int32, "q_pos0", 1)
-    _expect(segs, torch.int32, "segs", 2)
+    _segs_table(segs)
     _expect(seg_indptr, torch.int32, "seg_indptr", 1)
     B, C, Hq, D = q.shape
     P, bs, Hkv, Dk = k_pool.shape
     if Dk != D or seg_indptr.shape[0] != B + 1 or q_pos0.shape[0] != B:
         raise ValueError("shape mismatch between q, pools, q_pos0 and seg_indptr")
     dev = q.device
+    _expect_shape(out, (B, C, Hq, D), q.dtype, "out")
+    _expect_shape(lse, (B, C, Hq), torch.float32, "lse")
+    _same_device(dev, q_pos0=q_pos0, k_pool=k_pool, v_pool=v_pool, segs=segs,
+                 seg_indptr=seg_indptr, out=out, lse=lse, workspace=workspace)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -210,8 +255,7 @@ def msa_prefill_chunk(q: torch.Tensor, q_pos0: torch.Tensor, k_pool: torch.Tenso
                                _dev_ptr(segs, "segs"), _dev_ptr(seg_indptr, "seg_indptr"),
                                B, Hq, Hkv, D, int(max_ctx_len), _dtype_enum(q), float(scale),
                                int(split_blocks), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
-                               _dev_ptr(workspace, "workspace"),
-                               0 if workspace is None else workspace.numel() * workspace.element_size(),
+                               _dev_ptr(workspace, "workspace"), _nbytes(workspace),
                                _stream(stream, dev))
     _lib.check(st, "msa_prefill_chunk")
     return out, lse
@@ -236,6 +280,11 @@ def msa_merge_partials(o_part: torch.Tensor, m_part: torch.Tensor, l_part: torch
         raise ValueError("m_part/l_part must be [N, R, H]")
     B = part_indptr.shape[0] - 1
     dev = o_part.device
+    if out is not None:
+        out_dtype = out.dtype
+    _expect_shape(out, (B, R, H, D), out_dtype, "out")
+    _expect_shape(lse, (B, R, H), torch.float32, "lse")
+    _same_device(dev, m_part=m_part, l_part=l_part, part_indptr=part_indptr, out=out, lse=lse)
     if out is None:
         out = torch.empty((B, R, H, D), dtype=out_dtype, device=dev)
     if lse is None and want_lse:
@@ -264,18 +313,22 @@ def msa_gather_alive(k_pool: torch.Tensor, v_pool: torch.Tensor, segs: torch.Ten
     lib = _lib_handle()
     if k_pool.dim() != 4 or v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
         raise ValueError("k_pool/v_pool must be [P,bs,Hkv,D] of equal shape and dtype")
-    _expect(segs, torch.int32, "segs", 2)
+    _segs_table(segs)
     _expect(seg_indptr, torch.int32, "seg_indptr", 1)
     P, bs, Hkv, D = k_pool.shape
     B = seg_indptr.shape[0] - 1
     dev = k_pool.device
     shape = (B * int(blocks_per_seq), bs, Hkv, D)
+    _expect_shape(dense_k, shape, k_pool.dtype, "dense_k")
+    _expect_shape(dense_v, shape, k_pool.dtype, "dense_v")
+    _expect_shape(dense_segs, (B, 6), torch.int32, "dense_segs")
+    _expect_shape(dense_indptr, (B + 1,), torch.int32, "dense_indptr")
+    _same_device(dev, v_pool=v_pool, segs=segs, seg_indptr=seg_indptr, dense_k=dense_k,
+                 dense_v=dense_v, dense_segs=dense_segs, dense_indptr=dense_indptr)
     if dense_k is None:
         dense_k = torch.empty(shape, dtype=k_pool.dtype, device=dev)
     if dense_v is None:
         dense_v = torch.empty(shape, dtype=k_pool.dtype, device=dev)
-    if tuple(dense_k.shape) != shape or tuple(dense_v.shape) != shape:
-        raise ValueError(f"dense pools must be {shape}")
     if dense_segs is None:
         dense_segs = torch.empty((B, 6), dtype=torch.int32, device=dev)
     if dense_indptr is None:
