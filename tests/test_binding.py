@@ -5,10 +5,16 @@ output, plan or workspace buffer that is smaller than what the kernels will
 write, a buffer on another device, and host tensors (there is no CPU path).
 Every case here fails in the binding before any pointer reaches libmsa.
 """
+import os
+
 import pytest
 import torch
 
 import kv_cache_attention_msa_amd as msa
+from kv_cache_attention_msa_amd import _lib
+
+pytestmark = pytest.mark.skipif(not os.path.exists(_lib.LIB_PATH),
+                                reason="libmsa.so not built")
 
 
 def i32(*shape):
