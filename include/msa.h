@@ -193,10 +193,8 @@ size_t msa_prefill_workspace_size(int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
  * A row that sees no key gets out = 0 and lse = -inf.
  * Errors (returned before any launch): MSA_ERR_INVALID_ARG for null
  * pointers, C <= 0 or bad shapes; MSA_ERR_UNSUPPORTED for shapes not built
- * (msa_attention_supported), for pools of more than 2^27 blocks (the kernel
- * packs a block id and row count into one word per key tile) and when
- * B x splits > 65535 or, with more than one split, C > 65535 (launch-grid
- * limits); MSA_ERR_CAPACITY when a split
+ * (msa_attention_supported) and when B x splits > 65535 or, with more than
+ * one split, C > 65535 (launch-grid limits); MSA_ERR_CAPACITY when a split
  * is needed and the workspace is missing or smaller than
  * msa_prefill_workspace_size. */
 int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const void* k_pool,

@@ -189,7 +189,6 @@ int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const voi
   if (st != MSA_OK) return st;
   if (!q_pos0 || C <= 0) return MSA_ERR_INVALID_ARG;
   if (!prefill_supported(dtype, D, Hq / Hkv)) return MSA_ERR_UNSUPPORTED;
-  if (num_phys_blocks > prefill_max_pool_blocks()) return MSA_ERR_UNSUPPORTED;
   if (split_blocks > prefill_max_split_blocks()) return MSA_ERR_INVALID_ARG;
   const SplitPlan sp = prefill_split(B, C, Hq, Hkv, max_ctx_len, block_size, split_blocks);
   // grid z is (sequence, split); the split merge's grid y is the chunk row

@@ -149,8 +149,6 @@ SplitPlan prefill_split(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t m
 bool decode_supported(msa_dtype dtype, int32_t D, int32_t G);
 int32_t decode_max_split_blocks();
 int32_t prefill_max_split_blocks();
-// largest pool (in blocks) the chunked-prefill kernel addresses
-int32_t prefill_max_pool_blocks();
 bool prefill_supported(msa_dtype dtype, int32_t D, int32_t G);
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);

@@ -55,8 +55,7 @@ constexpr int kTK = 64;            // keys per tile (4 blocks)
 constexpr int kTileBytes = kTK * kRow;  // one K or V tile in LDS (16 KB)
 constexpr int kUnit = 1024;             // one LDS DMA unit: 16 keys of a block x 64 B of d
 constexpr int kStages = 4;              // K and V tiles resident or in flight
-constexpr int kChunkBlocks = 512;  // blocks expanded into LDS at a time (two tiles per lane)
-constexpr int kPhysLimit = 1 << 27;  // pool blocks addressable by the packed per-tile word
+constexpr int kChunkBlocks = 256;  // blocks expanded into LDS at a time
 constexpr int kMaxSplitBlocks = 1 << 20;
 constexpr float kLn2 = 0.69314718055994530942f;
 constexpr int kBufferFlags = 0x00020000;
@@ -152,7 +151,7 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
   __shared__ __align__(16) uint8_t v_lds[kStages][kTileBytes];
   __shared__ int32_t blk_rows[kChunkBlocks];  // rows present (0 = block missing)
   __shared__ int32_t blk_lpos[kChunkBlocks];  // logical block id
-  __shared__ int32_t blk_phys[kChunkBlocks];  // physical block id (0 if missing)
+  __shared__ uint2 blk_off[kChunkBlocks];     // byte offset of the block in a pool (64-bit)
   // segment staging for the chunk expansion; it only lives between chunks,
   // when no K tile is in LDS and no DMA is in flight, so it shares the
   // second K buffer
@@ -311,7 +310,8 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
       }
       const int off = j - st_start[lo];
       const bool ok = st_phys[lo] >= 0 && off >= 0 && off < st_nblk[lo];
-      blk_phys[jj] = ok ? st_phys[lo] + off : 0;
+      const uint64_t bo = ok ? uint64_t(st_phys[lo] + off) * blk_stride : 0;
+      blk_off[jj] = make_uint2(uint32_t(bo), uint32_t(bo >> 32));
       blk_lpos[jj] = st_lblk[lo] + off;
       blk_rows[jj] = !ok ? 0 : (j == nAB - 1 ? last_tokens : kBlk);
     }
@@ -321,22 +321,23 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
     // Each wavefront loads whole units of one block of every tile, so its
     // buffer descriptor is wave-uniform by construction.
     const int my_blk = u0 / 4;
-    // Per-tile bookkeeping in registers, lane t <-> tiles t and t+64 of the
-    // chunk: one word per tile packing the physical id (< 2^27) and row count
-    // (0..16) of the block this wavefront loads for it (read with
-    // v_readlane, no LDS round trip in the tile loop), and two wave masks per
-    // half: tiles at or past the last row of the workgroup, and tiles that
-    // need the per-element mask (padding rows or the diagonal).
-    static_assert(kChunkBlocks == 2 * 4 * kWave, "two tiles of the chunk per lane");
-    uint32_t t_pk[2];
-    uint64_t past_mask[2], mask_mask[2];
-#pragma unroll
-    for (int hf = 0; hf < 2; ++hf) {
-      const int tile = hf * kWave + lane;
-      const int jl = tile * 4 + my_blk;
+    // Per-tile bookkeeping in registers, lane t <-> tile t of the chunk: the
+    // pool offset and row count of the block this wavefront loads for tile
+    // t (read back with v_readlane, no LDS round trip in the tile loop), and
+    // two wave masks: tiles at or past the last row of the workgroup, and
+    // tiles that need the per-element mask (padding rows or the diagonal).
+    static_assert(kChunkBlocks == 4 * kWave, "one tile of the chunk per lane");
+    uint32_t t_off_lo, t_off_hi;
+    int t_rows;
+    uint64_t past_mask, mask_mask;
+    {
+      const int jl = lane * 4 + my_blk;
       const bool in = jl < nblk;
-      t_pk[hf] = in ? (uint32_t(blk_phys[jl]) << 5) | uint32_t(blk_rows[jl]) : 0u;
-      const int jt = tile * 4;
+      const uint2 off = blk_off[jl];
+      t_off_lo = in ? off.x : 0u;
+      t_off_hi = in ? off.y : 0u;
+      t_rows = in ? blk_rows[jl] : 0;
+      const int jt = lane * 4;
       bool full = jt + 3 < nblk;
       int lp_last = 0;
 #pragma unroll
@@ -345,20 +346,19 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
         full = full && blk_rows[jj] == kBlk;
         lp_last = blk_lpos[jj];
       }
-      const bool past = tile >= ntiles || blk_lpos[min(jt, nblk - 1)] * kBlk > wg_qmax;
+      const bool past = lane >= ntiles || blk_lpos[min(jt, nblk - 1)] * kBlk > wg_qmax;
       const bool need = !full || lp_last * kBlk + kBlk - 1 > wg_qmin;
-      past_mask[hf] = __builtin_amdgcn_ballot_w64(past);
-      mask_mask[hf] = __builtin_amdgcn_ballot_w64(need);
+      past_mask = __builtin_amdgcn_ballot_w64(past);
+      mask_mask = __builtin_amdgcn_ballot_w64(need);
     }
     // buffer descriptor of this wavefront's block of tile ti; tiles past the
     // chunk get an empty range, so their DMA writes zeros and reads nothing
     auto tile_desc = [&](const char* base, int ti) {
-      const int tl = ti & (kWave - 1);
-      uint32_t pk = 0u;
-      if (ti < kWave) pk = __builtin_amdgcn_readlane(t_pk[0], tl);
-      else if (ti < 2 * kWave) pk = __builtin_amdgcn_readlane(t_pk[1], tl);
-      const uint32_t rows = pk & 31u;
-      const uint64_t a = reinterpret_cast<uint64_t>(base) + uint64_t(pk >> 5) * blk_stride;
+      const int tl = min(ti, kWave - 1);
+      const uint32_t lo = __builtin_amdgcn_readlane(t_off_lo, tl);
+      const uint32_t hi = __builtin_amdgcn_readlane(t_off_hi, tl);
+      const int rows = ti < kWave ? __builtin_amdgcn_readlane(t_rows, tl) : 0;
+      const uint64_t a = reinterpret_cast<uint64_t>(base) + ((uint64_t(hi) << 32) | lo);
       const u32x4_t r = {uint32_t(a), uint32_t(a >> 32) & 0xffffu, uint32_t(rows * tok_stride),
                          uint32_t(kBufferFlags)};
       return r;
@@ -455,7 +455,7 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
           vpre[2 * i + 1] = ds_read_tr16(vb0 + kUnit / 2);
         }
       }
-      if (((j < kWave ? mask_mask[0] >> j : mask_mask[1] >> (j - kWave)) & 1) != 0) {
+      if ((mask_mask >> j) & 1) {
         int lp[4], rw[4];
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
@@ -533,10 +533,7 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
     // before half-step 2k, and V(k+1) (iteration k-2) before 2k+1: B passes
     // that barrier at the end of its iteration k-1, A in the middle of its
     // iteration k.  Tiles past the workgroup's last row are never processed.
-    const int n_first = past_mask[0] != 0 ? int(__builtin_ctzll(past_mask[0]))
-                        : past_mask[1] != 0 ? kWave + int(__builtin_ctzll(past_mask[1]))
-                                            : 2 * kWave;
-    const int n_eff = min(ntiles, n_first);
+    const int n_eff = past_mask == 0 ? kWave : min(ntiles, int(__builtin_ctzll(past_mask)));
     if (n_eff == 0) {
       done = true;
       continue;
@@ -652,7 +649,6 @@ bool prefill_supported(msa_dtype dtype, int32_t D, int32_t G) {
 }
 
 int32_t prefill_max_split_blocks() { return kMaxSplitBlocks; }
-int32_t prefill_max_pool_blocks() { return kPhysLimit; }
 
 SplitPlan prefill_split(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t max_ctx_len,
                         int32_t block_size, int32_t split_blocks) {

@@ -189,8 +189,6 @@ def test_prefill_rejects_bad_args():
     # with more rows than the merge grid takes
     assert _prefill(lib, B=40000, C=16, maxctx=1 << 20, split=64) == _lib.MSA_ERR_UNSUPPORTED
     assert _prefill(lib, B=1, C=70000, maxctx=1 << 20, split=64) == _lib.MSA_ERR_UNSUPPORTED
-    # the kernel packs a block id into 27 bits of its per-tile word
-    assert _prefill(lib, P=(1 << 27) + 1) == _lib.MSA_ERR_UNSUPPORTED
 
 
 def test_header_compiles_as_c_and_cpp(tmp_path):
