@@ -138,6 +138,26 @@ def test_prefill_full_forced_split_sampled():
     check(w, O, L, seqs=[1, 2], heads=heads, rows=rows)
 
 
+@pytest.mark.parametrize("B,cached,C,mean_alive,split_blocks", [
+    (1, 3584, 512, 1e9, 4096),   # 256 blocks: exactly one key chunk
+    (1, 3600, 512, 1e9, 4096),   # 257 blocks: a second chunk of one block
+    (1, 7680, 512, 1e9, 4096),   # 512 blocks: two full chunks
+    (2, 20480, 128, 16.0, 4096),  # ~1100 blocks with evictions: five chunks
+    (2, 20480, 128, 16.0, 700),   # splits of <= 700 blocks: three chunks per split
+])
+def test_prefill_key_chunk_boundaries(B, cached, C, mean_alive, split_blocks):
+    """The kernel expands a split's alive blocks 256 at a time and restarts
+    its tile pipeline for each such key chunk; sequences at and just past
+    the boundary, and long ones spanning several chunks (with and without
+    splits), against the oracle on sampled rows and heads."""
+    w = make_workload(3, seed=2, B=B, cached=cached, C=C, mean_alive=mean_alive)
+    O, L = run_prefill(w, split_blocks=split_blocks)
+    rng = np.random.default_rng(7)
+    rows = np.sort(np.unique(np.concatenate([[0, 1, C // 2, C - 1], rng.choice(C, 6, replace=False)])))
+    heads = sorted(rng.choice(w.Hq, size=4, replace=False).tolist())
+    check(w, O, L, heads=heads, rows=rows)
+
+
 def test_recompute_small():
     """Recompute of an evicted middle range: chunk rows at q_pos0 in the middle
     of the context, alive blocks after the chunk hidden by the causal mask."""
