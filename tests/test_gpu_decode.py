@@ -5,7 +5,8 @@ the C ABI: max-abs-error <= 1e-5 for the fp32 family, <= 2e-2 for bf16 inputs
 with fp32 accumulation.  Sizes span many tiles and splits with ragged tails
 (partial last blocks, splits that end mid-tile, single-split and many-split
 sequences); full-size families 4 and 5 are checked on sampled (sequence,
-head) pairs the oracle computes one by one.  Also: empty sequences,
+head) pairs the oracle computes one by one.  Also: empty sequences, the
+maximum batch the grid takes (65535 sequences, with and without splits),
 run-to-run bitwise determinism, physical-relayout invariance, and the
 stand-alone merge call.
 """
@@ -127,6 +128,17 @@ def test_decode_empty_and_tiny_sequences():
         for b in (0, 3):
             assert np.all(O[b] == 0) and np.all(np.isneginf(L[b]))
         check(w, O, L, seqs=[1, 2, 4])
+
+
+@pytest.mark.parametrize("split_blocks", [0, 1])
+def test_decode_max_batch(split_blocks):
+    """65535 sequences, the most the decode grid takes (sequence is its
+    slowest dimension), each of three blocks with one of the first two
+    evicted; with split_blocks=1 every alive block is its own split and the
+    LSE merge runs over the same 65535 sequences."""
+    w = make_workload(1, seed=3, B=65535, Hq=4, Hkv=1, nb=3, pool=3 * 65535, n_evict=1)
+    O, L = run_decode(w, split_blocks)
+    check(w, O, L, seqs=[0, 1, 2, 31337, 65533, 65534])
 
 
 def test_decode_determinism():

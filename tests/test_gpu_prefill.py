@@ -8,7 +8,8 @@ context (later alive blocks must be masked by logical position), every GQA
 group size, forced key splits merged by log-sum-exp, rows with no visible
 key, the full-size prefill workload on sampled rows and heads, and the
 recompute workload (an evicted middle range rebuilt as a chunk in fresh pool
-slots, with alive blocks after it that only the causal mask hides).
+slots, with alive blocks after it that only the causal mask hides), the
+256-block key-chunk boundary, and the maximum batch the grid takes.
 """
 import numpy as np
 import pytest
@@ -156,6 +157,30 @@ def test_prefill_key_chunk_boundaries(B, cached, C, mean_alive, split_blocks):
     rows = np.sort(np.unique(np.concatenate([[0, 1, C // 2, C - 1], rng.choice(C, 6, replace=False)])))
     heads = sorted(rng.choice(w.Hq, size=4, replace=False).tolist())
     check(w, O, L, heads=heads, rows=rows)
+
+
+def test_prefill_max_batch():
+    """65535 sequences (the most the grid takes without a key split), each
+    a 4-row chunk (a partial block) after two cached blocks; odd sequences
+    have their second cached block evicted, so they carry two segments.
+    Sequences b and b + 1000 share their physical blocks (as shared prefixes
+    do), which keeps the pool small."""
+    from workloads.gen import Workload, _fill_pools_and_q, _live_slots
+    B, Hq, Hkv, D, bs, C, P = 65535, 4, 1, 128, 16, 4, 3000
+    rng = np.random.default_rng(11)
+    table = (3 * (np.arange(B, dtype=np.int32) % 1000))[:, None] + np.arange(3, dtype=np.int32)
+    alive = np.ones((B, 3), dtype=np.uint8)
+    alive[1::2, 1] = 0
+    table[alive == 0] = -1
+    ctx_len = np.full(B, 2 * bs + C, dtype=np.int32)
+    live = _live_slots(P, bs, table, alive, ctx_len)
+    q, kp, vp = _fill_pools_and_q(rng, "bf16", (B, C, Hq, D), P, bs, Hkv, D, live)
+    w = Workload(name="prefill_max_batch", kind="prefill", dtype="bf16", B=B, Hq=Hq, Hkv=Hkv,
+                 D=D, block_size=bs, block_table=table, alive=alive, ctx_len=ctx_len, q=q,
+                 k_pool=kp, v_pool=vp, scale=1.0 / np.sqrt(D), C=C,
+                 q_pos0=np.full(B, 2 * bs, dtype=np.int32))
+    O, L = run_prefill(w)
+    check(w, O, L, seqs=[0, 1, 2, 31337, 65533, 65534])
 
 
 def test_recompute_small():
