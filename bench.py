@@ -62,6 +62,8 @@ def parse():
                          "131k-token fragmented batch")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 256 MiB device copy (for counter calibration)")
+    ap.add_argument("--no-layout", action="store_true",
+                    help="skip the head-major pool layout decode leg")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="time only one call (for profiler runs)")
     return ap.parse_args()
@@ -123,7 +125,7 @@ class Prepared:
     the timed loops make the library calls with no allocation and no
     per-call argument building."""
 
-    def __init__(self, w, split_blocks=0):
+    def __init__(self, w, split_blocks=0, kv_layout=0):
         import ctypes
         import torch
         from kv_cache_attention_msa_amd import _lib
@@ -131,6 +133,10 @@ class Prepared:
         self.lib = _lib.load()
         self.w = w
         d = to_device(w, "cuda")
+        if kv_layout == _lib.MSA_LAYOUT_HND:
+            # the same values in head-major blocks [P, Hkv, 16, D]
+            d["k_pool"] = d["k_pool"].permute(0, 2, 1, 3).contiguous()
+            d["v_pool"] = d["v_pool"].permute(0, 2, 1, 3).contiguous()
         self.d = d
         dev = d["q"].device
         B, mb = w.block_table.shape
@@ -156,20 +162,23 @@ class Prepared:
                           B, mb, w.block_size, w.num_phys_blocks, P(self.segs.data_ptr()), self.cap,
                           P(self.indptr.data_ptr()), P(self.err.data_ptr()), P(self.pws.data_ptr()),
                           self.pws.numel(), s)
+        # the default token-major layout goes through msa_decode /
+        # msa_prefill_chunk, any other through their *_ex forms
+        lay = () if kv_layout == _lib.MSA_LAYOUT_NHD else (kv_layout,)
         if w.kind == "decode":
-            self.attn = self.lib.msa_decode
+            self.attn = self.lib.msa_decode_ex if lay else self.lib.msa_decode
             self.attn_args = (P(d["q"].data_ptr()), P(d["k_pool"].data_ptr()), P(d["v_pool"].data_ptr()),
                               w.num_phys_blocks, w.block_size, P(self.segs.data_ptr()), P(self.indptr.data_ptr()),
                               B, w.Hq, w.Hkv, w.D, self.max_ctx, dt, float(w.scale), split_blocks,
                               P(self.out.data_ptr()), P(self.lse.data_ptr()), P(self.ws.data_ptr()),
-                              self.ws.numel(), s)
+                              self.ws.numel()) + lay + (s,)
         else:
-            self.attn = self.lib.msa_prefill_chunk
+            self.attn = self.lib.msa_prefill_chunk_ex if lay else self.lib.msa_prefill_chunk
             self.attn_args = (P(d["q"].data_ptr()), w.C, P(d["q_pos0"].data_ptr()), P(d["k_pool"].data_ptr()),
                               P(d["v_pool"].data_ptr()), w.num_phys_blocks, w.block_size,
                               P(self.segs.data_ptr()), P(self.indptr.data_ptr()), B, w.Hq, w.Hkv, w.D,
                               self.max_ctx, dt, float(w.scale), split_blocks, P(self.out.data_ptr()),
-                              P(self.lse.data_ptr()), P(self.ws.data_ptr()), self.ws.numel(), s)
+                              P(self.lse.data_ptr()), P(self.ws.data_ptr()), self.ws.numel()) + lay + (s,)
 
     def plan(self):
         st = self.lib.msa_plan_segments(*self.plan_args)
@@ -480,6 +489,7 @@ def main():
         # dominant call: msa_decode (decode kernel + its split merge), HIP events
         dec_s = time_calls(prep.attention, args.steps, stream)
         dec_dist = call_percentiles(prep.attention, args.steps, stream)
+        out_nhd = prep.out.clone()
         plan_s = time_calls(prep.plan, args.steps, stream)
         value = alg_bytes / step_s / 1e9
         achieved = alg_bytes / dec_s / 1e9
@@ -540,6 +550,23 @@ def main():
             result["cpu_baseline"] = cpu_baseline(w, alg_bytes)
         del prep
         torch.cuda.empty_cache()
+        if not args.no_layout:
+            # the same batch with head-major pool blocks (msa_decode_ex)
+            from kv_cache_attention_msa_amd import _lib as _l
+            hp = Prepared(w, args.split_blocks, kv_layout=_l.MSA_LAYOUT_HND)
+            hp.plan()
+            warm_for(hp.attention, 0.1)
+            torch.cuda.synchronize()
+            same = bool(torch.equal(hp.out, out_nhd))
+            hnd_s = time_calls(hp.attention, args.steps, stream)
+            result["decode_hnd"] = {
+                "us_per_call": round(hnd_s * 1e6, 3), "GB/s": round(alg_bytes / hnd_s / 1e9, 2),
+                "pct_hbm_peak": round(100 * alg_bytes / hnd_s / 1e9 / HBM_PEAK_GBS, 2),
+                "bitwise_equal_to_nhd": same,
+                "note": "msa_decode_ex on the same batch with head-major pool blocks [P, Hkv, 16, D] "
+                        "(each KV head's 16 rows of a block contiguous)"}
+            del hp
+            torch.cuda.empty_cache()
 
     # ------------------------------------------- decode latency model (next)
     if args.latency_model:

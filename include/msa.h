@@ -35,6 +35,10 @@
  *
  * Memory layouts (row-major, innermost last)
  *   K/V pool    [P, block_size, Hkv, D]   dtype; P = num_phys_blocks
+ *               (token-major, MSA_LAYOUT_NHD: the default; the *_ex calls
+ *               also take the head-major [P, Hkv, block_size, D],
+ *               MSA_LAYOUT_HND, in which each KV head's rows of a block are
+ *               one contiguous run)
  *   decode Q    [B, Hq, D]                dtype
  *   decode O    [B, Hq, D]                dtype;  LSE [B, Hq] float32
  *   prefill Q   [B, C, Hq, D]             dtype
@@ -67,6 +71,9 @@ typedef enum {
 } msa_status;
 
 typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
+
+/* Order of the dimensions inside one pool block (see Memory layouts). */
+typedef enum { MSA_LAYOUT_NHD = 0, MSA_LAYOUT_HND = 1 } msa_kv_layout;
 
 /* Bits of the plan's device error word. */
 #define MSA_DEVERR_PHYS_RANGE 1 /* an alive block's physical id is outside [0, P); it was treated as evicted */
@@ -163,6 +170,17 @@ int msa_decode(const void* q, const void* k_pool, const void* v_pool, int32_t nu
                float scale, int32_t split_blocks, void* out, float* lse_out, void* workspace,
                size_t workspace_bytes, void* stream);
 
+/* msa_decode over pools in the block layout kv_layout (msa_decode itself is
+ * this call with MSA_LAYOUT_NHD).  Same arguments, results and errors; a
+ * kv_layout other than the two above returns MSA_ERR_INVALID_ARG.  Both
+ * layouts give bitwise-identical results on the same values. */
+int msa_decode_ex(const void* q, const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
+                  int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr,
+                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len,
+                  msa_dtype dtype, float scale, int32_t split_blocks, void* out, float* lse_out,
+                  void* workspace, size_t workspace_bytes, msa_kv_layout kv_layout,
+                  void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* a2+a4(+a5): chunked prefill                                               */
 /* ------------------------------------------------------------------------ */
@@ -203,6 +221,16 @@ int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const voi
                       int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype, float scale,
                       int32_t split_blocks, void* out, float* lse_out, void* workspace,
                       size_t workspace_bytes, void* stream);
+
+/* msa_prefill_chunk over pools in the block layout kv_layout (as
+ * msa_decode_ex). */
+int msa_prefill_chunk_ex(const void* q, int32_t C, const int32_t* q_pos0, const void* k_pool,
+                         const void* v_pool, int32_t num_phys_blocks, int32_t block_size,
+                         const msa_segment* segs, const int32_t* seg_indptr, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype,
+                         float scale, int32_t split_blocks, void* out, float* lse_out,
+                         void* workspace, size_t workspace_bytes, msa_kv_layout kv_layout,
+                         void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* a5: log-sum-exp merge of partials                                         */

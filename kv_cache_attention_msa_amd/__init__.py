@@ -20,12 +20,13 @@ import torch
 
 from . import _lib
 from ._lib import (MsaError, MSA_F32, MSA_BF16, MSA_DEVERR_PHYS_RANGE, MSA_DEVERR_CAPACITY,
-                   MSA_DEVERR_CTX_RANGE)
+                   MSA_DEVERR_CTX_RANGE, MSA_LAYOUT_NHD, MSA_LAYOUT_HND)
 
 __all__ = ["msa_plan_segments", "msa_decode", "msa_prefill_chunk", "msa_merge_partials",
            "msa_plan_workspace_size", "msa_decode_workspace_size", "msa_prefill_workspace_size",
            "MsaError", "MSA_F32", "MSA_BF16", "MSA_DEVERR_PHYS_RANGE", "MSA_DEVERR_CAPACITY",
-           "MSA_DEVERR_CTX_RANGE", "SEG_FIELDS", "library_path", "prefill_available", "decode_available"]
+           "MSA_DEVERR_CTX_RANGE", "MSA_LAYOUT_NHD", "MSA_LAYOUT_HND", "SEG_FIELDS", "library_path",
+           "prefill_available", "decode_available"]
 
 SEG_FIELDS = ("seq", "logical_block", "phys_block", "num_blocks", "num_tokens",
               "alive_token_start")
@@ -108,6 +109,21 @@ def _nbytes(t):
     return 0 if t is None else t.numel() * t.element_size()
 
 
+_LAYOUTS = {"NHD": MSA_LAYOUT_NHD, "HND": MSA_LAYOUT_HND}
+
+
+def _pool_dims(k_pool, kv_layout):
+    """(P, block_size, Hkv, D) of a pool in layout "NHD" ([P, bs, Hkv, D]) or
+    "HND" ([P, Hkv, bs, D]), and the layout's msa_kv_layout value."""
+    if kv_layout not in _LAYOUTS:
+        raise ValueError(f"kv_layout must be 'NHD' or 'HND', got {kv_layout!r}")
+    if kv_layout == "HND":
+        P, Hkv, bs, D = k_pool.shape
+    else:
+        P, bs, Hkv, D = k_pool.shape
+    return P, bs, Hkv, D, _LAYOUTS[kv_layout]
+
+
 # ---------------------------------------------------------------------------
 # a1: plan
 # ---------------------------------------------------------------------------
@@ -174,8 +190,9 @@ def msa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs
                seg_indptr: torch.Tensor, max_ctx_len: int, scale: float = 0.0,
                split_blocks: int = 0, out: torch.Tensor | None = None,
                lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-               want_lse: bool = True, stream=None):
-    """Decode attention.  q [B, Hq, D]; pools [P, 16, Hkv, D] (same dtype as q).
+               want_lse: bool = True, kv_layout: str = "NHD", stream=None):
+    """Decode attention.  q [B, Hq, D]; pools [P, 16, Hkv, D] (kv_layout "NHD")
+    or [P, Hkv, 16, D] ("HND"), same dtype as q.
     Returns (out [B, Hq, D], lse [B, Hq] float32 or None)."""
     lib = _lib_handle()
     if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
@@ -185,7 +202,7 @@ def msa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs
     _segs_table(segs)
     _expect(seg_indptr, torch.int32, "seg_indptr", 1)
     B, Hq, D = q.shape
-    P, bs, Hkv, Dk = k_pool.shape
+    P, bs, Hkv, Dk, layout = _pool_dims(k_pool, kv_layout)
     if Dk != D or seg_indptr.shape[0] != B + 1:
         raise ValueError("shape mismatch between q, pools and seg_indptr")
     dev = q.device
@@ -200,13 +217,13 @@ def msa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs
     wsb = int(lib.msa_decode_workspace_size(B, Hq, Hkv, D, max_ctx_len, bs, split_blocks))
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    st = lib.msa_decode(_dev_ptr(q, "q"), _dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"),
-                        P, bs, _dev_ptr(segs, "segs"), _dev_ptr(seg_indptr, "seg_indptr"),
-                        B, Hq, Hkv, D, int(max_ctx_len), _dtype_enum(q), float(scale),
-                        int(split_blocks), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
-                        _dev_ptr(workspace, "workspace"), _nbytes(workspace),
-                        _stream(stream, dev))
-    _lib.check(st, "msa_decode")
+    st = lib.msa_decode_ex(_dev_ptr(q, "q"), _dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"),
+                           P, bs, _dev_ptr(segs, "segs"), _dev_ptr(seg_indptr, "seg_indptr"),
+                           B, Hq, Hkv, D, int(max_ctx_len), _dtype_enum(q), float(scale),
+                           int(split_blocks), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
+                           _dev_ptr(workspace, "workspace"), _nbytes(workspace), layout,
+                           _stream(stream, dev))
+    _lib.check(st, "msa_decode_ex")
     return out, lse
 
 
@@ -223,9 +240,10 @@ def msa_prefill_chunk(q: torch.Tensor, q_pos0: torch.Tensor, k_pool: torch.Tenso
                       v_pool: torch.Tensor, segs: torch.Tensor, seg_indptr: torch.Tensor,
                       max_ctx_len: int, scale: float = 0.0, split_blocks: int = 0,
                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
-                      workspace: torch.Tensor | None = None, want_lse: bool = True, stream=None):
-    """Chunked-prefill attention.  q [B, C, Hq, D] bf16; q_pos0 int32 [B].
-    Returns (out [B, C, Hq, D], lse [B, C, Hq] float32 or None)."""
+                      workspace: torch.Tensor | None = None, want_lse: bool = True,
+                      kv_layout: str = "NHD", stream=None):
+    """Chunked-prefill attention.  q [B, C, Hq, D] bf16; q_pos0 int32 [B]; pools
+    as for msa_decode.  Returns (out [B, C, Hq, D], lse [B, C, Hq] float32 or None)."""
     lib = _lib_handle()
     if q.dim() != 4 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
         raise ValueError("q must be [B,C,Hq,D]; k_pool/v_pool [P,bs,Hkv,D] of equal shape")
@@ -235,7 +253,7 @@ def msa_prefill_chunk(q: torch.Tensor, q_pos0: torch.Tensor, k_pool: torch.Tenso
     _segs_table(segs)
     _expect(seg_indptr, torch.int32, "seg_indptr", 1)
     B, C, Hq, D = q.shape
-    P, bs, Hkv, Dk = k_pool.shape
+    P, bs, Hkv, Dk, layout = _pool_dims(k_pool, kv_layout)
     if Dk != D or seg_indptr.shape[0] != B + 1 or q_pos0.shape[0] != B:
         raise ValueError("shape mismatch between q, pools, q_pos0 and seg_indptr")
     dev = q.device
@@ -250,14 +268,14 @@ def msa_prefill_chunk(q: torch.Tensor, q_pos0: torch.Tensor, k_pool: torch.Tenso
     wsb = int(lib.msa_prefill_workspace_size(B, C, Hq, Hkv, D, max_ctx_len, bs, split_blocks))
     if workspace is None and wsb > 0:
         workspace = torch.empty(wsb, dtype=torch.uint8, device=dev)
-    st = lib.msa_prefill_chunk(_dev_ptr(q, "q"), C, _dev_ptr(q_pos0, "q_pos0"),
-                               _dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"), P, bs,
-                               _dev_ptr(segs, "segs"), _dev_ptr(seg_indptr, "seg_indptr"),
-                               B, Hq, Hkv, D, int(max_ctx_len), _dtype_enum(q), float(scale),
-                               int(split_blocks), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
-                               _dev_ptr(workspace, "workspace"), _nbytes(workspace),
-                               _stream(stream, dev))
-    _lib.check(st, "msa_prefill_chunk")
+    st = lib.msa_prefill_chunk_ex(_dev_ptr(q, "q"), C, _dev_ptr(q_pos0, "q_pos0"),
+                                  _dev_ptr(k_pool, "k_pool"), _dev_ptr(v_pool, "v_pool"), P, bs,
+                                  _dev_ptr(segs, "segs"), _dev_ptr(seg_indptr, "seg_indptr"),
+                                  B, Hq, Hkv, D, int(max_ctx_len), _dtype_enum(q), float(scale),
+                                  int(split_blocks), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
+                                  _dev_ptr(workspace, "workspace"), _nbytes(workspace), layout,
+                                  _stream(stream, dev))
+    _lib.check(st, "msa_prefill_chunk_ex")
     return out, lse
 
 
@@ -305,20 +323,21 @@ def msa_gather_alive(k_pool: torch.Tensor, v_pool: torch.Tensor, segs: torch.Ten
                      seg_indptr: torch.Tensor, blocks_per_seq: int,
                      dense_k: torch.Tensor | None = None, dense_v: torch.Tensor | None = None,
                      dense_segs: torch.Tensor | None = None,
-                     dense_indptr: torch.Tensor | None = None, stream=None):
+                     dense_indptr: torch.Tensor | None = None, kv_layout: str = "NHD",
+                     stream=None):
     """Copy each sequence's alive blocks, in logical order, into dense pools
-    [B * blocks_per_seq, 16, Hkv, D] and write the one-segment-per-sequence
-    plan of those pools.  Returns (dense_k, dense_v, dense_segs [B, 6],
-    dense_indptr [B + 1])."""
+    of B * blocks_per_seq blocks in the layout of the source pools (whole
+    blocks are copied) and write the one-segment-per-sequence plan of those
+    pools.  Returns (dense_k, dense_v, dense_segs [B, 6], dense_indptr [B + 1])."""
     lib = _lib_handle()
     if k_pool.dim() != 4 or v_pool.shape != k_pool.shape or v_pool.dtype != k_pool.dtype:
         raise ValueError("k_pool/v_pool must be [P,bs,Hkv,D] of equal shape and dtype")
     _segs_table(segs)
     _expect(seg_indptr, torch.int32, "seg_indptr", 1)
-    P, bs, Hkv, D = k_pool.shape
+    P, bs, Hkv, D, _ = _pool_dims(k_pool, kv_layout)
     B = seg_indptr.shape[0] - 1
     dev = k_pool.device
-    shape = (B * int(blocks_per_seq), bs, Hkv, D)
+    shape = (B * int(blocks_per_seq),) + tuple(k_pool.shape[1:])
     _expect_shape(dense_k, shape, k_pool.dtype, "dense_k")
     _expect_shape(dense_v, shape, k_pool.dtype, "dense_v")
     _expect_shape(dense_segs, (B, 6), torch.int32, "dense_segs")

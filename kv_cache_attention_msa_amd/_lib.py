@@ -20,6 +20,9 @@ MSA_ERR_DEVICE = -4
 MSA_F32 = 0
 MSA_BF16 = 1
 
+MSA_LAYOUT_NHD = 0  # pool blocks [P, block_size, Hkv, D]
+MSA_LAYOUT_HND = 1  # pool blocks [P, Hkv, block_size, D]
+
 MSA_DEVERR_PHYS_RANGE = 1
 MSA_DEVERR_CAPACITY = 2
 MSA_DEVERR_CTX_RANGE = 4
@@ -39,9 +42,14 @@ SIGNATURES = {
     "msa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "msa_decode": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                   ctypes.c_int, _f, _i32, _p, _p, _p, _sz, _p]),
+    "msa_decode_ex": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32,
+                                     ctypes.c_int, _f, _i32, _p, _p, _p, _sz, ctypes.c_int, _p]),
     "msa_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "msa_prefill_chunk": (ctypes.c_int, [_p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32,
                                          _i32, _i32, ctypes.c_int, _f, _i32, _p, _p, _p, _sz, _p]),
+    "msa_prefill_chunk_ex": (ctypes.c_int, [_p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32,
+                                            _i32, _i32, _i32, ctypes.c_int, _f, _i32, _p, _p, _p,
+                                            _sz, ctypes.c_int, _p]),
     "msa_merge_partials": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _p, _p]),
     "msa_gather_alive": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, ctypes.c_int, _i32,
                                         _p, _p, _p, _p, _p]),

@@ -119,14 +119,16 @@ size_t msa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
   return part_layout(int64_t(B) * sp.S, 1, Hq, D).total;
 }
 
-int msa_decode(const void* q, const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
-               int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr, int32_t B,
-               int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype,
-               float scale, int32_t split_blocks, void* out, float* lse_out, void* workspace,
-               size_t workspace_bytes, void* stream) {
+int msa_decode_ex(const void* q, const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
+                  int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr,
+                  int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len,
+                  msa_dtype dtype, float scale, int32_t split_blocks, void* out, float* lse_out,
+                  void* workspace, size_t workspace_bytes, msa_kv_layout kv_layout,
+                  void* stream) {
   int st = check_attn_shape(q, k_pool, v_pool, num_phys_blocks, block_size, segs, seg_indptr, B,
                             Hq, Hkv, D, max_ctx_len, dtype, scale, split_blocks, out);
   if (st != MSA_OK) return st;
+  if (kv_layout != MSA_LAYOUT_NHD && kv_layout != MSA_LAYOUT_HND) return MSA_ERR_INVALID_ARG;
   if (!decode_supported(dtype, D, Hq / Hkv)) return MSA_ERR_UNSUPPORTED;
   if (split_blocks > decode_max_split_blocks()) return MSA_ERR_INVALID_ARG;
   const SplitPlan sp = decode_split(B, Hkv, max_ctx_len, block_size, split_blocks);
@@ -144,6 +146,7 @@ int msa_decode(const void* q, const void* k_pool, const void* v_pool, int32_t nu
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.D = D;
+  p.head_major = kv_layout == MSA_LAYOUT_HND ? 1 : 0;
   p.dtype = dtype;
   p.scale_log2 = resolve_scale(scale, D) * kLog2e;
   p.split_blocks = sp.split_blocks;
@@ -168,6 +171,16 @@ int msa_decode(const void* q, const void* k_pool, const void* v_pool, int32_t nu
   return MSA_OK;
 }
 
+int msa_decode(const void* q, const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
+               int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr, int32_t B,
+               int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype,
+               float scale, int32_t split_blocks, void* out, float* lse_out, void* workspace,
+               size_t workspace_bytes, void* stream) {
+  return msa_decode_ex(q, k_pool, v_pool, num_phys_blocks, block_size, segs, seg_indptr, B, Hq,
+                       Hkv, D, max_ctx_len, dtype, scale, split_blocks, out, lse_out, workspace,
+                       workspace_bytes, MSA_LAYOUT_NHD, stream);
+}
+
 // ---------------------------------------------------------------------------
 size_t msa_prefill_workspace_size(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t D,
                                   int32_t max_ctx_len, int32_t block_size, int32_t split_blocks) {
@@ -178,15 +191,17 @@ size_t msa_prefill_workspace_size(int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
   return part_layout(int64_t(B) * sp.S, C, Hq, D).total;
 }
 
-int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const void* k_pool,
-                      const void* v_pool, int32_t num_phys_blocks, int32_t block_size,
-                      const msa_segment* segs, const int32_t* seg_indptr, int32_t B, int32_t Hq,
-                      int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype, float scale,
-                      int32_t split_blocks, void* out, float* lse_out, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+int msa_prefill_chunk_ex(const void* q, int32_t C, const int32_t* q_pos0, const void* k_pool,
+                         const void* v_pool, int32_t num_phys_blocks, int32_t block_size,
+                         const msa_segment* segs, const int32_t* seg_indptr, int32_t B,
+                         int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype,
+                         float scale, int32_t split_blocks, void* out, float* lse_out,
+                         void* workspace, size_t workspace_bytes, msa_kv_layout kv_layout,
+                         void* stream) {
   int st = check_attn_shape(q, k_pool, v_pool, num_phys_blocks, block_size, segs, seg_indptr, B,
                             Hq, Hkv, D, max_ctx_len, dtype, scale, split_blocks, out);
   if (st != MSA_OK) return st;
+  if (kv_layout != MSA_LAYOUT_NHD && kv_layout != MSA_LAYOUT_HND) return MSA_ERR_INVALID_ARG;
   if (!q_pos0 || C <= 0) return MSA_ERR_INVALID_ARG;
   if (!prefill_supported(dtype, D, Hq / Hkv)) return MSA_ERR_UNSUPPORTED;
   if (split_blocks > prefill_max_split_blocks()) return MSA_ERR_INVALID_ARG;
@@ -210,6 +225,7 @@ int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const voi
   p.Hq = Hq;
   p.Hkv = Hkv;
   p.D = D;
+  p.head_major = kv_layout == MSA_LAYOUT_HND ? 1 : 0;
   p.scale_log2 = resolve_scale(scale, D) * kLog2e;
   p.split_blocks = sp.split_blocks;
   p.S = sp.S;
@@ -231,6 +247,17 @@ int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const voi
     if (e != hipSuccess) return MSA_ERR_DEVICE;
   }
   return MSA_OK;
+}
+
+int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const void* k_pool,
+                      const void* v_pool, int32_t num_phys_blocks, int32_t block_size,
+                      const msa_segment* segs, const int32_t* seg_indptr, int32_t B, int32_t Hq,
+                      int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype, float scale,
+                      int32_t split_blocks, void* out, float* lse_out, void* workspace,
+                      size_t workspace_bytes, void* stream) {
+  return msa_prefill_chunk_ex(q, C, q_pos0, k_pool, v_pool, num_phys_blocks, block_size, segs,
+                              seg_indptr, B, Hq, Hkv, D, max_ctx_len, dtype, scale, split_blocks,
+                              out, lse_out, workspace, workspace_bytes, MSA_LAYOUT_NHD, stream);
 }
 
 // ---------------------------------------------------------------------------

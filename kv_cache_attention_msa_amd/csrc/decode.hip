@@ -251,10 +251,14 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   // block c/LPB), each lane one 16-byte chunk.  The block's base address is
   // wave-uniform (scalar registers); the per-lane offset is fixed for the
   // whole kernel, so no vector address arithmetic happens in the loop.
-  const size_t tok_stride = size_t(p.Hkv) * ROW;  // bytes between slots
-  const size_t blk_stride = tok_stride * kBlk;    // bytes between blocks
-  const char* kbase = static_cast<const char*>(p.k_pool) + size_t(g) * ROW;
-  const char* vbase = static_cast<const char*>(p.v_pool) + size_t(g) * ROW;
+  // bytes between the slots of one head in a block, between blocks, and
+  // from a block's start to this KV head's first row, for the token-major
+  // [P, bs, Hkv, D] or the head-major [P, Hkv, bs, D] pool
+  const size_t tok_stride = p.head_major ? size_t(ROW) : size_t(p.Hkv) * ROW;
+  const size_t blk_stride = size_t(p.Hkv) * ROW * kBlk;
+  const size_t head_off = p.head_major ? size_t(g) * ROW * kBlk : size_t(g) * ROW;
+  const char* kbase = static_cast<const char*>(p.k_pool) + head_off;
+  const char* vbase = static_cast<const char*>(p.v_pool) + head_off;
   // (rows of a block are tok_stride apart; a row's ROW bytes never cross
   // into the next row's range, so row-granular num_records is exact)
   const int lrow = lane / CH, lch = lane % CH;
@@ -585,10 +589,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
       qop[ds] = hl < G ? *reinterpret_cast<const uint4*>(qsrc + (4 * ds + q4) * 16) : make_uint4(0, 0, 0, 0);
   }
 
-  const size_t tok_stride = size_t(p.Hkv) * kMRow;
-  const size_t blk_stride = tok_stride * kBlk;
-  const char* kbase = static_cast<const char*>(p.k_pool) + size_t(g) * kMRow;
-  const char* vbase = static_cast<const char*>(p.v_pool) + size_t(g) * kMRow;
+  // slot, block and KV-head strides of the token-major or head-major pool
+  const size_t tok_stride = p.head_major ? size_t(kMRow) : size_t(p.Hkv) * kMRow;
+  const size_t blk_stride = size_t(p.Hkv) * kMRow * kBlk;
+  const size_t head_off = p.head_major ? size_t(g) * kMRow * kBlk : size_t(g) * kMRow;
+  const char* kbase = static_cast<const char*>(p.k_pool) + head_off;
+  const char* vbase = static_cast<const char*>(p.v_pool) + head_off;
   // K operand loads: lane offset inside a block for d step ds (adds 64 B each)
   const uint32_t k_voff = uint32_t(hl * tok_stride + q4 * 16);
   // V DMA unit (block, quarter dq of d): lane i writes 16 B at 16 i holding

@@ -89,6 +89,7 @@ struct DecodeParams {
   const msa_segment* segs;
   const int32_t* indptr;
   int32_t B, Hq, Hkv, D;
+  int32_t head_major;    // pool layout: 0 = [P, bs, Hkv, D], 1 = [P, Hkv, bs, D]
   msa_dtype dtype;
   float scale_log2;      // softmax scale * log2(e)
   int32_t split_blocks;  // blocks per split
@@ -110,6 +111,7 @@ struct PrefillParams {
   const msa_segment* segs;
   const int32_t* indptr;
   int32_t B, Hq, Hkv, D;
+  int32_t head_major;    // pool layout: 0 = [P, bs, Hkv, D], 1 = [P, Hkv, bs, D]
   float scale_log2;
   int32_t split_blocks;  // 0 = no split
   int32_t S;

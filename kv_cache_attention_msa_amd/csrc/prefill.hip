@@ -251,10 +251,13 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
     l_lane[r] = 0.f;
   }
 
-  const size_t tok_stride = size_t(p.Hkv) * kRow;
-  const size_t blk_stride = tok_stride * kBlk;
-  const char* kbase = static_cast<const char*>(p.k_pool) + size_t(g) * kRow;
-  const char* vbase = static_cast<const char*>(p.v_pool) + size_t(g) * kRow;
+  // slot, block and KV-head strides of the token-major [P, bs, Hkv, D] or
+  // head-major [P, Hkv, bs, D] pool
+  const size_t tok_stride = p.head_major ? size_t(kRow) : size_t(p.Hkv) * kRow;
+  const size_t blk_stride = size_t(p.Hkv) * kRow * kBlk;
+  const size_t head_off = p.head_major ? size_t(g) * kRow * kBlk : size_t(g) * kRow;
+  const char* kbase = static_cast<const char*>(p.k_pool) + head_off;
+  const char* vbase = static_cast<const char*>(p.v_pool) + head_off;
 
   // ---- LDS tile layout --------------------------------------------------
   // A tile (64 keys = 4 blocks) is 16 DMA units of 1 KB; unit u covers block

@@ -89,6 +89,21 @@ def test_decode_rejects_bad_args():
     assert _decode(lib, ws=NULL) == _lib.MSA_ERR_CAPACITY
 
 
+def test_layout_entry_points_reject_an_unknown_layout():
+    lib = _lib.load()
+    ws = 1 << 30
+    # everything else valid: only the layout is wrong
+    assert lib.msa_decode_ex(FAKE, FAKE, FAKE, 100, 16, FAKE, FAKE, 2, 32, 8, 128, 4096,
+                             _lib.MSA_BF16, 0.0, 0, FAKE, NULL, FAKE, ws, 2, NULL) == _lib.MSA_ERR_INVALID_ARG
+    assert lib.msa_prefill_chunk_ex(FAKE, 512, FAKE, FAKE, FAKE, 100, 16, FAKE, FAKE, 4, 32, 8,
+                                    128, 8704, _lib.MSA_BF16, 0.0, 0, FAKE, NULL, FAKE, ws, -1,
+                                    None) == _lib.MSA_ERR_INVALID_ARG
+    # argument errors are still found first with a valid layout
+    assert lib.msa_decode_ex(NULL, FAKE, FAKE, 100, 16, FAKE, FAKE, 2, 32, 8, 128, 4096,
+                             _lib.MSA_BF16, 0.0, 0, FAKE, NULL, FAKE, ws, _lib.MSA_LAYOUT_HND,
+                             None) == _lib.MSA_ERR_INVALID_ARG
+
+
 def test_decode_workspace_arithmetic():
     lib = _lib.load()
     # one split covers the context -> no workspace at all

@@ -7,6 +7,7 @@ with fp32 accumulation.  Sizes span many tiles and splits with ragged tails
 sequences); full-size families 4 and 5 are checked on sampled (sequence,
 head) pairs the oracle computes one by one.  Also: empty sequences, the
 maximum batch the grid takes (65535 sequences, with and without splits),
+head-major pool blocks (bitwise equal to the token-major layout),
 run-to-run bitwise determinism, physical-relayout invariance, and the
 stand-alone merge call.
 """
@@ -139,6 +140,42 @@ def test_decode_max_batch(split_blocks):
     w = make_workload(1, seed=3, B=65535, Hq=4, Hkv=1, nb=3, pool=3 * 65535, n_evict=1)
     O, L = run_decode(w, split_blocks)
     check(w, O, L, seqs=[0, 1, 2, 31337, 65533, 65534])
+
+
+def _decode_both_layouts(w, split_blocks):
+    d = to_device(w, DEV)
+    segs, indptr, err = msa.msa_plan_segments(d["block_table"], d["alive"], d["ctx_len"],
+                                              w.block_size, w.num_phys_blocks)
+    outs = []
+    for layout in ("NHD", "HND"):
+        k, v = d["k_pool"], d["v_pool"]
+        if layout == "HND":
+            k, v = k.permute(0, 2, 1, 3).contiguous(), v.permute(0, 2, 1, 3).contiguous()
+        outs.append(msa.msa_decode(d["q"], k, v, segs, indptr, max_ctx_len=int(w.ctx_len.max()),
+                                   scale=w.scale, split_blocks=split_blocks, kv_layout=layout))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    return outs
+
+
+@pytest.mark.parametrize("cfg,split_blocks", [(1, 0), (1, 16), (2, 0), (2, 16), (4, 16), (5, 0)])
+def test_decode_head_major_layout(cfg, split_blocks):
+    """Pools in head-major blocks [P, Hkv, 16, D] (msa_decode_ex): the same
+    values give bitwise the same O and LSE as the token-major layout, and
+    both match the oracle.  Covers the VALU kernel (fp32; grouped heads with
+    many splits), the MFMA kernel for 4 and 8 heads per KV head, and the
+    split merge."""
+    w = make_workload(cfg, seed=6, size="small")
+    (o_n, l_n), (o_h, l_h) = _decode_both_layouts(w, split_blocks)
+    assert torch.equal(o_n, o_h) and torch.equal(l_n, l_h)
+    check(w, from_device(o_h), l_h.cpu().numpy().astype(np.float64))
+
+
+def test_decode_head_major_layout_full():
+    w = make_workload(2, seed=0)
+    (o_n, l_n), (o_h, l_h) = _decode_both_layouts(w, 0)
+    assert torch.equal(o_n, o_h) and torch.equal(l_n, l_h)
+    check(w, from_device(o_h), l_h.cpu().numpy().astype(np.float64), seqs=[0, 17, 31])
 
 
 def test_decode_determinism():

@@ -159,6 +159,34 @@ def test_prefill_key_chunk_boundaries(B, cached, C, mean_alive, split_blocks):
     check(w, O, L, heads=heads, rows=rows)
 
 
+@pytest.mark.parametrize("size,split_blocks", [("small", 0), ("small", 16), ("full", 0)])
+def test_prefill_head_major_layout(size, split_blocks):
+    """Pools in head-major blocks [P, Hkv, 16, D] (msa_prefill_chunk_ex):
+    bitwise the same O and LSE as the token-major layout on the same values,
+    and the oracle agrees."""
+    w = make_workload(3, seed=4, size=size)
+    d = to_device(w, DEV)
+    segs, indptr, err = msa.msa_plan_segments(d["block_table"], d["alive"], d["ctx_len"],
+                                              w.block_size, w.num_phys_blocks)
+    outs = []
+    for layout in ("NHD", "HND"):
+        k, v = d["k_pool"], d["v_pool"]
+        if layout == "HND":
+            k, v = k.permute(0, 2, 1, 3).contiguous(), v.permute(0, 2, 1, 3).contiguous()
+        outs.append(msa.msa_prefill_chunk(d["q"], d["q_pos0"], k, v, segs, indptr,
+                                          max_ctx_len=int(w.ctx_len.max()), scale=w.scale,
+                                          split_blocks=split_blocks, kv_layout=layout))
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    (o_n, l_n), (o_h, l_h) = outs
+    assert torch.equal(o_n, o_h) and torch.equal(l_n, l_h)
+    O, L = from_device(o_h), l_h.cpu().numpy().astype(np.float64)
+    if size == "small":
+        check(w, O, L)
+    else:
+        check(w, O, L, seqs=[1], heads=[0, 13, 31], rows=np.array([0, 100, 255, 256, 511]))
+
+
 def test_prefill_max_batch():
     """65535 sequences (the most the grid takes without a key split), each
     a 4-row chunk (a partial block) after two cached blocks; odd sequences
