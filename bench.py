@@ -64,6 +64,9 @@ def parse():
                     help="also run a plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--no-layout", action="store_true",
                     help="skip the head-major pool layout decode leg")
+    ap.add_argument("--kv-layout", choices=["nhd", "hnd"], default="nhd",
+                    help="pool block layout of the headline decode leg: token-major "
+                         "[P, 16, Hkv, D] (default) or head-major [P, Hkv, 16, D]")
     ap.add_argument("--only", choices=["decode", "prefill"], default=None,
                     help="time only one call (for profiler runs)")
     return ap.parse_args()
@@ -223,6 +226,7 @@ class GatherBaseline:
         a[1], a[2], a[3] = P(self.dk.data_ptr()), P(self.dv.data_ptr()), w.B * bps
         a[5], a[6] = P(self.dsegs.data_ptr()), P(self.dind.data_ptr())
         self.attn_args = tuple(a)
+        self.attn = prep.attn  # msa_decode, or msa_decode_ex with the layout argument
 
     def gather(self):
         st = self.lib.msa_gather_alive(*self.gather_args)
@@ -230,7 +234,7 @@ class GatherBaseline:
             raise RuntimeError(f"msa_gather_alive failed: {st}")
 
     def attention(self):
-        st = self.lib.msa_decode(*self.attn_args)
+        st = self.attn(*self.attn_args)
         if st != 0:
             raise RuntimeError(f"msa_decode (dense) failed: {st}")
 
@@ -464,8 +468,11 @@ def main():
     result = {}
     # ---------------------------------------------------------------- decode
     if args.only in (None, "decode"):
+        from kv_cache_attention_msa_amd import _lib as _l
         w = make_workload(2, seed=args.seed)
-        prep = Prepared(w, args.split_blocks)
+        head_major = args.kv_layout == "hnd"
+        prep = Prepared(w, args.split_blocks,
+                        kv_layout=_l.MSA_LAYOUT_HND if head_major else _l.MSA_LAYOUT_NHD)
         esz = 2 if w.dtype == "bf16" else 4
         alive = alive_tokens_per_seq(w)
         kv_bytes = sum(alive) * w.Hkv * w.D * 2 * esz
@@ -496,7 +503,8 @@ def main():
         traffic = None
         if os.path.exists(COUNTERS):
             c = json.load(open(COUNTERS))
-            if c.get("sources_sha") == sources_sha(DECODE_SOURCES) and c.get("split_blocks", 0) == args.split_blocks:
+            if (c.get("sources_sha") == sources_sha(DECODE_SOURCES) and c.get("split_blocks", 0) == args.split_blocks
+                    and c.get("kv_layout", "nhd") == args.kv_layout):
                 traffic = c.get("bytes_per_call")
         result.update({
             "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
@@ -507,6 +515,7 @@ def main():
                        "head_dim": w.D, "ctx_len": int(w.ctx_len[0]), "block_size": w.block_size,
                        "evicted_fraction": round(w.meta["evicted_fraction"], 4),
                        "alive_tokens": int(sum(alive)), "segments": nseg,
+                       "kv_layout": "[P, Hkv, 16, D]" if head_major else "[P, 16, Hkv, D]",
                        "step": "msa_plan_segments + msa_decode (decode kernel + split-K merge)",
                        "seed": args.seed, "parallelism": "single GPU"},
             "tokens_per_s": round(w.B / step_s, 1),
@@ -550,9 +559,8 @@ def main():
             result["cpu_baseline"] = cpu_baseline(w, alg_bytes)
         del prep
         torch.cuda.empty_cache()
-        if not args.no_layout:
+        if not args.no_layout and not head_major:
             # the same batch with head-major pool blocks (msa_decode_ex)
-            from kv_cache_attention_msa_amd import _lib as _l
             hp = Prepared(w, args.split_blocks, kv_layout=_l.MSA_LAYOUT_HND)
             hp.plan()
             warm_for(hp.attention, 0.1)
