@@ -584,8 +584,10 @@ def main():
     if args.more_decode and args.only in (None, "decode"):
         legs = []
         for fam in (4, 5):
+            from kv_cache_attention_msa_amd import _lib as _l
             wf = make_workload(fam, seed=args.seed)
-            prep = Prepared(wf, args.split_blocks)
+            prep = Prepared(wf, args.split_blocks, kv_layout=_l.MSA_LAYOUT_HND if args.kv_layout == "hnd"
+                            else _l.MSA_LAYOUT_NHD)
             prep.plan()
             warm_for(prep.attention)
             t = time_calls(prep.attention, max(10, args.steps // 10), prep.stream)
@@ -596,7 +598,8 @@ def main():
                          "GB/s_logical": round(logical / t / 1e9, 1),
                          "GB/s_unique": round(unique / t / 1e9, 1),
                          "pct_hbm_peak_unique": round(100 * unique / t / 1e9 / HBM_PEAK_GBS, 2),
-                         "tokens_per_s": round(wf.B / t, 1), **realised(wf, prep)})
+                         "tokens_per_s": round(wf.B / t, 1), "kv_layout": args.kv_layout,
+                         **realised(wf, prep)})
             del prep, wf
             torch.cuda.empty_cache()
         result["more_decode"] = legs
