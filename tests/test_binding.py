@@ -114,3 +114,18 @@ def test_gather_refuses_misshapen_outputs(kw, msg):
     _, k, v, segs, ind = decode_inputs()
     with pytest.raises(ValueError, match=msg):
         msa.msa_gather_alive(k, v, segs, ind, 8, **kw)
+
+
+def test_layout_argument():
+    q, k, v, segs, ind = decode_inputs()
+    with pytest.raises(ValueError, match="kv_layout must be 'NHD' or 'HND'"):
+        msa.msa_decode(q, k, v, segs, ind, max_ctx_len=64, kv_layout="NDH")
+    # head-major pools [P, Hkv, 16, D]: the shapes are read in that order, so
+    # a well-formed call only stops at the host-tensor check
+    kh, vh = k.permute(0, 2, 1, 3).contiguous(), v.permute(0, 2, 1, 3).contiguous()
+    with pytest.raises(ValueError, match="device"):
+        msa.msa_decode(q, kh, vh, segs, ind, max_ctx_len=64, kv_layout="HND")
+    # a head dimension that disagrees with q's is refused
+    with pytest.raises(ValueError, match="shape mismatch"):
+        msa.msa_decode(q, bf16(10, 2, 16, 32), bf16(10, 2, 16, 32), segs, ind, max_ctx_len=64,
+                       kv_layout="HND")
