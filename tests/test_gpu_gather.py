@@ -6,7 +6,8 @@ must equal the pool row bit for bit, and the dense plan must be the
 one-segment-per-sequence plan.  Decode over the dense pools walks the same
 alive blocks in the same order with the same split boundaries, so its output
 must equal MSA decode over the fragmented pool bit for bit (and both match
-the fp64 oracle within the decode tolerances).
+the fp64 oracle within the decode tolerances).  Head-major pool blocks
+gather and decode to the same bits.
 """
 import numpy as np
 import pytest
@@ -85,3 +86,31 @@ def test_gather_bitwise_decode_full():
     torch.cuda.synchronize()
     assert np.array_equal(bits(out_g), bits(out_m))
     assert torch.equal(lse_g, lse_m)
+
+
+def test_gather_head_major_pools():
+    """Head-major pool blocks: the gather copies whole blocks whatever their
+    inner order, so gathering head-major pools gives the head-major image of
+    the token-major dense pools, and decode over it (msa_decode_ex) equals
+    the token-major dense decode bit for bit."""
+    w = make_workload(2, seed=3, size="small")
+    d = to_device(w, DEV)
+    segs, indptr, err = plan(w, d)
+    bps = int(-(-w.ctx_len.max() // w.block_size))
+    dk, dv, dsegs, dind, out_n, lse_n = dense_path(w, d, segs, indptr, bps)
+    kh = d["k_pool"].permute(0, 2, 1, 3).contiguous()
+    vh = d["v_pool"].permute(0, 2, 1, 3).contiguous()
+    dkh, dvh, dsegs_h, dind_h = msa.msa_gather_alive(kh, vh, segs, indptr, bps, kv_layout="HND")
+    out_h, lse_h = msa.msa_decode(d["q"], dkh, dvh, dsegs_h, dind_h, max_ctx_len=int(w.ctx_len.max()),
+                                  scale=w.scale, kv_layout="HND")
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    assert torch.equal(dsegs_h, dsegs) and torch.equal(dind_h, dind)
+    # alive blocks of the dense pools agree (dead dense slots are never read)
+    live = torch.zeros(dk.shape[0], dtype=torch.bool, device=dk.device)
+    for b in range(w.B):
+        n_alive = int(w.alive[b, :-(-int(w.ctx_len[b]) // w.block_size)].sum())
+        live[b * bps:b * bps + n_alive] = True
+    assert np.array_equal(bits(dkh[live]), bits(dk[live].permute(0, 2, 1, 3).contiguous()))
+    assert np.array_equal(bits(dvh[live]), bits(dv[live].permute(0, 2, 1, 3).contiguous()))
+    assert torch.equal(out_h, out_n) and torch.equal(lse_h, lse_n)
