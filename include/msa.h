@@ -269,7 +269,10 @@ int msa_merge_partials(const float* o_part, const float* m_part, const float* l_
  * then computes the same attention with a single segment per sequence.
  * Logical positions are renumbered, so the dense plan suits decode only.
  *
- *   k_pool, v_pool   [P, 16, Hkv, D] dtype (device, read)
+ *   k_pool, v_pool   [P, 16, Hkv, D] dtype (device, read); whole blocks are
+ *                    copied, so head-major [P, Hkv, 16, D] pools work alike
+ *                    (pass the same block_size and Hkv) and give head-major
+ *                    dense pools
  *   segs, seg_indptr a plan of those pools (device)
  *   dense_k, dense_v [B * blocks_per_seq, 16, Hkv, D] dtype (device, written)
  *   dense_segs       [B] msa_segment (device, written)
