@@ -171,11 +171,18 @@ def test_decode_head_major_layout(cfg, split_blocks):
     check(w, from_device(o_h), l_h.cpu().numpy().astype(np.float64))
 
 
-def test_decode_head_major_layout_full():
-    w = make_workload(2, seed=0)
+@pytest.mark.parametrize("cfg", [2, 4, 5])
+def test_decode_head_major_layout_full(cfg):
+    """Full-size batches (the headline one, the lognormal shared-prefix one
+    with its 11 splits, the 131k-token one): head-major equals token-major
+    bit for bit, and sampled (sequence, head) pairs match the oracle."""
+    w = make_workload(cfg, seed=0)
     (o_n, l_n), (o_h, l_h) = _decode_both_layouts(w, 0)
     assert torch.equal(o_n, o_h) and torch.equal(l_n, l_h)
-    check(w, from_device(o_h), l_h.cpu().numpy().astype(np.float64), seqs=[0, 17, 31])
+    rng = np.random.default_rng(10 + cfg)
+    seqs = sorted(rng.choice(w.B, size=min(w.B, 3), replace=False).tolist())
+    heads = sorted(rng.choice(w.Hq, size=4, replace=False).tolist())
+    check(w, from_device(o_h), l_h.cpu().numpy().astype(np.float64), seqs=seqs, heads=heads)
 
 
 def test_decode_determinism():
