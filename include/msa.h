@@ -28,9 +28,11 @@
  *     must be ordered on one stream.
  *   - Host-detectable argument errors return a negative msa_status before
  *     anything is enqueued.  Data errors that only the device can see are
- *     reported through the plan's `dev_error` word (see below); the kernels
- *     never read or write outside the buffers described here, whatever the
- *     data.
+ *     reported through a device error word (MSA_DEVERR_* bits): the plan
+ *     overwrites its `dev_error`; decode and prefill OR their bit into the
+ *     `dev_error` they are given (pass the plan's word to collect a whole
+ *     plan + attention step in one place).  The kernels never read or write
+ *     outside the buffers described here, whatever the data.
  *   - Logarithms are natural: LSE = ln(sum exp(score)), score = scale*q.k.
  *
  * Memory layouts (row-major, innermost last)
@@ -60,7 +62,7 @@
 extern "C" {
 #endif
 
-#define MSA_VERSION 1
+#define MSA_VERSION 2
 
 typedef enum {
   MSA_OK = 0,
@@ -75,10 +77,18 @@ typedef enum { MSA_F32 = 0, MSA_BF16 = 1 } msa_dtype;
 /* Order of the dimensions inside one pool block (see Memory layouts). */
 typedef enum { MSA_LAYOUT_NHD = 0, MSA_LAYOUT_HND = 1 } msa_kv_layout;
 
-/* Bits of the plan's device error word. */
-#define MSA_DEVERR_PHYS_RANGE 1 /* an alive block's physical id is outside [0, P); it was treated as evicted */
-#define MSA_DEVERR_CAPACITY 2   /* more segments than seg_capacity; extra records dropped, indptr clamped */
-#define MSA_DEVERR_CTX_RANGE 4  /* ctx_len < 0 or > max_blocks*block_size; clamped into range */
+/* Bits of the device error word. */
+#define MSA_DEVERR_PHYS_RANGE 1 /* plan: an alive block's physical id is outside [0, P); it was treated as evicted */
+#define MSA_DEVERR_CAPACITY 2   /* plan: more segments than seg_capacity; extra records dropped, indptr clamped */
+#define MSA_DEVERR_CTX_RANGE 4  /* plan: ctx_len < 0 or > max_blocks*block_size; clamped into range */
+#define MSA_DEVERR_TRUNCATED 8  /* decode/prefill: a sequence has more alive tokens than max_ctx_len
+                                   allows for; its keys were cut at the grid's capacity */
+
+/* Which decode kernel runs (msa_decode_ex).  AUTO picks per shape and split
+ * count; VECTOR is the vector-ALU kernel (every supported shape); MATRIX the
+ * matrix-core kernel, built for bf16 with D 128 and Hq/Hkv 4 or 8 only
+ * (MSA_ERR_UNSUPPORTED otherwise). */
+typedef enum { MSA_DECODE_AUTO = 0, MSA_DECODE_VECTOR = 1, MSA_DECODE_MATRIX = 2 } msa_decode_kernel;
 
 /* One segment: a maximal run of alive blocks of one sequence that are
  * consecutive both in logical index and in physical id.  24 bytes, plain
@@ -157,9 +167,13 @@ size_t msa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  *                a sequence with more alive tokens is cut to its first
  *                ceil(ceil(max_ctx_len/16) / split_blocks) x split_blocks
  *                alive blocks in logical order -- memory-safe, but the
- *                result then covers only those keys)
+ *                result then covers only those keys, and the cut sets
+ *                MSA_DEVERR_TRUNCATED in dev_error)
  *   scale        softmax scale; <= 0 selects 1/sqrt(D)
  *   out          [B, Hq, D] dtype           lse_out  [B, Hq] float32, may be NULL
+ *   dev_error    int32 [1], may be NULL: MSA_DEVERR_TRUNCATED is ORed in
+ *                when a sequence was cut at the grid (understated
+ *                max_ctx_len); the word is never cleared by this call
  * A sequence with no alive token gets out = 0 and lse = -inf.  Accumulation
  * is float32 throughout; for bf16 with D 128 and Hq/Hkv 4 or 8 the scores
  * and the output run on bf16 matrix cores, so the softmax weights are rounded
@@ -168,18 +182,22 @@ int msa_decode(const void* q, const void* k_pool, const void* v_pool, int32_t nu
                int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr, int32_t B,
                int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype,
                float scale, int32_t split_blocks, void* out, float* lse_out, void* workspace,
-               size_t workspace_bytes, void* stream);
+               size_t workspace_bytes, int32_t* dev_error, void* stream);
 
-/* msa_decode over pools in the block layout kv_layout (msa_decode itself is
- * this call with MSA_LAYOUT_NHD).  Same arguments, results and errors; a
- * kv_layout other than the two above returns MSA_ERR_INVALID_ARG.  Both
- * layouts give bitwise-identical results on the same values. */
+/* msa_decode over pools in the block layout kv_layout, with the decode
+ * kernel chosen by `kernel` (msa_decode itself is this call with
+ * MSA_LAYOUT_NHD and MSA_DECODE_AUTO).  Same arguments, results and errors;
+ * a kv_layout or kernel value other than those above returns
+ * MSA_ERR_INVALID_ARG, MSA_DECODE_MATRIX on a shape it was not built for
+ * MSA_ERR_UNSUPPORTED.  Both layouts give bitwise-identical results on the
+ * same values; the two kernels agree within the bf16 tolerance (the matrix
+ * kernel rounds the softmax weights to bf16 for P x V). */
 int msa_decode_ex(const void* q, const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
                   int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr,
                   int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len,
                   msa_dtype dtype, float scale, int32_t split_blocks, void* out, float* lse_out,
                   void* workspace, size_t workspace_bytes, msa_kv_layout kv_layout,
-                  void* stream);
+                  msa_decode_kernel kernel, int32_t* dev_error, void* stream);
 
 /* ------------------------------------------------------------------------ */
 /* a2+a4(+a5): chunked prefill                                               */
@@ -202,7 +220,8 @@ size_t msa_prefill_workspace_size(int32_t B, int32_t C, int32_t Hq, int32_t Hkv,
  *   out     [B, C, Hq, D] bf16     lse_out [B, C, Hq] float32, may be NULL
  *   max_ctx_len  as for msa_decode: bounds every sequence's alive tokens
  *                (the chunk's included) and sizes the grid; a longer
- *                sequence is cut the same way
+ *                sequence is cut the same way and sets MSA_DEVERR_TRUNCATED
+ *   dev_error    int32 [1], may be NULL: as for msa_decode
  *   split_blocks  0 = automatic: the alive-key stream is split only when the
  *                 (row tile, KV head, sequence) work items do not cover the
  *                 chip's 256 CUs; otherwise it is cut into near-equal splits
@@ -220,7 +239,7 @@ int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const voi
                       const msa_segment* segs, const int32_t* seg_indptr, int32_t B, int32_t Hq,
                       int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype, float scale,
                       int32_t split_blocks, void* out, float* lse_out, void* workspace,
-                      size_t workspace_bytes, void* stream);
+                      size_t workspace_bytes, int32_t* dev_error, void* stream);
 
 /* msa_prefill_chunk over pools in the block layout kv_layout (as
  * msa_decode_ex). */
@@ -230,7 +249,27 @@ int msa_prefill_chunk_ex(const void* q, int32_t C, const int32_t* q_pos0, const 
                          int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype,
                          float scale, int32_t split_blocks, void* out, float* lse_out,
                          void* workspace, size_t workspace_bytes, msa_kv_layout kv_layout,
-                         void* stream);
+                         int32_t* dev_error, void* stream);
+
+/* Chunk length for the next msa_prefill_chunk call of an adaptive chunking
+ * scheduler (P1 "3. 自适应分块调度器": prefill of a long prompt runs in
+ * chunks whose size follows the attention kernel's occupancy).
+ *
+ * msa_prefill_chunk runs one workgroup per (256/(Hq/Hkv) query positions,
+ * KV head, sequence), one workgroup per compute unit.  The call returns the
+ * smallest multiple of those 256/(Hq/Hkv) positions whose workgroups cover
+ * all `compute_units` (<= 0 selects 256, MI355X); below it the kernel must
+ * split the key stream (partials and a merge), above it the rate per flop
+ * stays flat while each chunk, and the decode steps waiting on it, takes
+ * longer.  The result is capped at max_rows and at remaining_tokens (the
+ * prompt tokens still to prefill, per sequence), and a remainder shorter
+ * than one position tile is folded into this chunk when max_rows allows.
+ * Returns the chunk length (0 when remaining_tokens is 0), or a negative
+ * msa_status: INVALID_ARG for non-positive B, Hq, Hkv or max_rows, negative
+ * remaining_tokens or Hq % Hkv != 0; UNSUPPORTED for a group size the
+ * prefill kernel was not built for.  Host only, no device work. */
+int32_t msa_prefill_chunk_rows(int32_t B, int32_t Hq, int32_t Hkv, int32_t remaining_tokens,
+                               int32_t max_rows, int32_t compute_units);
 
 /* ------------------------------------------------------------------------ */
 /* a5: log-sum-exp merge of partials                                         */

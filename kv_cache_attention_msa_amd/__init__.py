@@ -20,13 +20,16 @@ import torch
 
 from . import _lib
 from ._lib import (MsaError, MSA_F32, MSA_BF16, MSA_DEVERR_PHYS_RANGE, MSA_DEVERR_CAPACITY,
-                   MSA_DEVERR_CTX_RANGE, MSA_LAYOUT_NHD, MSA_LAYOUT_HND)
+                   MSA_DEVERR_CTX_RANGE, MSA_DEVERR_TRUNCATED, MSA_LAYOUT_NHD, MSA_LAYOUT_HND,
+                   MSA_DECODE_AUTO, MSA_DECODE_VECTOR, MSA_DECODE_MATRIX)
 
 __all__ = ["msa_plan_segments", "msa_decode", "msa_prefill_chunk", "msa_merge_partials",
+           "msa_prefill_chunk_rows",
            "msa_plan_workspace_size", "msa_decode_workspace_size", "msa_prefill_workspace_size",
            "MsaError", "MSA_F32", "MSA_BF16", "MSA_DEVERR_PHYS_RANGE", "MSA_DEVERR_CAPACITY",
-           "MSA_DEVERR_CTX_RANGE", "MSA_LAYOUT_NHD", "MSA_LAYOUT_HND", "SEG_FIELDS", "library_path",
-           "prefill_available", "decode_available"]
+           "MSA_DEVERR_CTX_RANGE", "MSA_DEVERR_TRUNCATED", "MSA_LAYOUT_NHD", "MSA_LAYOUT_HND",
+           "MSA_DECODE_AUTO", "MSA_DECODE_VECTOR", "MSA_DECODE_MATRIX", "SEG_FIELDS",
+           "library_path", "prefill_available", "decode_available"]
 
 SEG_FIELDS = ("seq", "logical_block", "phys_block", "num_blocks", "num_tokens",
               "alive_token_start")
@@ -110,6 +113,7 @@ def _nbytes(t):
 
 
 _LAYOUTS = {"NHD": MSA_LAYOUT_NHD, "HND": MSA_LAYOUT_HND}
+_KERNELS = {"auto": MSA_DECODE_AUTO, "vector": MSA_DECODE_VECTOR, "matrix": MSA_DECODE_MATRIX}
 
 
 def _pool_dims(k_pool, kv_layout):
@@ -190,11 +194,16 @@ def msa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs
                seg_indptr: torch.Tensor, max_ctx_len: int, scale: float = 0.0,
                split_blocks: int = 0, out: torch.Tensor | None = None,
                lse: torch.Tensor | None = None, workspace: torch.Tensor | None = None,
-               want_lse: bool = True, kv_layout: str = "NHD", stream=None):
+               want_lse: bool = True, kv_layout: str = "NHD", kernel: str = "auto",
+               dev_error: torch.Tensor | None = None, stream=None):
     """Decode attention.  q [B, Hq, D]; pools [P, 16, Hkv, D] (kv_layout "NHD")
-    or [P, Hkv, 16, D] ("HND"), same dtype as q.
+    or [P, Hkv, 16, D] ("HND"), same dtype as q.  kernel: "auto", "vector" or
+    "matrix" (msa_decode_kernel).  dev_error: optional int32 [1] device word
+    into which MSA_DEVERR_TRUNCATED is ORed (pass the plan's).
     Returns (out [B, Hq, D], lse [B, Hq] float32 or None)."""
     lib = _lib_handle()
+    if kernel not in _KERNELS:
+        raise ValueError(f"kernel must be one of {sorted(_KERNELS)}, got {kernel!r}")
     if q.dim() != 3 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
         raise ValueError("q must be [B,Hq,D]; k_pool/v_pool [P,bs,Hkv,D] of equal shape")
     if q.dtype != k_pool.dtype or v_pool.dtype != k_pool.dtype:
@@ -208,8 +217,9 @@ def msa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs
     dev = q.device
     _expect_shape(out, (B, Hq, D), q.dtype, "out")
     _expect_shape(lse, (B, Hq), torch.float32, "lse")
+    _expect_shape(dev_error, (1,), torch.int32, "dev_error")
     _same_device(dev, k_pool=k_pool, v_pool=v_pool, segs=segs, seg_indptr=seg_indptr, out=out,
-                 lse=lse, workspace=workspace)
+                 lse=lse, workspace=workspace, dev_error=dev_error)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -222,7 +232,7 @@ def msa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs
                            B, Hq, Hkv, D, int(max_ctx_len), _dtype_enum(q), float(scale),
                            int(split_blocks), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
                            _dev_ptr(workspace, "workspace"), _nbytes(workspace), layout,
-                           _stream(stream, dev))
+                           _KERNELS[kernel], _dev_ptr(dev_error, "dev_error"), _stream(stream, dev))
     _lib.check(st, "msa_decode_ex")
     return out, lse
 
@@ -241,9 +251,10 @@ def msa_prefill_chunk(q: torch.Tensor, q_pos0: torch.Tensor, k_pool: torch.Tenso
                       max_ctx_len: int, scale: float = 0.0, split_blocks: int = 0,
                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                       workspace: torch.Tensor | None = None, want_lse: bool = True,
-                      kv_layout: str = "NHD", stream=None):
+                      kv_layout: str = "NHD", dev_error: torch.Tensor | None = None, stream=None):
     """Chunked-prefill attention.  q [B, C, Hq, D] bf16; q_pos0 int32 [B]; pools
-    as for msa_decode.  Returns (out [B, C, Hq, D], lse [B, C, Hq] float32 or None)."""
+    and dev_error as for msa_decode.
+    Returns (out [B, C, Hq, D], lse [B, C, Hq] float32 or None)."""
     lib = _lib_handle()
     if q.dim() != 4 or k_pool.dim() != 4 or v_pool.shape != k_pool.shape:
         raise ValueError("q must be [B,C,Hq,D]; k_pool/v_pool [P,bs,Hkv,D] of equal shape")
@@ -259,8 +270,9 @@ def msa_prefill_chunk(q: torch.Tensor, q_pos0: torch.Tensor, k_pool: torch.Tenso
     dev = q.device
     _expect_shape(out, (B, C, Hq, D), q.dtype, "out")
     _expect_shape(lse, (B, C, Hq), torch.float32, "lse")
+    _expect_shape(dev_error, (1,), torch.int32, "dev_error")
     _same_device(dev, q_pos0=q_pos0, k_pool=k_pool, v_pool=v_pool, segs=segs,
-                 seg_indptr=seg_indptr, out=out, lse=lse, workspace=workspace)
+                 seg_indptr=seg_indptr, out=out, lse=lse, workspace=workspace, dev_error=dev_error)
     if out is None:
         out = torch.empty_like(q)
     if lse is None and want_lse:
@@ -274,9 +286,22 @@ def msa_prefill_chunk(q: torch.Tensor, q_pos0: torch.Tensor, k_pool: torch.Tenso
                                   B, Hq, Hkv, D, int(max_ctx_len), _dtype_enum(q), float(scale),
                                   int(split_blocks), _dev_ptr(out, "out"), _dev_ptr(lse, "lse"),
                                   _dev_ptr(workspace, "workspace"), _nbytes(workspace), layout,
-                                  _stream(stream, dev))
+                                  _dev_ptr(dev_error, "dev_error"), _stream(stream, dev))
     _lib.check(st, "msa_prefill_chunk_ex")
     return out, lse
+
+
+def msa_prefill_chunk_rows(B: int, Hq: int, Hkv: int, remaining_tokens: int, max_rows: int = 8192,
+                           compute_units: int = 0) -> int:
+    """Chunk length for the next prefill chunk of an adaptive chunking
+    scheduler (msa_prefill_chunk_rows in include/msa.h): the smallest whole
+    number of the kernel's position tiles whose workgroups cover every
+    compute unit, capped at max_rows and remaining_tokens."""
+    r = int(_lib_handle().msa_prefill_chunk_rows(B, Hq, Hkv, remaining_tokens, max_rows,
+                                                 compute_units))
+    if r < 0:
+        raise MsaError(r, "msa_prefill_chunk_rows")
+    return r
 
 
 # ---------------------------------------------------------------------------

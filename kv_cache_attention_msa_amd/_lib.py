@@ -26,6 +26,11 @@ MSA_LAYOUT_HND = 1  # pool blocks [P, Hkv, block_size, D]
 MSA_DEVERR_PHYS_RANGE = 1
 MSA_DEVERR_CAPACITY = 2
 MSA_DEVERR_CTX_RANGE = 4
+MSA_DEVERR_TRUNCATED = 8
+
+MSA_DECODE_AUTO = 0    # decode kernel chosen per shape and split count
+MSA_DECODE_VECTOR = 1  # vector-ALU decode kernel
+MSA_DECODE_MATRIX = 2  # matrix-core decode kernel (bf16, D 128, Hq/Hkv 4 or 8)
 
 # every symbol include/msa.h declares, with (restype, argtypes)
 _i32 = ctypes.c_int32
@@ -41,15 +46,18 @@ SIGNATURES = {
     "msa_plan_segments": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _i32, _i32, _p, _i32, _p, _p, _p, _sz, _p]),
     "msa_decode_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "msa_decode": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32,
-                                  ctypes.c_int, _f, _i32, _p, _p, _p, _sz, _p]),
+                                  ctypes.c_int, _f, _i32, _p, _p, _p, _sz, _p, _p]),
     "msa_decode_ex": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32,
-                                     ctypes.c_int, _f, _i32, _p, _p, _p, _sz, ctypes.c_int, _p]),
+                                     ctypes.c_int, _f, _i32, _p, _p, _p, _sz, ctypes.c_int,
+                                     ctypes.c_int, _p, _p]),
     "msa_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "msa_prefill_chunk": (ctypes.c_int, [_p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32,
-                                         _i32, _i32, ctypes.c_int, _f, _i32, _p, _p, _p, _sz, _p]),
+                                         _i32, _i32, ctypes.c_int, _f, _i32, _p, _p, _p, _sz, _p,
+                                         _p]),
     "msa_prefill_chunk_ex": (ctypes.c_int, [_p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32,
                                             _i32, _i32, _i32, ctypes.c_int, _f, _i32, _p, _p, _p,
-                                            _sz, ctypes.c_int, _p]),
+                                            _sz, ctypes.c_int, _p, _p]),
+    "msa_prefill_chunk_rows": (_i32, [_i32, _i32, _i32, _i32, _i32, _i32]),
     "msa_merge_partials": (ctypes.c_int, [_p, _p, _p, _p, _i32, _i32, _i32, _i32, ctypes.c_int, _p, _p, _p]),
     "msa_gather_alive": (ctypes.c_int, [_p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, ctypes.c_int, _i32,
                                         _p, _p, _p, _p, _p]),

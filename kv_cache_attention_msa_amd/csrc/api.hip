@@ -79,7 +79,8 @@ const char* msa_status_string(int status) {
 }
 
 // ---------------------------------------------------------------------------
-size_t msa_plan_workspace_size(int32_t B) { return B > 0 ? align_up(size_t(B) * 2 * sizeof(int32_t)) : 0; }
+// per sequence: segment count, error flags, record offset
+size_t msa_plan_workspace_size(int32_t B) { return B > 0 ? align_up(size_t(B) * 3 * sizeof(int32_t)) : 0; }
 
 int msa_plan_segments(const int32_t* block_table, const uint8_t* alive, const int32_t* ctx_len,
                       int32_t B, int32_t max_blocks, int32_t block_size, int32_t num_phys_blocks,
@@ -107,6 +108,7 @@ int msa_plan_segments(const int32_t* block_table, const uint8_t* alive, const in
   p.indptr = seg_indptr;
   p.dev_error = dev_error;
   p.ws = static_cast<int32_t*>(workspace);
+  p.scanned = plan_uses_scan(B) ? 1 : 0;
   return from_hip(launch_plan(p, as_stream(stream)));
 }
 
@@ -124,12 +126,16 @@ int msa_decode_ex(const void* q, const void* k_pool, const void* v_pool, int32_t
                   int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len,
                   msa_dtype dtype, float scale, int32_t split_blocks, void* out, float* lse_out,
                   void* workspace, size_t workspace_bytes, msa_kv_layout kv_layout,
-                  void* stream) {
+                  msa_decode_kernel kernel, int32_t* dev_error, void* stream) {
   int st = check_attn_shape(q, k_pool, v_pool, num_phys_blocks, block_size, segs, seg_indptr, B,
                             Hq, Hkv, D, max_ctx_len, dtype, scale, split_blocks, out);
   if (st != MSA_OK) return st;
   if (kv_layout != MSA_LAYOUT_NHD && kv_layout != MSA_LAYOUT_HND) return MSA_ERR_INVALID_ARG;
+  if (kernel != MSA_DECODE_AUTO && kernel != MSA_DECODE_VECTOR && kernel != MSA_DECODE_MATRIX)
+    return MSA_ERR_INVALID_ARG;
   if (!decode_supported(dtype, D, Hq / Hkv)) return MSA_ERR_UNSUPPORTED;
+  if (kernel == MSA_DECODE_MATRIX && !decode_matrix_supported(dtype, D, Hq / Hkv))
+    return MSA_ERR_UNSUPPORTED;
   if (split_blocks > decode_max_split_blocks()) return MSA_ERR_INVALID_ARG;
   const SplitPlan sp = decode_split(B, Hkv, max_ctx_len, block_size, split_blocks);
   const size_t need = msa_decode_workspace_size(B, Hq, Hkv, D, max_ctx_len, block_size, split_blocks);
@@ -151,6 +157,8 @@ int msa_decode_ex(const void* q, const void* k_pool, const void* v_pool, int32_t
   p.scale_log2 = resolve_scale(scale, D) * kLog2e;
   p.split_blocks = sp.split_blocks;
   p.S = sp.S;
+  p.kernel = kernel;
+  p.dev_error = dev_error;
   p.out = out;
   p.lse = lse_out;
   p.o_part = p.m_part = p.l_part = nullptr;
@@ -175,10 +183,10 @@ int msa_decode(const void* q, const void* k_pool, const void* v_pool, int32_t nu
                int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr, int32_t B,
                int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype,
                float scale, int32_t split_blocks, void* out, float* lse_out, void* workspace,
-               size_t workspace_bytes, void* stream) {
+               size_t workspace_bytes, int32_t* dev_error, void* stream) {
   return msa_decode_ex(q, k_pool, v_pool, num_phys_blocks, block_size, segs, seg_indptr, B, Hq,
                        Hkv, D, max_ctx_len, dtype, scale, split_blocks, out, lse_out, workspace,
-                       workspace_bytes, MSA_LAYOUT_NHD, stream);
+                       workspace_bytes, MSA_LAYOUT_NHD, MSA_DECODE_AUTO, dev_error, stream);
 }
 
 // ---------------------------------------------------------------------------
@@ -197,7 +205,7 @@ int msa_prefill_chunk_ex(const void* q, int32_t C, const int32_t* q_pos0, const 
                          int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype,
                          float scale, int32_t split_blocks, void* out, float* lse_out,
                          void* workspace, size_t workspace_bytes, msa_kv_layout kv_layout,
-                         void* stream) {
+                         int32_t* dev_error, void* stream) {
   int st = check_attn_shape(q, k_pool, v_pool, num_phys_blocks, block_size, segs, seg_indptr, B,
                             Hq, Hkv, D, max_ctx_len, dtype, scale, split_blocks, out);
   if (st != MSA_OK) return st;
@@ -229,6 +237,7 @@ int msa_prefill_chunk_ex(const void* q, int32_t C, const int32_t* q_pos0, const 
   p.scale_log2 = resolve_scale(scale, D) * kLog2e;
   p.split_blocks = sp.split_blocks;
   p.S = sp.S;
+  p.dev_error = dev_error;
   p.out = out;
   p.lse = lse_out;
   p.o_part = p.m_part = p.l_part = nullptr;
@@ -254,10 +263,21 @@ int msa_prefill_chunk(const void* q, int32_t C, const int32_t* q_pos0, const voi
                       const msa_segment* segs, const int32_t* seg_indptr, int32_t B, int32_t Hq,
                       int32_t Hkv, int32_t D, int32_t max_ctx_len, msa_dtype dtype, float scale,
                       int32_t split_blocks, void* out, float* lse_out, void* workspace,
-                      size_t workspace_bytes, void* stream) {
+                      size_t workspace_bytes, int32_t* dev_error, void* stream) {
   return msa_prefill_chunk_ex(q, C, q_pos0, k_pool, v_pool, num_phys_blocks, block_size, segs,
                               seg_indptr, B, Hq, Hkv, D, max_ctx_len, dtype, scale, split_blocks,
-                              out, lse_out, workspace, workspace_bytes, MSA_LAYOUT_NHD, stream);
+                              out, lse_out, workspace, workspace_bytes, MSA_LAYOUT_NHD, dev_error,
+                              stream);
+}
+
+int32_t msa_prefill_chunk_rows(int32_t B, int32_t Hq, int32_t Hkv, int32_t remaining_tokens,
+                               int32_t max_rows, int32_t compute_units) {
+  if (B <= 0 || Hq <= 0 || Hkv <= 0 || Hq % Hkv != 0 || remaining_tokens < 0 || max_rows <= 0)
+    return MSA_ERR_INVALID_ARG;
+  const int G = Hq / Hkv;
+  if (G != 1 && G != 2 && G != 4 && G != 8) return MSA_ERR_UNSUPPORTED;
+  if (remaining_tokens == 0) return 0;
+  return prefill_chunk_rows(B, Hq, Hkv, remaining_tokens, max_rows, compute_units);
 }
 
 // ---------------------------------------------------------------------------

@@ -195,8 +195,12 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
     const msa_segment last = p.segs[s1 - 1];
     A = last.alive_token_start + last.num_tokens;
   }
-  // a plan with more alive tokens than max_ctx_len promised is cut at the grid
-  const int nAB = min((A + kBlk - 1) / kBlk, p.S * T);
+  // a plan with more alive tokens than max_ctx_len promised is cut at the
+  // grid, and the cut is reported (once per sequence)
+  const int nAB_all = (A + kBlk - 1) / kBlk;
+  const int nAB = min(nAB_all, p.S * T);
+  if (nAB_all > nAB && s == 0 && g == 0 && tid == 0 && p.dev_error)
+    atomicOr(p.dev_error, MSA_DEVERR_TRUNCATED);
   const int Sb = (nAB + T - 1) / T;
   if (s >= Sb) {
     if (s == 0 && p.S == 1) {  // no alive token at all: O = 0, LSE = -inf
@@ -534,7 +538,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
     const msa_segment last = p.segs[s1 - 1];
     A = last.alive_token_start + last.num_tokens;
   }
-  const int nAB = min((A + kBlk - 1) / kBlk, p.S * T);
+  const int nAB_all = (A + kBlk - 1) / kBlk;
+  const int nAB = min(nAB_all, p.S * T);
+  if (nAB_all > nAB && s == 0 && g == 0 && tid == 0 && p.dev_error)
+    atomicOr(p.dev_error, MSA_DEVERR_TRUNCATED);
   const int Sb = (nAB + T - 1) / T;
   if (s >= Sb) {
     if (s == 0 && p.S == 1) {  // no alive token at all: O = 0, LSE = -inf
@@ -810,9 +817,13 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   // many-split contexts the VALU kernel's full-row loads measured faster
   // (289 against 298 us on the lognormal batch, 241 against 274 us on the
   // 131k-token layout with 32 query heads).
+  // A caller may also ask for one kernel explicitly (msa_decode_kernel); the
+  // API has checked that the matrix-core kernel exists for the shape.
   bool mfma = false;
   if constexpr (std::is_same<KV, uint16_t>::value && D == kMD && (G == 4 || G == 8))
-    mfma = G == 8 || p.S <= 4;
+    mfma = p.kernel == MSA_DECODE_MATRIX ? true
+         : p.kernel == MSA_DECODE_VECTOR ? false
+         : (G == 8 || p.S <= 4);
   if (mfma) {
     if constexpr (std::is_same<KV, uint16_t>::value && D == kMD && (G == 4 || G == 8))
       hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(kThreads), 0, stream, p);
@@ -877,6 +888,10 @@ SplitPlan decode_split(int32_t B, int32_t Hkv, int32_t max_ctx_len, int32_t bloc
   sp.split_blocks = int32_t(T);
   sp.S = int32_t(nbm == 0 ? 1 : (nbm + T - 1) / T);
   return sp;
+}
+
+bool decode_matrix_supported(msa_dtype dtype, int32_t D, int32_t G) {
+  return dtype == MSA_BF16 && D == kMD && (G == 4 || G == 8);
 }
 
 int32_t decode_max_split_blocks() { return kMaxSplitBlocks; }

@@ -78,7 +78,8 @@ struct PlanParams {
   int32_t cap;
   int32_t* indptr;
   int32_t* dev_error;
-  int32_t* ws;  // [2*B]: per-sequence segment counts, then error flags
+  int32_t* ws;  // [3*B]: per-sequence segment counts, error flags, record offsets
+  int32_t scanned;  // 1: a scan launch wrote the offsets, indptr and dev_error
 };
 
 struct DecodeParams {
@@ -94,6 +95,8 @@ struct DecodeParams {
   float scale_log2;      // softmax scale * log2(e)
   int32_t split_blocks;  // blocks per split
   int32_t S;             // splits per sequence in the grid
+  int32_t kernel;        // msa_decode_kernel: automatic, vector or matrix-core kernel
+  int32_t* dev_error;    // nullable: MSA_DEVERR_TRUNCATED is ORed in
   void* out;
   float* lse;
   float* o_part;  // [B*S, Hq, D]
@@ -115,6 +118,7 @@ struct PrefillParams {
   float scale_log2;
   int32_t split_blocks;  // 0 = no split
   int32_t S;
+  int32_t* dev_error;    // nullable: MSA_DEVERR_TRUNCATED is ORed in
   void* out;
   float* lse;
   float* o_part;  // [B*S, C, Hq, D]
@@ -149,10 +153,15 @@ SplitPlan prefill_split(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t m
                         int32_t block_size, int32_t split_blocks);
 
 bool decode_supported(msa_dtype dtype, int32_t D, int32_t G);
+bool decode_matrix_supported(msa_dtype dtype, int32_t D, int32_t G);
 int32_t decode_max_split_blocks();
 int32_t prefill_max_split_blocks();
 bool prefill_supported(msa_dtype dtype, int32_t D, int32_t G);
+int32_t prefill_chunk_rows(int32_t B, int32_t Hq, int32_t Hkv, int32_t remaining,
+                           int32_t max_rows, int32_t compute_units);
 
+// true if the plan of B sequences takes the three-launch form (scan launch)
+bool plan_uses_scan(int32_t B);
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);

@@ -10,6 +10,11 @@
 //   write  -- prefix of the counts -> seg_indptr; every block that ENDS a
 //             run writes that run's whole record, so each record has exactly
 //             one writer and no cross-workgroup coordination is needed.
+// For small batches each write workgroup sums the counts before its own
+// sequence itself (B reads each, cheaper than a launch).  Above kDirectMaxB
+// sequences that would be B^2 reads in all, so a one-workgroup scan launch
+// between the two computes every record offset, seg_indptr and the error
+// word once, and each write workgroup reads only its own offset.
 // A block l "is alive" iff alive[b][l] != 0 and its physical id is in
 // [0, P); an out-of-range id is reported and the block treated as evicted,
 // so no consumer of the plan can be sent outside the pool.
@@ -19,6 +24,8 @@ namespace msa {
 namespace {
 
 constexpr int kPlanThreads = 256;
+constexpr int kScanThreads = 1024;
+constexpr int kDirectMaxB = 1024;  // above this many sequences the scan launch runs
 constexpr int kPerThread = 4;  // consecutive blocks per thread per chunk
 constexpr int kChunk = kPlanThreads * kPerThread;
 
@@ -179,23 +186,29 @@ __global__ void __launch_bounds__(kPlanThreads) plan_write_kernel(PlanParams p) 
   for (int k = 0; k < kPerThread + 2; ++k)
     r0[k] = load_raw(p, v, threadIdx.x * kPerThread - 1 + k);
 
-  // offset of this sequence's records; workgroup 0 also publishes the totals
-  int before = 0, all = 0, fl = 0;
-  for (int i = threadIdx.x; i < p.B; i += kPlanThreads) {
-    const int c = p.ws[i];
-    if (i < b) before += c;
-    all += c;
-    fl |= p.ws[p.B + i];
-  }
-  const int off = block_sum_int(before, red);
-  const int count_b = p.ws[b];
-  if (threadIdx.x == 0) p.indptr[b + 1] = min(off + count_b, p.cap);
-  if (b == 0) {
-    const int total = block_sum_int(all, red);
-    const int flags = block_or_int(fl, red);
-    if (threadIdx.x == 0) {
-      p.indptr[0] = 0;
-      p.dev_error[0] = flags | (total > p.cap ? MSA_DEVERR_CAPACITY : 0);
+  // offset of this sequence's records: from the scan launch, or summed here
+  // (workgroup 0 then also publishes the totals)
+  int off;
+  if (p.scanned) {
+    off = p.ws[2 * p.B + b];
+  } else {
+    int before = 0, all = 0, fl = 0;
+    for (int i = threadIdx.x; i < p.B; i += kPlanThreads) {
+      const int c = p.ws[i];
+      if (i < b) before += c;
+      all += c;
+      fl |= p.ws[p.B + i];
+    }
+    off = block_sum_int(before, red);
+    const int count_b = p.ws[b];
+    if (threadIdx.x == 0) p.indptr[b + 1] = min(off + count_b, p.cap);
+    if (b == 0) {
+      const int total = block_sum_int(all, red);
+      const int flags = block_or_int(fl, red);
+      if (threadIdx.x == 0) {
+        p.indptr[0] = 0;
+        p.dev_error[0] = flags | (total > p.cap ? MSA_DEVERR_CAPACITY : 0);
+      }
     }
   }
 
@@ -265,12 +278,62 @@ __global__ void __launch_bounds__(kPlanThreads) plan_write_kernel(PlanParams p) 
   }
 }
 
+// One workgroup: exclusive prefix of the B segment counts.  Thread t owns the
+// contiguous sequences [t*per, t*per + per); its local sums are scanned
+// across the workgroup, then it writes its sequences' record offsets
+// (unclamped, for the write pass), seg_indptr (clamped to the capacity) and,
+// from thread 0, the error word.
+__global__ void __launch_bounds__(kScanThreads) plan_scan_kernel(PlanParams p) {
+  __shared__ int wsum[kScanThreads / kWave];
+  __shared__ int wor[kScanThreads / kWave];
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int per = (p.B + kScanThreads - 1) / kScanThreads;
+  const int lo = min(p.B, int(threadIdx.x) * per), hi = min(p.B, lo + per);
+  int sum = 0, fl = 0;
+  for (int i = lo; i < hi; ++i) {
+    sum += p.ws[i];
+    fl |= p.ws[p.B + i];
+  }
+  int inc = sum;
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int t = __shfl_up(inc, o);
+    if (lane >= o) inc += t;
+  }
+  int wfl = fl;
+  for (int o = 32; o > 0; o >>= 1) wfl |= __shfl_xor(wfl, o);
+  if (lane == kWave - 1) wsum[w] = inc;
+  if (lane == 0) wor[w] = wfl;
+  __syncthreads();
+  int run = inc - sum, total = 0, flags = 0;
+  for (int i = 0; i < kScanThreads / kWave; ++i) {
+    if (i < w) run += wsum[i];
+    total += wsum[i];
+    flags |= wor[i];
+  }
+  for (int i = lo; i < hi; ++i) {
+    p.ws[2 * p.B + i] = run;
+    run += p.ws[i];
+    p.indptr[i + 1] = min(run, p.cap);
+  }
+  if (threadIdx.x == 0) {
+    p.indptr[0] = 0;
+    p.dev_error[0] = flags | (total > p.cap ? MSA_DEVERR_CAPACITY : 0);
+  }
+}
+
 }  // namespace
+
+bool plan_uses_scan(int32_t B) { return B > kDirectMaxB; }
 
 hipError_t launch_plan(const PlanParams& p, hipStream_t stream) {
   hipLaunchKernelGGL(plan_count_kernel, dim3(p.B), dim3(kPlanThreads), 0, stream, p);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (p.scanned) {
+    hipLaunchKernelGGL(plan_scan_kernel, dim3(1), dim3(kScanThreads), 0, stream, p);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(plan_write_kernel, dim3(p.B), dim3(kPlanThreads), 0, stream, p);
   return hipGetLastError();
 }

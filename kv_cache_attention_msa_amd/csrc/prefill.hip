@@ -205,14 +205,20 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
     A = last.alive_token_start + last.num_tokens;
   }
   const int T = p.split_blocks;
-  const int nAB = min((A + kBlk - 1) / kBlk, p.S * T);
+  // more alive tokens than max_ctx_len promised: cut at the grid, reported
+  // once per sequence
+  const int nAB_all = (A + kBlk - 1) / kBlk;
+  const int nAB = min(nAB_all, p.S * T);
+  if (nAB_all > nAB && s == 0 && g == 0 && ptile == 0 && tid == 0 && p.dev_error)
+    atomicOr(p.dev_error, MSA_DEVERR_TRUNCATED);
   const int Sb = (nAB + T - 1) / T;
   // a split past this sequence's keys has nothing to contribute (split 0 of
   // a sequence without keys still writes O = 0, LSE = -inf below)
   if (s > 0 && s >= Sb) return;
-  // the sequence's Sb splits share its nAB blocks evenly (each <= T blocks)
-  const int j_begin = int(int64_t(s) * nAB / Sb);
-  const int j_end = int(int64_t(s + 1) * nAB / Sb);
+  // the sequence's Sb splits share its nAB blocks evenly (each <= T blocks);
+  // a sequence without alive keys (Sb = 0) has an empty key range
+  const int j_begin = Sb > 0 ? int(int64_t(s) * nAB / Sb) : 0;
+  const int j_end = Sb > 0 ? int(int64_t(s + 1) * nAB / Sb) : 0;
   const int last_tokens = min(kBlk, A - kBlk * (nAB - 1));
 
   // ---- Q of this lane's row into MFMA B-operand registers ----------------
@@ -673,6 +679,25 @@ SplitPlan prefill_split(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t m
   sp.S = int32_t(nbm == 0 ? 1 : (nbm + sp.split_blocks - 1) / sp.split_blocks);
   if (sp.S < 1) sp.S = 1;
   return sp;
+}
+
+int32_t prefill_chunk_rows(int32_t B, int32_t Hq, int32_t Hkv, int32_t remaining,
+                           int32_t max_rows, int32_t compute_units) {
+  const int G = Hq / Hkv;
+  const int64_t npos = 256 / G;  // query positions per workgroup
+  const int64_t cus = compute_units > 0 ? compute_units : 256;
+  const int64_t cap = min(int64_t(remaining), int64_t(max_rows));
+  // smallest whole number of position tiles whose (tile, KV head, sequence)
+  // workgroups cover every compute unit at one workgroup per unit; below it
+  // the key stream has to be split (partials + merge), above it throughput
+  // is flat while every chunk waits longer
+  const int64_t per_tile = int64_t(Hkv) * B;
+  const int64_t tiles = (cus + per_tile - 1) / per_tile;
+  int64_t C = tiles * npos;
+  if (C >= cap) return int32_t(cap);
+  // a tail shorter than one position tile rides along with this chunk
+  if (remaining - C < npos && remaining <= max_rows) return remaining;
+  return int32_t(C);
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {

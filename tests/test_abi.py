@@ -36,7 +36,7 @@ def test_every_declared_symbol_is_exported():
 
 def test_version_and_strings():
     lib = _lib.load()
-    assert lib.msa_version() == 1
+    assert lib.msa_version() == 2
     assert b"INVALID" in lib.msa_status_string(-1)
 
 
@@ -63,11 +63,22 @@ def test_plan_rejects_bad_args():
 def _decode(lib, **kw):
     a = dict(q=FAKE, k=FAKE, v=FAKE, P=100, bs=16, segs=FAKE, indptr=FAKE, B=2, Hq=32, Hkv=8, D=128,
              maxctx=4096, dtype=_lib.MSA_BF16, scale=0.0, split=0, out=FAKE, lse=NULL, ws=FAKE,
-             wsb=1 << 30, stream=NULL)
+             wsb=1 << 30, err=NULL, stream=NULL)
     a.update(kw)
     return lib.msa_decode(a["q"], a["k"], a["v"], a["P"], a["bs"], a["segs"], a["indptr"], a["B"],
                           a["Hq"], a["Hkv"], a["D"], a["maxctx"], a["dtype"], a["scale"], a["split"],
-                          a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+                          a["out"], a["lse"], a["ws"], a["wsb"], a["err"], a["stream"])
+
+
+def _decode_ex(lib, layout=_lib.MSA_LAYOUT_NHD, kernel=_lib.MSA_DECODE_AUTO, **kw):
+    a = dict(q=FAKE, k=FAKE, v=FAKE, P=100, bs=16, segs=FAKE, indptr=FAKE, B=2, Hq=32, Hkv=8, D=128,
+             maxctx=4096, dtype=_lib.MSA_BF16, scale=0.0, split=0, out=FAKE, lse=NULL, ws=FAKE,
+             wsb=1 << 30, err=NULL, stream=NULL)
+    a.update(kw)
+    return lib.msa_decode_ex(a["q"], a["k"], a["v"], a["P"], a["bs"], a["segs"], a["indptr"],
+                             a["B"], a["Hq"], a["Hkv"], a["D"], a["maxctx"], a["dtype"], a["scale"],
+                             a["split"], a["out"], a["lse"], a["ws"], a["wsb"], layout, kernel,
+                             a["err"], a["stream"])
 
 
 def test_decode_rejects_bad_args():
@@ -93,15 +104,28 @@ def test_layout_entry_points_reject_an_unknown_layout():
     lib = _lib.load()
     ws = 1 << 30
     # everything else valid: only the layout is wrong
-    assert lib.msa_decode_ex(FAKE, FAKE, FAKE, 100, 16, FAKE, FAKE, 2, 32, 8, 128, 4096,
-                             _lib.MSA_BF16, 0.0, 0, FAKE, NULL, FAKE, ws, 2, NULL) == _lib.MSA_ERR_INVALID_ARG
+    assert _decode_ex(lib, layout=2) == _lib.MSA_ERR_INVALID_ARG
     assert lib.msa_prefill_chunk_ex(FAKE, 512, FAKE, FAKE, FAKE, 100, 16, FAKE, FAKE, 4, 32, 8,
                                     128, 8704, _lib.MSA_BF16, 0.0, 0, FAKE, NULL, FAKE, ws, -1,
-                                    None) == _lib.MSA_ERR_INVALID_ARG
+                                    NULL, None) == _lib.MSA_ERR_INVALID_ARG
     # argument errors are still found first with a valid layout
-    assert lib.msa_decode_ex(NULL, FAKE, FAKE, 100, 16, FAKE, FAKE, 2, 32, 8, 128, 4096,
-                             _lib.MSA_BF16, 0.0, 0, FAKE, NULL, FAKE, ws, _lib.MSA_LAYOUT_HND,
-                             None) == _lib.MSA_ERR_INVALID_ARG
+    assert _decode_ex(lib, layout=_lib.MSA_LAYOUT_HND, q=NULL) == _lib.MSA_ERR_INVALID_ARG
+
+
+def test_decode_kernel_choice_is_validated():
+    """msa_decode_ex's kernel argument: unknown values are argument errors;
+    the matrix-core kernel exists only for bf16 with D 128 and 4 or 8 query
+    heads per KV head; the vector kernel for every supported shape."""
+    lib = _lib.load()
+    assert _decode_ex(lib, kernel=3) == _lib.MSA_ERR_INVALID_ARG
+    assert _decode_ex(lib, kernel=-1) == _lib.MSA_ERR_INVALID_ARG
+    for hq, d, dt in ((16, 128, _lib.MSA_BF16), (8, 128, _lib.MSA_BF16), (32, 64, _lib.MSA_BF16),
+                      (32, 64, _lib.MSA_F32)):
+        assert _decode_ex(lib, kernel=_lib.MSA_DECODE_MATRIX, Hq=hq, D=d,
+                          dtype=dt) == _lib.MSA_ERR_UNSUPPORTED, (hq, d, dt)
+    # the shape checks still come first
+    assert _decode_ex(lib, kernel=_lib.MSA_DECODE_VECTOR, Hq=24) == _lib.MSA_ERR_UNSUPPORTED
+    assert _decode_ex(lib, kernel=_lib.MSA_DECODE_MATRIX, B=0) == _lib.MSA_ERR_INVALID_ARG
 
 
 def test_decode_workspace_arithmetic():
@@ -177,11 +201,12 @@ def test_gather_rejects_bad_args():
 def _prefill(lib, **kw):
     a = dict(q=FAKE, C=512, qpos=FAKE, k=FAKE, v=FAKE, P=100, bs=16, segs=FAKE, indptr=FAKE, B=4,
              Hq=32, Hkv=8, D=128, maxctx=8704, dtype=_lib.MSA_BF16, scale=0.0, split=0, out=FAKE,
-             lse=NULL, ws=FAKE, wsb=1 << 30, stream=NULL)
+             lse=NULL, ws=FAKE, wsb=1 << 30, err=NULL, stream=NULL)
     a.update(kw)
     return lib.msa_prefill_chunk(a["q"], a["C"], a["qpos"], a["k"], a["v"], a["P"], a["bs"], a["segs"],
                                  a["indptr"], a["B"], a["Hq"], a["Hkv"], a["D"], a["maxctx"], a["dtype"],
-                                 a["scale"], a["split"], a["out"], a["lse"], a["ws"], a["wsb"], a["stream"])
+                                 a["scale"], a["split"], a["out"], a["lse"], a["ws"], a["wsb"], a["err"],
+                                 a["stream"])
 
 
 def test_prefill_rejects_bad_args():

@@ -26,13 +26,15 @@ DEV = "cuda"
 TOL = {"f32": 1e-5, "bf16": 2e-2}
 
 
-def run_decode(w, split_blocks=0, d=None):
+def run_decode(w, split_blocks=0, d=None, kernel="auto"):
     d = d or to_device(w, DEV)
     segs, indptr, err = msa.msa_plan_segments(d["block_table"], d["alive"], d["ctx_len"],
                                               w.block_size, w.num_phys_blocks)
+    # the plan's error word also collects the decode's (a true max_ctx_len:
+    # no truncation may be reported)
     out, lse = msa.msa_decode(d["q"], d["k_pool"], d["v_pool"], segs, indptr,
                               max_ctx_len=int(w.ctx_len.max()), scale=w.scale,
-                              split_blocks=split_blocks)
+                              split_blocks=split_blocks, kernel=kernel, dev_error=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     return from_device(out), lse.cpu().numpy().astype(np.float64)
@@ -297,10 +299,13 @@ def test_decode_understated_max_ctx_len_truncates_safely(cfg):
     d = to_device(w, DEV)
     segs, indptr, err = msa.msa_plan_segments(d["block_table"], d["alive"], d["ctx_len"],
                                               w.block_size, w.num_phys_blocks)
-    out, lse = msa.msa_decode(d["q"], d["k_pool"], d["v_pool"], segs, indptr,
-                              max_ctx_len=max_ctx, scale=w.scale, split_blocks=T)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
+    out, lse = msa.msa_decode(d["q"], d["k_pool"], d["v_pool"], segs, indptr,
+                              max_ctx_len=max_ctx, scale=w.scale, split_blocks=T, dev_error=err)
+    torch.cuda.synchronize()
+    # the cut is reported, and only the cut
+    assert int(err.item()) == msa.MSA_DEVERR_TRUNCATED
     kept = w.alive.copy()
     cut_any = False
     for b in range(w.B):
@@ -315,3 +320,35 @@ def test_decode_understated_max_ctx_len_truncates_safely(cfg):
     tol = TOL[w.dtype]
     assert np.max(np.abs(from_device(out) - Or)) <= tol
     assert np.max(np.abs(lse.cpu().numpy().astype(np.float64) - Lr)) <= tol
+
+
+@pytest.mark.parametrize("cfg,Hq,split_blocks", [(2, 32, 0), (2, 64, 0), (2, 32, 16), (5, 64, 0),
+                                                 (5, 32, 0), (4, 32, 0)])
+def test_decode_vector_and_matrix_kernels(cfg, Hq, split_blocks):
+    """msa_decode_ex with the kernel chosen explicitly: the vector-ALU kernel
+    (fp32 softmax weights) and the matrix-core kernel (weights rounded to
+    bf16 for P x V) on the same small batches, 4 and 8 query heads per KV
+    head, with and without splits.  Both match the oracle within the bf16
+    tolerance, and agree with each other within it too."""
+    w = make_workload(cfg, seed=8, size="small", Hq=Hq)
+    d = to_device(w, DEV)
+    res = {}
+    for kern in ("vector", "matrix"):
+        O, L = run_decode(w, split_blocks, d, kernel=kern)
+        res[kern] = check(w, O, L) + (O, L)
+    assert np.max(np.abs(res["vector"][2] - res["matrix"][2])) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("cfg", [2, 5])
+def test_decode_vector_and_matrix_kernels_full(cfg):
+    """Full-size headline batch (4 query heads per KV head) and the
+    131k-token batch (8 per KV head): each kernel against the oracle on
+    sampled (sequence, head) pairs."""
+    w = make_workload(cfg, seed=0)
+    d = to_device(w, DEV)
+    rng = np.random.default_rng(20 + cfg)
+    seqs = sorted(rng.choice(w.B, size=min(w.B, 3), replace=False).tolist())
+    heads = sorted(rng.choice(w.Hq, size=4, replace=False).tolist())
+    for kern in ("vector", "matrix"):
+        O, L = run_decode(w, 0, d, kernel=kern)
+        check(w, O, L, seqs=seqs, heads=heads)

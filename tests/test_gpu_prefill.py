@@ -31,9 +31,10 @@ def run_prefill(w, split_blocks=0, q_pos0=None):
         d["q_pos0"] = tensor(np.asarray(q_pos0, dtype=np.int32), DEV)
     segs, indptr, err = msa.msa_plan_segments(d["block_table"], d["alive"], d["ctx_len"],
                                               w.block_size, w.num_phys_blocks)
+    # the plan's error word also collects the prefill's (none expected)
     out, lse = msa.msa_prefill_chunk(d["q"], d["q_pos0"], d["k_pool"], d["v_pool"], segs, indptr,
-                                     max_ctx_len=int(w.ctx_len.max()), scale=w.scale,
-                                     split_blocks=split_blocks)
+                                     max_ctx_len=max(1, int(w.ctx_len.max())), scale=w.scale,
+                                     split_blocks=split_blocks, dev_error=err)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     return from_device(out), lse.cpu().numpy().astype(np.float64)
@@ -242,10 +243,14 @@ def test_prefill_understated_max_ctx_len_truncates_safely():
     d = to_device(w, DEV)
     segs, indptr, err = msa.msa_plan_segments(d["block_table"], d["alive"], d["ctx_len"],
                                               w.block_size, w.num_phys_blocks)
-    out, lse = msa.msa_prefill_chunk(d["q"], d["q_pos0"], d["k_pool"], d["v_pool"], segs, indptr,
-                                     max_ctx_len=max_ctx, scale=w.scale, split_blocks=T)
     torch.cuda.synchronize()
     assert int(err.item()) == 0
+    out, lse = msa.msa_prefill_chunk(d["q"], d["q_pos0"], d["k_pool"], d["v_pool"], segs, indptr,
+                                     max_ctx_len=max_ctx, scale=w.scale, split_blocks=T,
+                                     dev_error=err)
+    torch.cuda.synchronize()
+    # the cut is reported, and only the cut
+    assert int(err.item()) == msa.MSA_DEVERR_TRUNCATED
     kept = w.alive.copy()
     for b in range(w.B):
         nb = -(-int(w.ctx_len[b]) // w.block_size)
@@ -257,3 +262,36 @@ def test_prefill_understated_max_ctx_len_truncates_safely():
                                 w.block_size, w.scale)
     assert np.max(np.abs(from_device(out) - Or)) <= TOL
     assert np.max(np.abs(lse.cpu().numpy().astype(np.float64) - Lr)) <= TOL
+
+
+@pytest.mark.parametrize("split_blocks", [0, 16])
+def test_prefill_sequences_without_keys(split_blocks):
+    """A sequence whose every block was evicted (the chunk's own too) and a
+    sequence with ctx_len 0 (no block at all) beside ordinary ones: their
+    rows see no key and get O = 0, LSE = -inf; the other sequences match the
+    oracle, with and without a forced key split."""
+    w = make_workload(3, seed=9, size="small", B=4, C=48)
+    w.alive[1, :] = 0
+    w.ctx_len[2] = 0
+    q_pos0 = w.q_pos0.copy()
+    q_pos0[2] = 0
+    O, L = run_prefill(w, split_blocks, q_pos0=q_pos0)
+    for b in (1, 2):
+        assert np.all(O[b] == 0) and np.all(np.isneginf(L[b]))
+    check(w, O, L, q_pos0=q_pos0)
+
+
+@pytest.mark.parametrize("C", [128, 256, 1024, 2048])
+def test_prefill_chunk_sizes_full_sampled(C):
+    """The chunk sizes of the chunk-size curve (prefill workload with C
+    varied, 8192 cached tokens): C 128 and 256 split the key stream to fill
+    the chip, 1024 and 2048 run several position tiles per (KV head,
+    sequence).  Sampled rows (both ends, tile edges) and heads against the
+    oracle."""
+    w = make_workload(3, seed=0, C=C)
+    O, L = run_prefill(w)
+    rng = np.random.default_rng(C)
+    edges = [0, 31, 32, 63, 64, C // 2, C - 1]
+    rows = np.unique(np.concatenate([edges, rng.choice(C, 6, replace=False)]))
+    heads = sorted(rng.choice(w.Hq, size=3, replace=False).tolist())
+    check(w, O, L, seqs=[0, 3], heads=heads, rows=rows)
