@@ -7,12 +7,21 @@ plan (msa_plan_segments) followed by decode attention with its split-K merge
 heads, head_dim 128, 4096-token contexts, block size 16, 20% of blocks evicted
 in geometric runs).  Inputs are resident in HBM before the timed region.
 
-Printed: ONE JSON line with the decode KV GB/s (value), tokens/s, % of HBM
-peak, a roofline object for the dominant call (measured live with HIP events
-on the launch stream), the fp64 oracle timed on the host cores
-(cpu_baseline), cold-cache timing, and the chunked-prefill TFLOP/s / % of bf16
-MFMA peak on the prefill workload (bf16, batch 4, chunk 512 over 8192 cached
-tokens, 15% evicted).
+Timing is cold by default: before every timed step or call a 1 GiB read
+evicts L2 and the 256 MB Infinity Cache (outside the timed region), so each
+call streams its K/V from HBM, as it does in a model where other layers run
+between two attention calls.  Back-to-back (warm) figures are reported beside
+the cold ones.  GPU times come from HIP events on the launch stream.
+
+Printed: ONE JSON line with the decode KV GB/s (value, cold), tokens/s, % of
+HBM peak, a roofline object for the dominant call, the fp64 oracle timed on
+the host cores (cpu_baseline), and legs for the other workloads: the small
+fp32 decode batch, the lognormal shared-prefix batch and the 131k-token
+fragmented batch (each with roofline and oracle baseline), the chunked
+prefill (TFLOP/s, % of the bf16 MFMA peak) and the recompute chunk, the
+gather-then-attend detour, head-major pool blocks, the vector against the
+matrix-core decode kernel, kernel-aware against hit-only eviction, and the
+chunk-size curve with the adaptive chooser's pick.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
 """
@@ -37,39 +46,46 @@ COUNTERS = os.path.join(ROOT, "profiles", "decode_cfg2_counters.json")
 DECODE_SOURCES = ["decode.hip", "merge.hip", "msa_internal.h"]
 PF_COUNTERS = os.path.join(ROOT, "profiles", "prefill_cfg3_counters.json")
 PREFILL_SOURCES = ["prefill.hip", "msa_internal.h"]
+FLUSH_BYTES = 1 << 30  # > L2 + Infinity Cache (256 MB)
+
+ONLY = ("decode", "decode-warm", "decode4", "decode5", "prefill", "kernels")
 
 
-def parse():
+def parse(argv=None):
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=200)
-    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--seed", type=int, default=0)
     ap.add_argument("--split-blocks", type=int, default=0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--no-cold", action="store_true")
     ap.add_argument("--no-gather", action="store_true",
                     help="skip the gather-then-attend baseline leg")
     ap.add_argument("--no-recompute", action="store_true",
                     help="skip the recompute (middle chunk) prefill leg")
-    ap.add_argument("--latency-model", action="store_true",
-                    help="fit the decode latency model used by the eviction scorer")
-    ap.add_argument("--chunk-sweep", action="store_true",
-                    help="also time the prefill workload at chunk sizes 128..2048")
-    ap.add_argument("--more-decode", action="store_true",
-                    help="also time msa_decode on the lognormal shared-prefix batch and the "
-                         "131k-token fragmented batch")
-    ap.add_argument("--copy-calibration", action="store_true",
-                    help="also run a plain 256 MiB device copy (for counter calibration)")
+    ap.add_argument("--no-more-decode", action="store_true",
+                    help="skip the small fp32, lognormal and 131k-token decode legs")
+    ap.add_argument("--no-kernels", action="store_true",
+                    help="skip the vector against matrix-core decode kernel leg")
+    ap.add_argument("--no-eviction", action="store_true",
+                    help="skip the kernel-aware against hit-only eviction leg")
+    ap.add_argument("--no-chunk-sweep", action="store_true",
+                    help="skip the prefill chunk-size curve")
     ap.add_argument("--no-layout", action="store_true",
                     help="skip the head-major pool layout decode leg")
+    ap.add_argument("--latency-model", action="store_true",
+                    help="also fit the decode latency model over new batches of varied context "
+                         "length and alive-run length")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 256 MiB device copy (for counter calibration)")
     ap.add_argument("--kv-layout", choices=["nhd", "hnd"], default="nhd",
                     help="pool block layout of the headline decode leg: token-major "
                          "[P, 16, Hkv, D] (default) or head-major [P, Hkv, 16, D]")
-    ap.add_argument("--only", choices=["decode", "prefill"], default=None,
-                    help="time only one call (for profiler runs)")
-    return ap.parse_args()
+    ap.add_argument("--only", choices=ONLY, default=None,
+                    help="time only one call, cold (decode, decode4, decode5, prefill, kernels) "
+                         "or back to back (decode-warm), for profiler runs")
+    return ap.parse_args(argv)
 
 
 def sources_sha(names):
@@ -79,6 +95,10 @@ def sources_sha(names):
             h.update(f.read())
     return h.hexdigest()[:16]
 
+
+# --------------------------------------------------------------------------
+# algorithmic work (host bookkeeping over the generated inputs)
+# --------------------------------------------------------------------------
 
 def alive_tokens_per_seq(w):
     """Number of alive tokens per sequence (input bookkeeping for byte counts)."""
@@ -90,6 +110,21 @@ def alive_tokens_per_seq(w):
         tok = np.minimum(w.block_size, n - w.block_size * np.arange(nb))
         out.append(int((tok * (w.alive[b, :nb] != 0)).sum()))
     return out
+
+
+def esize(w):
+    return 2 if w.dtype == "bf16" else 4
+
+
+def decode_bytes(w, seqs=None):
+    """Algorithmic bytes of one decode call: the alive K and V rows of every
+    sequence (a shared block counted once per sequence that reads it) plus Q,
+    O and LSE.  seqs restricts the count to a subset of sequences."""
+    per = alive_tokens_per_seq(w)
+    sel = range(w.B) if seqs is None else seqs
+    kv = sum(per[b] for b in sel) * w.Hkv * w.D * 2 * esize(w)
+    qo = len(list(sel)) * w.Hq * (2 * w.D * esize(w) + 4)
+    return kv + qo
 
 
 def unique_alive_bytes(w):
@@ -104,7 +139,7 @@ def unique_alive_bytes(w):
             t = min(w.block_size, n - w.block_size * int(l))
             ph = int(w.block_table[b, l])
             tok[ph] = max(tok.get(ph, 0), t)
-    return sum(tok.values()) * w.Hkv * w.D * (2 if w.dtype == "bf16" else 4) * 2
+    return sum(tok.values()) * w.Hkv * w.D * esize(w) * 2
 
 
 def visible_pairs(w, rows=None):
@@ -123,23 +158,29 @@ def visible_pairs(w, rows=None):
     return tot
 
 
+# --------------------------------------------------------------------------
+# pre-marshalled library calls
+# --------------------------------------------------------------------------
+
 class Prepared:
     """Device buffers and pre-marshalled C-ABI arguments for one workload, so
     the timed loops make the library calls with no allocation and no
-    per-call argument building."""
+    per-call argument building.  The attention call ORs its truncation bit
+    into the plan's error word."""
 
-    def __init__(self, w, split_blocks=0, kv_layout=0):
+    def __init__(self, w, split_blocks=0, kv_layout=0, kernel=0, d=None):
         import ctypes
         import torch
         from kv_cache_attention_msa_amd import _lib
         from workloads.device import to_device
         self.lib = _lib.load()
         self.w = w
-        d = to_device(w, "cuda")
-        if kv_layout == _lib.MSA_LAYOUT_HND:
-            # the same values in head-major blocks [P, Hkv, 16, D]
-            d["k_pool"] = d["k_pool"].permute(0, 2, 1, 3).contiguous()
-            d["v_pool"] = d["v_pool"].permute(0, 2, 1, 3).contiguous()
+        if d is None:
+            d = to_device(w, "cuda")
+            if kv_layout == _lib.MSA_LAYOUT_HND:
+                # the same values in head-major blocks [P, Hkv, 16, D]
+                d["k_pool"] = d["k_pool"].permute(0, 2, 1, 3).contiguous()
+                d["v_pool"] = d["v_pool"].permute(0, 2, 1, 3).contiguous()
         self.d = d
         dev = d["q"].device
         B, mb = w.block_table.shape
@@ -165,23 +206,22 @@ class Prepared:
                           B, mb, w.block_size, w.num_phys_blocks, P(self.segs.data_ptr()), self.cap,
                           P(self.indptr.data_ptr()), P(self.err.data_ptr()), P(self.pws.data_ptr()),
                           self.pws.numel(), s)
-        # the default token-major layout goes through msa_decode /
-        # msa_prefill_chunk, any other through their *_ex forms
-        lay = () if kv_layout == _lib.MSA_LAYOUT_NHD else (kv_layout,)
+        errp = P(self.err.data_ptr())
         if w.kind == "decode":
-            self.attn = self.lib.msa_decode_ex if lay else self.lib.msa_decode
+            self.attn = self.lib.msa_decode_ex
             self.attn_args = (P(d["q"].data_ptr()), P(d["k_pool"].data_ptr()), P(d["v_pool"].data_ptr()),
                               w.num_phys_blocks, w.block_size, P(self.segs.data_ptr()), P(self.indptr.data_ptr()),
                               B, w.Hq, w.Hkv, w.D, self.max_ctx, dt, float(w.scale), split_blocks,
                               P(self.out.data_ptr()), P(self.lse.data_ptr()), P(self.ws.data_ptr()),
-                              self.ws.numel()) + lay + (s,)
+                              self.ws.numel(), kv_layout, kernel, errp, s)
         else:
-            self.attn = self.lib.msa_prefill_chunk_ex if lay else self.lib.msa_prefill_chunk
+            self.attn = self.lib.msa_prefill_chunk_ex
             self.attn_args = (P(d["q"].data_ptr()), w.C, P(d["q_pos0"].data_ptr()), P(d["k_pool"].data_ptr()),
                               P(d["v_pool"].data_ptr()), w.num_phys_blocks, w.block_size,
                               P(self.segs.data_ptr()), P(self.indptr.data_ptr()), B, w.Hq, w.Hkv, w.D,
                               self.max_ctx, dt, float(w.scale), split_blocks, P(self.out.data_ptr()),
-                              P(self.lse.data_ptr()), P(self.ws.data_ptr()), self.ws.numel()) + lay + (s,)
+                              P(self.lse.data_ptr()), P(self.ws.data_ptr()), self.ws.numel(), kv_layout,
+                              errp, s)
 
     def plan(self):
         st = self.lib.msa_plan_segments(*self.plan_args)
@@ -196,6 +236,13 @@ class Prepared:
     def step(self):
         self.plan()
         self.attention()
+
+    def check_error(self):
+        import torch
+        torch.cuda.synchronize()
+        e = int(self.err.item())
+        if e != 0:
+            raise RuntimeError(f"device error word {e}")
 
 
 class GatherBaseline:
@@ -212,7 +259,7 @@ class GatherBaseline:
         s = P(prep.stream.cuda_stream)
         bps = -(-prep.max_ctx // w.block_size)
         dev = d["q"].device
-        shape = (w.B * bps, w.block_size, w.Hkv, w.D)
+        shape = (w.B * bps,) + tuple(d["k_pool"].shape[1:])
         self.dk = torch.empty(shape, dtype=d["k_pool"].dtype, device=dev)
         self.dv = torch.empty_like(self.dk)
         self.dsegs = torch.empty((w.B, 6), dtype=torch.int32, device=dev)
@@ -226,7 +273,7 @@ class GatherBaseline:
         a[1], a[2], a[3] = P(self.dk.data_ptr()), P(self.dv.data_ptr()), w.B * bps
         a[5], a[6] = P(self.dsegs.data_ptr()), P(self.dind.data_ptr())
         self.attn_args = tuple(a)
-        self.attn = prep.attn  # msa_decode, or msa_decode_ex with the layout argument
+        self.attn = prep.attn
 
     def gather(self):
         st = self.lib.msa_gather_alive(*self.gather_args)
@@ -243,9 +290,13 @@ class GatherBaseline:
         self.attention()
 
 
+# --------------------------------------------------------------------------
+# timing
+# --------------------------------------------------------------------------
+
 def time_calls(fn, n, stream):
-    """Average duration of fn() over n back-to-back calls, from HIP events
-    recorded on the launch stream."""
+    """Average duration (s) of fn() over n back-to-back (warm) calls, from HIP
+    events recorded on the launch stream."""
     import torch
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
@@ -254,33 +305,30 @@ def time_calls(fn, n, stream):
         fn()
     e1.record(stream)
     e1.synchronize()
-    return e0.elapsed_time(e1) / n * 1e-3  # seconds
+    return e0.elapsed_time(e1) / n * 1e-3
 
 
-def call_percentiles(fn, n, stream):
-    """p10 / median / p90 of single-call durations (us), each call between
-    its own pair of HIP events on the launch stream, calls back to back."""
-    import torch
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(n)]
-    for a, b in ev:
-        a.record(stream)
-        fn()
-        b.record(stream)
-    ev[-1][1].synchronize()
-    us = sorted(a.elapsed_time(b) * 1e3 for a, b in ev)
-    q = lambda f: us[min(n - 1, int(round(f * (n - 1))))]
-    return {"p10": round(q(0.1), 3), "p50": round(q(0.5), 3), "p90": round(q(0.9), 3), "calls": n}
+class Flush:
+    """A 1 GiB read that evicts L2 and the Infinity Cache.  A read leaves
+    clean lines, so the timed call after it pays no write-back."""
+
+    def __init__(self):
+        import torch
+        self.buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.float32, device="cuda")
+        self.sink = torch.empty((), dtype=torch.float32, device="cuda")
+
+    def __call__(self):
+        import torch
+        torch.sum(self.buf, dim=0, out=self.sink)
 
 
-def time_cold(fn, n, stream, flush):
-    """Median duration of fn() when a 1 GiB read evicts L2 and the Infinity
-    Cache before every call (the read is outside the events; a read leaves
-    clean lines, so the call pays no write-back of the flush)."""
+def cold_times(fn, n, stream, flush):
+    """Durations (s) of n calls of fn(), each after a cache flush (outside the
+    events) and timed alone between its own pair of HIP events."""
     import torch
     ts = []
-    sink = torch.empty((), dtype=torch.float32, device=flush.device)
     for _ in range(n):
-        torch.sum(flush, dim=0, out=sink)
+        flush()
         e0 = torch.cuda.Event(enable_timing=True)
         e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
@@ -288,17 +336,15 @@ def time_cold(fn, n, stream, flush):
         e1.record(stream)
         e1.synchronize()
         ts.append(e0.elapsed_time(e1) * 1e-3)
-    return statistics.median(ts)
+    return ts
 
 
-def realised(w, prep):
-    """What the seeded draw actually produced: eviction fraction, segment
-    count (from the device plan) and context lengths."""
-    import numpy as np
-    ctx = np.asarray(w.ctx_len)
-    return {"evicted_fraction": round(float(w.meta["evicted_fraction"]), 4),
-            "segments": int(prep.indptr[-1].item()),
-            "ctx_len": {"min": int(ctx.min()), "median": int(np.median(ctx)), "max": int(ctx.max())}}
+def dist_us(ts):
+    s = sorted(ts)
+    n = len(s)
+    q = lambda f: s[min(n - 1, int(round(f * (n - 1))))] * 1e6
+    return {"mean": round(statistics.fmean(s) * 1e6, 3), "p10": round(q(0.1), 3),
+            "p50": round(q(0.5), 3), "p90": round(q(0.9), 3), "calls": n}
 
 
 def warm_for(fn, seconds=0.25):
@@ -312,144 +358,357 @@ def warm_for(fn, seconds=0.25):
         torch.cuda.synchronize()
 
 
-def prefill_leg(w, n, warm):
-    """Time msa_prefill_chunk (plus its merge when split) on workload w."""
+def realised(w, prep):
+    """What the seeded draw actually produced: eviction fraction, segment
+    count (from the device plan) and context lengths."""
+    import numpy as np
+    ctx = np.asarray(w.ctx_len)
+    return {"evicted_fraction": round(float(w.meta.get("evicted_fraction", 0.0)), 4),
+            "segments": int(prep.indptr[-1].item()),
+            "ctx_len": {"min": int(ctx.min()), "median": int(np.median(ctx)), "max": int(ctx.max())}}
+
+
+def counter_traffic(path, names, **want):
+    """HBM bytes per call from a committed counter summary, if it was taken on
+    the current kernel sources and the same launch configuration."""
+    if not os.path.exists(path):
+        return None
+    c = json.load(open(path))
+    if c.get("sources_sha") != sources_sha(names):
+        return None
+    for k, v in want.items():
+        if c.get(k, {"split_blocks": 0, "kv_layout": "nhd"}.get(k)) != v:
+            return None
+    return c.get("bytes_per_call")
+
+
+# --------------------------------------------------------------------------
+# the oracle on the host cores (CPU baseline)
+# --------------------------------------------------------------------------
+
+def host_cores():
+    return len(os.sched_getaffinity(0))
+
+
+def _oracle_rate(fn, work, budget_s, max_reps, threads):
+    """Run fn() (one oracle pass over `work` units) repeatedly for about
+    budget_s with the BLAS pool limited to `threads`; returns (units/s,
+    passes, seconds, threads the BLAS pool reported)."""
+    from threadpoolctl import threadpool_info, threadpool_limits
+    with threadpool_limits(limits=threads):
+        used = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+        reps, t0 = 0, time.perf_counter()
+        while reps < max_reps:
+            fn()
+            reps += 1
+            if time.perf_counter() - t0 >= budget_s:
+                break
+        dt = time.perf_counter() - t0
+    return work * reps / dt, reps, dt, used
+
+
+def oracle_baseline(fn, work, unit, scale, sample, budget_s=6.0, max_reps=20, single=True,
+                    single_budget_s=3.0):
+    """CPU-baseline record: the fp64 oracle as it stands, on every core of
+    this process's affinity mask, and (single=True) on one thread."""
+    cores = host_cores()
+    rate, reps, dt, used = _oracle_rate(fn, work, budget_s, max_reps, cores)
+    rec = {"value": round(rate / scale, 6), "unit": unit, "cores": used, "kind": "oracle",
+           "sample": f"{sample}; {reps} passes in {dt:.1f} s, BLAS threads {used} of {cores} host "
+                     f"cores (the gather loops are single-threaded)",
+           "seconds_per_pass": round(dt / reps, 4), "host_cores": cores}
+    if single:
+        r1, reps1, dt1, _ = _oracle_rate(fn, work, single_budget_s, max_reps, 1)
+        rec["single_thread"] = {"value": round(r1 / scale, 6), "unit": unit, "cores": 1,
+                                "seconds_per_pass": round(dt1 / reps1, 4), "passes": reps1}
+    return rec
+
+
+def decode_cpu_baseline(w, seqs=None, budget_s=6.0, single=True, label=""):
+    """The oracle's decode (decode_ref) on the whole batch or on the given
+    sequences (all heads), as GB/s of algorithmic bytes."""
+    import oracle
+    work = decode_bytes(w, seqs)
+    which = "all sequences" if seqs is None else f"sequences {list(seqs)}"
+    fn = lambda: oracle.decode_ref(w.q, w.k_pool, w.v_pool, w.block_table, w.alive, w.ctx_len,
+                                   w.block_size, w.scale, seqs=seqs)
+    return oracle_baseline(fn, work, "GB/s", 1e9,
+                           f"fp64 numpy oracle (decode_ref) on {label} {which} x {w.Hq} heads "
+                           f"({work / 1e6:.1f} MB of alive K/V + Q/O)", budget_s=budget_s,
+                           single=single)
+
+
+def prefill_cpu_baseline(w, row_step=16, budget_s=6.0, max_reps=5, single=True):
+    """The oracle's prefill (prefill_ref) on a row sample of the chunk: every
+    row_step-th chunk row of every sequence and head, over all the keys each
+    row sees."""
+    import numpy as np
+    import oracle
+    rows = np.arange(0, w.C, row_step)
+    flops = 4.0 * w.D * w.Hq * visible_pairs(w, rows)
+    fn = lambda: oracle.prefill_ref(w.q, w.q_pos0, w.k_pool, w.v_pool, w.block_table, w.alive,
+                                    w.ctx_len, w.block_size, w.scale, rows=rows)
+    return oracle_baseline(fn, flops, "TFLOP/s", 1e12,
+                           f"fp64 numpy oracle (prefill_ref) on every {row_step}th chunk row "
+                           f"({len(rows)} of {w.C}) of all {w.B} sequences x {w.Hq} heads, visible "
+                           f"keys only", budget_s=budget_s, max_reps=max_reps, single=single)
+
+
+# --------------------------------------------------------------------------
+# legs
+# --------------------------------------------------------------------------
+
+def decode_roofline(alg_bytes, cold_mean_s, warm_s, traffic=None, kernel="msa_decode"):
+    a = alg_bytes / cold_mean_s / 1e9
+    return {"bound": "hbm", "achieved": round(a, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_unit": "bytes per call",
+            "kernel": kernel, "timing": "cold (1 GiB read flush before each call), mean of the calls",
+            "algorithmic_bytes_per_call": int(alg_bytes), "us_per_call": round(cold_mean_s * 1e6, 3),
+            "warm": {"achieved": round(alg_bytes / warm_s / 1e9, 2),
+                     "frac": round(alg_bytes / warm_s / 1e9 / HBM_PEAK_GBS, 4),
+                     "us_per_call": round(warm_s * 1e6, 3)}}
+
+
+def decode_leg(w, n, flush, split_blocks=0, kv_layout=0, kernel=0, unique=False, d=None):
+    """Cold and warm msa_decode on workload w, with its roofline (on the
+    distinct alive bytes too when unique=True)."""
+    import torch
+    prep = Prepared(w, split_blocks, kv_layout=kv_layout, kernel=kernel, d=d)
+    prep.plan()
+    prep.attention()
+    prep.check_error()
+    warm_for(prep.attention, 0.1)
+    cold = cold_times(prep.attention, n, prep.stream, flush)
+    warm_s = time_calls(prep.attention, n, prep.stream)
+    alg = decode_bytes(w)
+    cold_mean = statistics.fmean(cold)
+    leg = {"us_per_call": round(cold_mean * 1e6, 3), "cold_us": dist_us(cold),
+           "warm_us_per_call": round(warm_s * 1e6, 3),
+           "GB/s": round(alg / cold_mean / 1e9, 2), "pct_hbm_peak": round(100 * alg / cold_mean / 8e12, 2),
+           "tokens_per_s": round(w.B / cold_mean, 1),
+           "roofline": decode_roofline(alg, cold_mean, warm_s), **realised(w, prep)}
+    if unique:
+        ub = unique_alive_bytes(w) + w.B * w.Hq * (2 * w.D * esize(w) + 4)
+        leg["roofline"]["logical_bytes_per_call"] = leg["roofline"].pop("algorithmic_bytes_per_call")
+        leg["roofline"]["logical_GB/s"] = leg["roofline"]["achieved"]
+        leg["roofline"]["algorithmic_bytes_per_call"] = int(ub)
+        leg["roofline"]["achieved"] = round(ub / cold_mean / 1e9, 2)
+        leg["roofline"]["frac"] = round(ub / cold_mean / 1e9 / HBM_PEAK_GBS, 4)
+        leg["roofline"]["note"] = ("algorithmic bytes = distinct alive blocks (a shared prefix counted "
+                                   "once) + Q/O/LSE; logical = per sequence")
+        leg["roofline"]["warm"]["frac"] = round(ub / warm_s / 1e9 / HBM_PEAK_GBS, 4)
+    out = prep.out.clone()
+    del prep
+    torch.cuda.empty_cache()
+    return leg, out
+
+
+def prefill_leg(w, n, warm, flush=None):
+    """Time msa_prefill_chunk (plus its merge when split) on workload w: the
+    mean of back-to-back calls after a quarter second of warm-up (the rate
+    of a stream of chunks), and cold single calls when flush is given."""
     import torch
     prep = Prepared(w)
     flops = 4.0 * w.D * w.Hq * visible_pairs(w)
     prep.plan()
     for _ in range(warm):
         prep.attention()
-    torch.cuda.synchronize()
+    prep.check_error()
     # keep the matrix cores busy for a quarter second before timing: the
     # first milliseconds of a burst run at a lower clock (about 10% slower)
     warm_for(prep.attention)
     t = time_calls(prep.attention, n, prep.stream)
-    dist = call_percentiles(prep.attention, n, prep.stream)
     tfs = flops / t / 1e12
     stats = realised(w, prep)
+    rec = {"us_per_call": round(t * 1e6, 3), "TFLOP/s": round(tfs, 2),
+           "pct_mfma_bf16_peak": round(100 * tfs / MFMA_BF16_PEAK_TFS, 2), "calls": n, **stats}
+    if flush is not None:
+        cold = cold_times(prep.attention, max(5, n // 2), prep.stream, flush)
+        rec["cold_us"] = dist_us(cold)
     del prep
+    torch.cuda.empty_cache()
     G = w.Hq // w.Hkv
-    # (256 query rows, KV head, sequence) work items: one workgroup each; the
-    # library splits the key stream too when these do not cover the 256 CUs
-    items = -(-w.C * G // 256) * w.Hkv * w.B
-    return {"us_per_call": round(t * 1e6, 3), "TFLOP/s": round(tfs, 2),
-            "pct_mfma_bf16_peak": round(100 * tfs / MFMA_BF16_PEAK_TFS, 2), "calls": n,
-            "call_us": dist, **stats,
-            "row_tile_items": items, "flops": flops}
+    # (256/G query positions, KV head, sequence) work items: one workgroup
+    # each; the library splits the key stream too when these do not cover
+    # the 256 CUs
+    rec["row_tile_items"] = -(-w.C * G // 256) * w.Hkv * w.B
+    rec["flops"] = flops
+    return rec
 
 
-def latency_model_leg(args):
-    """Fit msa_decode time = c0 + c_tok * alive tokens + c_seg * segments over
-    decode batches that vary the context length (alive tokens) and the mean
-    alive-run length (segments at a given token count), then use the fitted
-    model in the kernel-aware eviction scorer on the headline batch and
-    check its prediction against the measured time after eviction."""
+def kernel_cases(args, w2, w5):
+    """Batches for the decode-kernel comparison: the headline batch as drawn
+    (G 4) and with 64 query heads (G 8: 32 more rows drawn N(0,1)); the
+    131k-token batch as drawn (G 8) and with its first 32 query heads (G 4)."""
+    import copy
+    import numpy as np
+    from workloads import f32_to_bf16_bits
+    rng = np.random.default_rng(args.seed + 30)
+    w2g8 = copy.copy(w2)
+    extra = f32_to_bf16_bits(rng.standard_normal((w2.B, w2.Hq, w2.D)).astype(np.float32))
+    w2g8.q = np.concatenate([w2.q, extra], axis=1)
+    w2g8.Hq = 2 * w2.Hq
+    w5g4 = copy.copy(w5)
+    w5g4.q = np.ascontiguousarray(w5.q[:, :w5.Hq // 2])
+    w5g4.Hq = w5.Hq // 2
+    return (("headline batch, G 4", w2), ("headline batch, G 8", w2g8),
+            ("131k-token batch, G 8", w5), ("131k-token batch, G 4", w5g4))
+
+
+def kernels_leg(args, flush, w2, w5):
+    """The vector-ALU and the matrix-core decode kernel on the same batches
+    (4 and 8 query heads per KV head): cold time and max error against the
+    oracle on sampled (sequence, head) pairs."""
     import numpy as np
     import torch
-    from workloads import make_workload
+    import oracle
+    from kv_cache_attention_msa_amd import _lib
+    from workloads.device import from_device
+    rng = np.random.default_rng(args.seed + 31)
+    cases = []
+    for name, w in kernel_cases(args, w2, w5):
+        seqs = sorted(rng.choice(w.B, size=min(2, w.B), replace=False).tolist())
+        heads = sorted(rng.choice(w.Hq, size=3, replace=False).tolist())
+        Or, Lr = oracle.decode_ref(w.q, w.k_pool, w.v_pool, w.block_table, w.alive, w.ctx_len,
+                                   w.block_size, w.scale, seqs=seqs, heads=heads)
+        row = {"batch": name, "G": w.Hq // w.Hkv}
+        for kname, k in (("vector", _lib.MSA_DECODE_VECTOR), ("matrix", _lib.MSA_DECODE_MATRIX)):
+            leg, out = decode_leg(w, max(10, args.steps // 2), flush, kernel=k)
+            O = from_device(out)
+            sel = np.ix_(seqs, heads)
+            err = float(np.max(np.abs(O[sel] - Or[sel])))
+            row[kname] = {"us_per_call": leg["us_per_call"], "warm_us_per_call": leg["warm_us_per_call"],
+                          "pct_hbm_peak": leg["pct_hbm_peak"], "max_abs_err_vs_oracle": err,
+                          "checked": f"sequences {seqs} x heads {heads}"}
+            del out
+        cases.append(row)
+        torch.cuda.empty_cache()
+    return cases
+
+
+def eviction_leg(args, flush, w):
+    """Kernel-aware eviction (keep-score = hit probability + recompute cost +
+    the decode time a block costs, from a latency model of msa_decode fitted
+    here) against hit-only eviction, at the same number of evicted blocks, on
+    the headline batch.  Only the alive mask changes, so the same device pools
+    serve every point; each point re-plans and times msa_decode cold."""
+    import numpy as np
+    import torch
     from kv_cache_attention_msa_amd.evict import (DecodeLatencyModel, choose_evictions,
                                                   recompute_cost_us)
-    pts = []
-    for ctx in (2048, 4096, 8192):
-        for run in (1.0, 4.0, 32.0):
-            w = make_workload(2, seed=args.seed, ctx=ctx, mean_alive=run, mean_dead=max(1.0, run / 4),
-                              pool_factor=2.5)
-            prep = Prepared(w)
-            prep.plan()
-            for _ in range(5):
-                prep.attention()
-            torch.cuda.synchronize()
-            t = time_calls(prep.attention, 30, prep.stream)
-            pts.append({"ctx": ctx, "mean_alive_run": run, "alive_tokens": int(sum(alive_tokens_per_seq(w))),
-                        "segments": int(prep.indptr[-1].item()), "us": round(t * 1e6, 3)})
-            del prep, w
+    from workloads.device import to_device
+    base = to_device(w, "cuda")
+    rng = np.random.default_rng(args.seed + 7)
+    B = w.B
+    nb = -(-w.ctx_len.astype(np.int64) // w.block_size)
+    evictable = [(b, l) for b in range(B) for l in range(int(nb[b]) - 1) if w.alive[b, l]]
+
+    def measure(alive):
+        import copy
+        wv = copy.copy(w)
+        wv.alive = alive
+        d = dict(base)
+        d["alive"] = torch.from_numpy(np.ascontiguousarray(alive)).to("cuda")
+        prep = Prepared(wv, d=d)
+        prep.plan()
+        prep.attention()
+        prep.check_error()
+        ts = cold_times(prep.attention, max(10, args.steps // 2), prep.stream, flush)
+        segs = int(prep.indptr[-1].item())
+        del prep
+        return {"alive_tokens": int(sum(alive_tokens_per_seq(wv))), "segments": segs,
+                "us": round(statistics.fmean(ts) * 1e6, 3)}
+
+    # fit points: extra evictions of single random blocks (more segments) and
+    # of whole alive runs (fewer segments) at three fractions each
+    pts = [dict(kind="as drawn", **measure(w.alive))]
+    for frac in (0.1, 0.2, 0.3):
+        al = w.alive.copy()
+        pick = rng.choice(len(evictable), size=int(frac * len(evictable)), replace=False)
+        for i in pick:
+            al[evictable[i]] = 0
+        pts.append(dict(kind=f"random blocks {frac:.0%}", **measure(al)))
+        al = w.alive.copy()
+        runs = []
+        for b in range(B):
+            l = 0
+            while l < nb[b] - 1:
+                if al[b, l]:
+                    s = l
+                    while l < nb[b] - 1 and al[b, l]:
+                        l += 1
+                    runs.append((b, s, l))
+                else:
+                    l += 1
+        order = rng.permutation(len(runs))
+        target, done = int(frac * len(evictable)), 0
+        for i in order:
+            b, s, e = runs[i]
+            if done >= target:
+                break
+            al[b, s:e] = 0
+            done += e - s
+        pts.append(dict(kind=f"whole runs {frac:.0%}", **measure(al)))
     m = DecodeLatencyModel.fit([p["alive_tokens"] for p in pts], [p["segments"] for p in pts],
                                [p["us"] for p in pts])
-    pred = m.predict([p["alive_tokens"] for p in pts], [p["segments"] for p in pts])
     meas = np.array([p["us"] for p in pts])
-    r2 = 1.0 - float(((meas - pred) ** 2).sum() / ((meas - meas.mean()) ** 2).sum())
-    # the scorer on the headline batch: evict a further 10% of the blocks
-    w = make_workload(2, seed=args.seed)
-    rng = np.random.default_rng(args.seed + 7)
+    pred = m.predict([p["alive_tokens"] for p in pts], [p["segments"] for p in pts])
+    r2 = 1.0 - float(((meas - pred) ** 2).sum() / max(((meas - meas.mean()) ** 2).sum(), 1e-30))
     hit = rng.random(w.alive.shape)
-    rec = [recompute_cost_us(w.alive[b], w.ctx_len[b], 16, w.D, w.Hq, 800.0) for b in range(w.B)]
-    n_ev = int(0.1 * w.alive.sum())
-    al, _ = choose_evictions(w.block_table, w.alive, w.ctx_len, 16, n_ev, hit, rec, m,
-                             alpha=float(np.mean([r.mean() for r in rec])), beta=1.0, gamma=1000.0,
-                             batch_seqs=w.B)
-    w.alive = al
-    prep = Prepared(w)
-    prep.plan()
-    for _ in range(5):
-        prep.attention()
-    torch.cuda.synchronize()
-    t_after = time_calls(prep.attention, 30, prep.stream)
-    segs_after = int(prep.indptr[-1].item())
-    tok_after = int(sum(alive_tokens_per_seq(w)))
-    del prep
-    return {"c0_us": round(m.c0, 3), "c_tok_us": m.c_tok, "c_seg_us": m.c_seg, "r2": round(r2, 4),
-            "points": pts,
-            "eviction_check": {"evicted_blocks": n_ev, "alive_tokens": tok_after, "segments": segs_after,
-                               "predicted_us": round(float(m.predict(tok_after, segs_after)), 3),
-                               "measured_us": round(t_after * 1e6, 3)}}
+    rec = [recompute_cost_us(w.alive[b], w.ctx_len[b], w.block_size, w.D, w.Hq, 1000.0)
+           for b in range(B)]
+    n_ev = int(0.1 * len(evictable))
+    policies = {}
+    for name, kw in (("kernel_aware", dict(alpha=float(np.mean([r.mean() for r in rec])), beta=1.0,
+                                           gamma=1000.0)),
+                     ("hit_only", dict(alpha=1.0, beta=0.0, gamma=0.0))):
+        al, ev = choose_evictions(w.block_table, w.alive, w.ctx_len, w.block_size, n_ev, hit, rec, m,
+                                  batch_seqs=B, **kw)
+        r = measure(al)
+        r["predicted_us"] = round(float(m.predict(r["alive_tokens"], r["segments"])), 3)
+        r["evicted_blocks"] = len(ev)
+        r["mean_hit_prob_evicted"] = round(float(np.mean([hit[b, l] for b, l in ev])), 4)
+        policies[name] = r
+    del base
+    torch.cuda.empty_cache()
+    return {"model": {"c0_us": round(m.c0, 3), "c_tok_us": m.c_tok, "c_seg_us": m.c_seg,
+                      "r2": round(r2, 4), "points": pts},
+            "evicted_blocks": n_ev, "policies": policies,
+            "decode_us_saved_by_kernel_aware": round(policies["hit_only"]["us"]
+                                                     - policies["kernel_aware"]["us"], 3)}
 
 
-def cpu_baseline(w, bytes_per_pass, budget_s=10.0, max_reps=20):
-    """The fp64 oracle, as it stands, on the same decode workload."""
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    reps, t0 = 0, time.perf_counter()
-    while reps < max_reps:
-        oracle.decode_ref(w.q, w.k_pool, w.v_pool, w.block_table, w.alive, w.ctx_len,
-                          w.block_size, w.scale)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(bytes_per_pass * reps / dt / 1e9, 4), "unit": "GB/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"fp64 numpy oracle (decode_ref) over the full headline decode batch "
-                      f"({w.B} sequences x {w.Hq} heads), {reps} passes in {dt:.1f} s; "
-                      f"BLAS threads {threads}, gathering single-threaded",
-            "seconds_per_pass": round(dt / reps, 4)}
+def chunk_sweep_leg(args, flush):
+    """The prefill workload with the chunk length varied (8192 cached tokens,
+    batch 4, 32 / 8 heads): the chunk-size curve, and the chunk length the
+    adaptive chooser (msa_prefill_chunk_rows) picks for this batch."""
+    import kv_cache_attention_msa_amd as msa
+    from workloads import make_workload
+    n = max(10, args.steps // 2)
+    pts = []
+    for C in (128, 256, 512, 1024, 2048):
+        wc = make_workload(3, seed=args.seed, C=C)
+        leg = prefill_leg(wc, n, 3)
+        leg.pop("flops")
+        pts.append({"C": C, "us_per_call": leg["us_per_call"], "TFLOP/s": leg["TFLOP/s"],
+                    "pct_mfma_bf16_peak": leg["pct_mfma_bf16_peak"],
+                    "row_tile_items": leg["row_tile_items"],
+                    "us_per_chunk_row": round(leg["us_per_call"] / C, 4)})
+        del wc
+    pick = msa.msa_prefill_chunk_rows(4, 32, 8, 1 << 20)
+    best = max(p["TFLOP/s"] for p in pts)
+    at = [p for p in pts if p["C"] == pick]
+    return {"workload": "prefill workload with the chunk length C varied", "points": pts,
+            "chooser": {"call": "msa_prefill_chunk_rows(B=4, Hq=32, Hkv=8, remaining=2^20)",
+                        "chunk_rows": pick,
+                        "TFLOP/s_at_pick": at[0]["TFLOP/s"] if at else None,
+                        "fraction_of_best_point": round(at[0]["TFLOP/s"] / best, 4) if at else None}}
 
 
-def prefill_cpu_baseline(w, row_step=16, budget_s=10.0, max_reps=5):
-    """The fp64 oracle, as it stands, on a row sample of the prefill workload:
-    every row_step-th chunk row of every sequence and head, over all the keys
-    each row sees."""
-    import numpy as np
-    import oracle
-    try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    rows = np.arange(0, w.C, row_step)
-    flops = 4.0 * w.D * w.Hq * visible_pairs(w, rows)
-    reps, t0 = 0, time.perf_counter()
-    while reps < max_reps:
-        oracle.prefill_ref(w.q, w.q_pos0, w.k_pool, w.v_pool, w.block_table, w.alive, w.ctx_len,
-                           w.block_size, w.scale, rows=rows)
-        reps += 1
-        if time.perf_counter() - t0 >= budget_s:
-            break
-    dt = time.perf_counter() - t0
-    return {"value": round(flops * reps / dt / 1e12, 6), "unit": "TFLOP/s", "cores": threads,
-            "kind": "oracle",
-            "sample": f"fp64 numpy oracle (prefill_ref) on every {row_step}th chunk row "
-                      f"({len(rows)} of {w.C}) of all {w.B} sequences x {w.Hq} heads, visible keys "
-                      f"only; {reps} passes in {dt:.1f} s; BLAS threads {threads}",
-            "seconds_per_pass": round(dt / reps, 4)}
+# --------------------------------------------------------------------------
 
-
-def main():
-    args = parse()
+def main(argv=None):
+    args = parse(argv)
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py: this build runs on exactly one GPU; multi-GPU runs are not supported "
@@ -458,190 +717,242 @@ def main():
 
     import numpy as np
     import torch
+    import kv_cache_attention_msa_amd as msa
+    from kv_cache_attention_msa_amd import _lib
     from workloads import make_workload, NAMES
 
     if not torch.cuda.is_available():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     torch.cuda.set_device(0)
-
+    flush = Flush()
+    cpu = not args.no_cpu_baseline and args.only is None
     result = {}
-    # ---------------------------------------------------------------- decode
-    if args.only in (None, "decode"):
-        from kv_cache_attention_msa_amd import _lib as _l
-        w = make_workload(2, seed=args.seed)
-        head_major = args.kv_layout == "hnd"
-        prep = Prepared(w, args.split_blocks,
-                        kv_layout=_l.MSA_LAYOUT_HND if head_major else _l.MSA_LAYOUT_NHD)
-        esz = 2 if w.dtype == "bf16" else 4
-        alive = alive_tokens_per_seq(w)
-        kv_bytes = sum(alive) * w.Hkv * w.D * 2 * esz
-        qo_bytes = 2 * w.B * w.Hq * w.D * esz + w.B * w.Hq * 4
-        alg_bytes = kv_bytes + qo_bytes
-        stream = prep.stream
-        for _ in range(args.warmup):
-            prep.step()
-        torch.cuda.synchronize()
-        err = int(prep.err.item())
-        nseg = int(prep.indptr[-1].item())
-        if err != 0:
-            raise RuntimeError(f"plan reported device error {err}")
-        # contract timing: K whole steps bracketed by synchronize
-        torch.cuda.synchronize()
-        t0 = time.perf_counter()
-        for _ in range(args.steps):
-            prep.step()
-        torch.cuda.synchronize()
-        step_s = (time.perf_counter() - t0) / args.steps
-        # dominant call: msa_decode (decode kernel + its split merge), HIP events
-        dec_s = time_calls(prep.attention, args.steps, stream)
-        dec_dist = call_percentiles(prep.attention, args.steps, stream)
-        out_nhd = prep.out.clone()
-        plan_s = time_calls(prep.plan, args.steps, stream)
-        value = alg_bytes / step_s / 1e9
-        achieved = alg_bytes / dec_s / 1e9
-        traffic = None
-        if os.path.exists(COUNTERS):
-            c = json.load(open(COUNTERS))
-            if (c.get("sources_sha") == sources_sha(DECODE_SOURCES) and c.get("split_blocks", 0) == args.split_blocks
-                    and c.get("kv_layout", "nhd") == args.kv_layout):
-                traffic = c.get("bytes_per_call")
-        result.update({
-            "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
-            "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
-            "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
-            "data": "synthetic",
-            "config": {"workload": NAMES[2], "batch": w.B, "q_heads": w.Hq, "kv_heads": w.Hkv,
-                       "head_dim": w.D, "ctx_len": int(w.ctx_len[0]), "block_size": w.block_size,
-                       "evicted_fraction": round(w.meta["evicted_fraction"], 4),
-                       "alive_tokens": int(sum(alive)), "segments": nseg,
-                       "kv_layout": "[P, Hkv, 16, D]" if head_major else "[P, 16, Hkv, D]",
-                       "step": "msa_plan_segments + msa_decode (decode kernel + split-K merge)",
-                       "seed": args.seed, "parallelism": "single GPU"},
-            "tokens_per_s": round(w.B / step_s, 1),
-            "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
-            "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS,
-                         "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                         "traffic": traffic, "traffic_unit": "bytes per call",
-                         "kernel": "msa_decode (decode kernel, plus the split merge when a sequence has several splits)",
-                         "algorithmic_bytes_per_call": int(alg_bytes),
-                         "us_per_call": round(dec_s * 1e6, 3)},
-            "plan_us_per_call": round(plan_s * 1e6, 3),
-            "decode_tokens_per_s": round(w.B / dec_s, 1),
-            "decode_call_us": dec_dist,
-        })
-        if not args.no_cold:
-            flush = torch.ones(1 << 28, dtype=torch.float32, device="cuda")
-            cold_s = time_cold(prep.attention, 30, stream, flush)
-            del flush
-            result["cold"] = {"us_per_call": round(cold_s * 1e6, 3),
-                              "GB/s": round(alg_bytes / cold_s / 1e9, 2),
-                              "pct_hbm_peak": round(100 * alg_bytes / cold_s / 1e9 / HBM_PEAK_GBS, 2),
-                              "note": "msa_decode alone, a 1 GiB read evicts L2 and Infinity Cache before each call"}
-        if not args.no_gather:
-            # the gather-then-attend detour on the same inputs, same kernel
-            gb = GatherBaseline(prep)
-            for _ in range(3):
-                gb.step()
-            torch.cuda.synchronize()
-            g_step = time_calls(gb.step, max(20, args.steps // 4), stream)
-            g_copy = time_calls(gb.gather, max(20, args.steps // 4), stream)
-            g_attn = time_calls(gb.attention, max(20, args.steps // 4), stream)
-            result["gather_baseline"] = {
-                "us_per_call": round(g_step * 1e6, 3), "gather_us": round(g_copy * 1e6, 3),
-                "dense_decode_us": round(g_attn * 1e6, 3), "msa_decode_us": round(dec_s * 1e6, 3),
-                "msa_speedup": round(g_step / dec_s, 3),
-                "note": "gather alive K/V blocks into dense pools (msa_gather_alive) + msa_decode "
-                        "over one segment per sequence, vs msa_decode over the segments"}
-            del gb
-            torch.cuda.empty_cache()
-        if not args.no_cpu_baseline:
-            result["cpu_baseline"] = cpu_baseline(w, alg_bytes)
-        del prep
-        torch.cuda.empty_cache()
-        if not args.no_layout and not head_major:
-            # the same batch with head-major pool blocks (msa_decode_ex)
-            hp = Prepared(w, args.split_blocks, kv_layout=_l.MSA_LAYOUT_HND)
-            hp.plan()
-            warm_for(hp.attention, 0.1)
-            torch.cuda.synchronize()
-            same = bool(torch.equal(hp.out, out_nhd))
-            hnd_s = time_calls(hp.attention, args.steps, stream)
-            result["decode_hnd"] = {
-                "us_per_call": round(hnd_s * 1e6, 3), "GB/s": round(alg_bytes / hnd_s / 1e9, 2),
-                "pct_hbm_peak": round(100 * alg_bytes / hnd_s / 1e9 / HBM_PEAK_GBS, 2),
-                "bitwise_equal_to_nhd": same,
-                "note": "msa_decode_ex on the same batch with head-major pool blocks [P, Hkv, 16, D] "
-                        "(each KV head's 16 rows of a block contiguous)"}
-            del hp
-            torch.cuda.empty_cache()
+    layout = _lib.MSA_LAYOUT_HND if args.kv_layout == "hnd" else _lib.MSA_LAYOUT_NHD
 
-    # ------------------------------------------- decode latency model (next)
-    if args.latency_model:
-        result["latency_model"] = latency_model_leg(args)
-
-    # ------------------------- decode on the other two decode families
-    if args.more_decode and args.only in (None, "decode"):
-        legs = []
-        for fam in (4, 5):
-            from kv_cache_attention_msa_amd import _lib as _l
-            wf = make_workload(fam, seed=args.seed)
-            prep = Prepared(wf, args.split_blocks, kv_layout=_l.MSA_LAYOUT_HND if args.kv_layout == "hnd"
-                            else _l.MSA_LAYOUT_NHD)
+    # ------------------------------------------------------------ profiler modes
+    if args.only is not None:
+        n = args.steps
+        if args.only in ("decode", "decode-warm"):
+            w = make_workload(2, seed=args.seed)
+            prep = Prepared(w, args.split_blocks, kv_layout=layout)
+            for _ in range(args.warmup):
+                prep.step()
+            prep.check_error()
+            if args.only == "decode-warm":
+                result["us_per_call_warm"] = round(time_calls(prep.attention, n, prep.stream) * 1e6, 3)
+            else:
+                result["cold_us"] = dist_us(cold_times(prep.attention, n, prep.stream, flush))
+        elif args.only == "kernels":
+            # each batch with the vector kernel, then the matrix-core kernel
+            cases = kernel_cases(args, make_workload(2, seed=args.seed), make_workload(5, seed=args.seed))
+            for name, w in cases:
+                for kname, k in (("vector", _lib.MSA_DECODE_VECTOR), ("matrix", _lib.MSA_DECODE_MATRIX)):
+                    prep = Prepared(w, kernel=k)
+                    for _ in range(args.warmup):
+                        prep.step()
+                    prep.check_error()
+                    result[f"{name}, {kname}"] = dist_us(cold_times(prep.attention, n, prep.stream, flush))
+                    del prep
+                    torch.cuda.empty_cache()
+        elif args.only in ("decode4", "decode5"):
+            w = make_workload(4 if args.only == "decode4" else 5, seed=args.seed)
+            prep = Prepared(w, args.split_blocks, kv_layout=layout)
+            for _ in range(args.warmup):
+                prep.step()
+            prep.check_error()
+            result["cold_us"] = dist_us(cold_times(prep.attention, n, prep.stream, flush))
+        elif args.only == "prefill":
+            w = make_workload(3, seed=args.seed)
+            prep = Prepared(w)
             prep.plan()
+            for _ in range(args.warmup):
+                prep.attention()
+            prep.check_error()
             warm_for(prep.attention)
-            t = time_calls(prep.attention, max(10, args.steps // 10), prep.stream)
-            logical = sum(alive_tokens_per_seq(wf)) * wf.Hkv * wf.D * (2 if wf.dtype == "bf16" else 4) * 2
-            unique = unique_alive_bytes(wf)
-            legs.append({"workload": NAMES[fam], "us_per_call": round(t * 1e6, 3),
-                         "logical_bytes": logical, "unique_bytes": unique,
-                         "GB/s_logical": round(logical / t / 1e9, 1),
-                         "GB/s_unique": round(unique / t / 1e9, 1),
-                         "pct_hbm_peak_unique": round(100 * unique / t / 1e9 / HBM_PEAK_GBS, 2),
-                         "tokens_per_s": round(wf.B / t, 1), "kv_layout": args.kv_layout,
-                         **realised(wf, prep)})
-            del prep, wf
-            torch.cuda.empty_cache()
-        result["more_decode"] = legs
+            result["us_per_call"] = round(time_calls(prep.attention, n, prep.stream) * 1e6, 3)
+        if args.copy_calibration:
+            a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
+            bb = torch.empty_like(a)
+            for _ in range(5):
+                bb.copy_(a)
+            torch.cuda.synchronize()
+            result["copy_calibration_bytes"] = 256 << 20
+        result["only"] = args.only
+        print(json.dumps(result), flush=True)
+        return
+
+    # ------------------------------------------------------ headline decode step
+    w2 = make_workload(2, seed=args.seed)
+    head_major = layout == _lib.MSA_LAYOUT_HND
+    prep = Prepared(w2, args.split_blocks, kv_layout=layout)
+    alg_bytes = decode_bytes(w2)
+    stream = prep.stream
+    for _ in range(args.warmup):
+        prep.step()
+    prep.check_error()
+    nseg = int(prep.indptr[-1].item())
+    # contract region: exactly K steps, each after an untimed cache flush and
+    # timed by its own HIP events; bracketed by synchronize on both sides
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    step_ts = cold_times(prep.step, args.steps, stream, flush)
+    torch.cuda.synchronize()
+    bracket_s = time.perf_counter() - t0
+    step_s = statistics.fmean(step_ts)
+    # the same K steps back to back (warm)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        prep.step()
+    torch.cuda.synchronize()
+    warm_step_s = (time.perf_counter() - t0) / args.steps
+    prep.check_error()
+    # dominant call: msa_decode (decode kernel + split merge), cold and warm
+    dec_cold = cold_times(prep.attention, args.steps, stream, flush)
+    dec_warm_s = time_calls(prep.attention, args.steps, stream)
+    plan_s = time_calls(prep.plan, args.steps, stream)
+    dec_mean = statistics.fmean(dec_cold)
+    out_headline = prep.out.clone()
+    traffic = counter_traffic(COUNTERS, DECODE_SOURCES, split_blocks=args.split_blocks,
+                              kv_layout=args.kv_layout)
+    value = alg_bytes / step_s / 1e9
+    result.update({
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1,
+        "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(step_s * 1e3, 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": NAMES[2], "batch": w2.B, "q_heads": w2.Hq, "kv_heads": w2.Hkv,
+                   "head_dim": w2.D, "ctx_len": int(w2.ctx_len[0]), "block_size": w2.block_size,
+                   "evicted_fraction": round(w2.meta["evicted_fraction"], 4),
+                   "alive_tokens": int(sum(alive_tokens_per_seq(w2))), "segments": nseg,
+                   "kv_layout": "[P, Hkv, 16, D]" if head_major else "[P, 16, Hkv, D]",
+                   "step": "msa_plan_segments + msa_decode (decode kernel + split-K merge)",
+                   "timing": "cold: a 1 GiB read evicts L2 and the Infinity Cache before each step "
+                             "(outside the step's HIP events); value and ms_per_step are the mean "
+                             "over the K steps",
+                   "seed": args.seed, "parallelism": "single GPU"},
+        "tokens_per_s": round(w2.B / step_s, 1),
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
+        "step_us": dist_us(step_ts),
+        "contract_bracket_s": round(bracket_s, 4),
+        "warm_step": {"ms_per_step": round(warm_step_s * 1e3, 4),
+                      "GB/s": round(alg_bytes / warm_step_s / 1e9, 2),
+                      "tokens_per_s": round(w2.B / warm_step_s, 1),
+                      "note": "the same K steps back to back (caches warm), bracketed by synchronize"},
+        "roofline": decode_roofline(alg_bytes, dec_mean, dec_warm_s, traffic,
+                                    kernel="msa_decode (decode kernel, plus the split merge when a "
+                                           "sequence has several splits)"),
+        "decode_call_us": dist_us(dec_cold),
+        "plan_us_per_call": round(plan_s * 1e6, 3),
+        "decode_tokens_per_s": round(w2.B / dec_mean, 1),
+    })
+    if not args.no_gather:
+        # the gather-then-attend detour on the same inputs, same kernel
+        gb = GatherBaseline(prep)
+        for _ in range(3):
+            gb.step()
+        torch.cuda.synchronize()
+        n = max(10, args.steps // 2)
+        g_step = statistics.fmean(cold_times(gb.step, n, stream, flush))
+        g_copy = statistics.fmean(cold_times(gb.gather, n, stream, flush))
+        g_attn = time_calls(gb.attention, n, stream)
+        result["gather_baseline"] = {
+            "us_per_call": round(g_step * 1e6, 3), "gather_us": round(g_copy * 1e6, 3),
+            "dense_decode_us_warm": round(g_attn * 1e6, 3), "msa_decode_us": round(dec_mean * 1e6, 3),
+            "msa_speedup": round(g_step / dec_mean, 3),
+            "note": "cold: gather alive K/V blocks into dense pools (msa_gather_alive) + msa_decode "
+                    "over one segment per sequence, vs msa_decode over the segments"}
+        del gb
+        torch.cuda.empty_cache()
+    d2 = prep.d
+    del prep
+    torch.cuda.empty_cache()
+    if cpu:
+        result["cpu_baseline"] = decode_cpu_baseline(w2, budget_s=8.0, label="the headline batch,")
+    if not args.no_layout and not head_major:
+        # the same batch with head-major pool blocks (msa_decode_ex)
+        dh = dict(d2)
+        dh["k_pool"] = d2["k_pool"].permute(0, 2, 1, 3).contiguous()
+        dh["v_pool"] = d2["v_pool"].permute(0, 2, 1, 3).contiguous()
+        leg, out = decode_leg(w2, args.steps, flush, kv_layout=_lib.MSA_LAYOUT_HND, d=dh)
+        leg["bitwise_equal_to_token_major"] = bool(torch.equal(out, out_headline))
+        leg["note"] = ("msa_decode_ex on the same batch with head-major pool blocks [P, Hkv, 16, D] "
+                       "(each KV head's 16 rows of a block contiguous)")
+        result["decode_hnd"] = leg
+        del dh, out
+        torch.cuda.empty_cache()
+    del d2
+    torch.cuda.empty_cache()
+
+    # --------------------------------------- the other decode workloads
+    w5 = None
+    if not args.no_more_decode:
+        w1 = make_workload(1, seed=args.seed)
+        leg, _ = decode_leg(w1, args.steps, flush)
+        leg["note"] = "correctness configuration: 0.79 MB of K/V per call, launch-latency bound"
+        if cpu:
+            leg["cpu_baseline"] = decode_cpu_baseline(w1, budget_s=2.0, label="the fp32 batch,")
+        result["decode_small_fp32"] = {"workload": NAMES[1], **leg}
+        n = max(10, args.steps // 2)
+        w4 = make_workload(4, seed=args.seed)
+        leg, _ = decode_leg(w4, n, flush, kv_layout=layout, unique=True)
+        if cpu:
+            pick = sorted(np.random.default_rng(args.seed + 4).choice(w4.B, 4, replace=False).tolist())
+            leg["cpu_baseline"] = decode_cpu_baseline(w4, seqs=pick, budget_s=4.0, single=False,
+                                                      label="the lognormal batch,")
+        result["decode_lognormal"] = {"workload": NAMES[4], **leg}
+        del w4
+        w5 = make_workload(5, seed=args.seed)
+        leg, _ = decode_leg(w5, n, flush, kv_layout=layout)
+        if cpu:
+            leg["cpu_baseline"] = decode_cpu_baseline(w5, seqs=[0], budget_s=4.0, single=False,
+                                                      label="the 131k-token batch,")
+        result["decode_long"] = {"workload": NAMES[5], **leg}
+        torch.cuda.empty_cache()
+
+    # --------------------------- vector against matrix-core decode kernel
+    if not args.no_kernels:
+        if w5 is None:
+            w5 = make_workload(5, seed=args.seed)
+        result["decode_kernels"] = kernels_leg(args, flush, w2, w5)
+    del w5
+    torch.cuda.empty_cache()
+
+    # -------------------------- kernel-aware against hit-only eviction
+    if not args.no_eviction:
+        result["eviction"] = eviction_leg(args, flush, w2)
+
+    if args.latency_model:
+        result["latency_model"] = latency_model_leg(args, flush)
 
     # --------------------------------------------------------------- prefill
-    import kv_cache_attention_msa_amd as msa
-    if args.only in (None, "prefill") and not args.no_prefill and msa.prefill_available():
-        n = max(10, args.steps // 4)
+    if not args.no_prefill and msa.prefill_available():
+        n = max(10, args.steps // 2)
         wp = make_workload(3, seed=args.seed)
-        leg = prefill_leg(wp, n, max(3, args.warmup // 4))
+        leg = prefill_leg(wp, n, max(3, args.warmup // 4), flush)
         tfs = leg["TFLOP/s"]
-        pf_traffic = None
-        if os.path.exists(PF_COUNTERS):
-            c = json.load(open(PF_COUNTERS))
-            if c.get("sources_sha") == sources_sha(PREFILL_SOURCES):
-                pf_traffic = c.get("bytes_per_call")
+        pf_traffic = counter_traffic(PF_COUNTERS, PREFILL_SOURCES, split_blocks=0)
         leg["roofline"] = {"bound": "mfma", "achieved": tfs, "peak": MFMA_BF16_PEAK_TFS,
                            "unit": "TFLOP/s", "frac": round(tfs / MFMA_BF16_PEAK_TFS, 4),
                            "traffic": pf_traffic, "traffic_unit": "bytes per call",
                            "kernel": "msa_prefill_chunk",
+                           "timing": "mean of back-to-back calls after a quarter second of warm-up",
                            "algorithmic_flops_per_call": leg.pop("flops")}
-        if not args.no_cpu_baseline:
+        if cpu:
             leg["cpu_baseline"] = prefill_cpu_baseline(wp)
         result["prefill"] = {"workload": NAMES[3], **leg}
         del wp
-        # recompute of an evicted middle range (chunk rows in the middle of the
-        # context, later alive blocks hidden by the causal mask)
         if not args.no_recompute:
+            # recompute of an evicted middle range (chunk rows in the middle of
+            # the context, later alive blocks hidden by the causal mask)
             wr = make_workload(6, seed=args.seed)
             leg = prefill_leg(wr, n, 3)
             leg.pop("flops")
             result["recompute"] = {"workload": NAMES[6], **leg}
             del wr
-        if args.chunk_sweep:
-            sweep = []
-            for C in (128, 256, 512, 1024, 2048):
-                wc = make_workload(3, seed=args.seed, C=C)
-                leg = prefill_leg(wc, n, 3)
-                leg.pop("flops")
-                sweep.append({"C": C, **leg})
-                del wc
-            result["chunk_sweep"] = {"workload": NAMES[3] + " with chunk C varied", "points": sweep}
+        if not args.no_chunk_sweep:
+            result["chunk_sweep"] = chunk_sweep_leg(args, flush)
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         bb = torch.empty_like(a)
@@ -650,6 +961,37 @@ def main():
         torch.cuda.synchronize()
         result["copy_calibration_bytes"] = 256 << 20
     print(json.dumps(result), flush=True)
+
+
+def latency_model_leg(args, flush):
+    """Fit msa_decode time = c0 + c_tok * alive tokens + c_seg * segments over
+    new decode batches that vary the context length (alive tokens) and the
+    mean alive-run length (segments at a given token count)."""
+    import numpy as np
+    import torch
+    from kv_cache_attention_msa_amd.evict import DecodeLatencyModel
+    from workloads import make_workload
+    pts = []
+    for ctx in (2048, 4096, 8192):
+        for run in (1.0, 4.0, 32.0):
+            w = make_workload(2, seed=args.seed, ctx=ctx, mean_alive=run, mean_dead=max(1.0, run / 4),
+                              pool_factor=2.5)
+            prep = Prepared(w)
+            prep.plan()
+            prep.attention()
+            prep.check_error()
+            t = statistics.fmean(cold_times(prep.attention, 20, prep.stream, flush))
+            pts.append({"ctx": ctx, "mean_alive_run": run, "alive_tokens": int(sum(alive_tokens_per_seq(w))),
+                        "segments": int(prep.indptr[-1].item()), "us": round(t * 1e6, 3)})
+            del prep, w
+            torch.cuda.empty_cache()
+    m = DecodeLatencyModel.fit([p["alive_tokens"] for p in pts], [p["segments"] for p in pts],
+                               [p["us"] for p in pts])
+    pred = m.predict([p["alive_tokens"] for p in pts], [p["segments"] for p in pts])
+    meas = np.array([p["us"] for p in pts])
+    r2 = 1.0 - float(((meas - pred) ** 2).sum() / ((meas - meas.mean()) ** 2).sum())
+    return {"c0_us": round(m.c0, 3), "c_tok_us": m.c_tok, "c_seg_us": m.c_seg, "r2": round(r2, 4),
+            "points": pts}
 
 
 if __name__ == "__main__":
