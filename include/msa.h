@@ -9,10 +9,10 @@
  * log-sum-exp normaliser.
  *   Source: "AsymCache：把 KV Cache 决策摆到 GPU 注意力内核的同一张桌子上"
  *   (papers.ananclaw.com explainer of arXiv 2606.02964), section
- *   "核心方法 / 1. Multi-Segment Attention (MSA)", its pseudocode
- *   (multi_segment_attention, split_into_contiguous_segments,
- *   attention_kernel(Q, seg.K, seg.V) * normalizer(seg)) and the paragraph
- *   after it; "Multi-Segment Attention: Enabling Efficient KV-Cache
+ *   "核心方法 / 1. Multi-Segment Attention (MSA)", its pseudocode (a split
+ *   of the alive blocks into contiguous segments, attention per segment,
+ *   results summed with a per-segment normaliser) and the paragraph after
+ *   it; "Multi-Segment Attention: Enabling Efficient KV-Cache
  *   Management for Faster LLM Serving" (gptget.net), Methodology and Key
  *   Results (one kernel processes many disjoint segments).
  *
@@ -275,8 +275,8 @@ int32_t msa_prefill_chunk_rows(int32_t B, int32_t Hq, int32_t Hkv, int32_t remai
 /* a5: log-sum-exp merge of partials                                         */
 /* ------------------------------------------------------------------------ */
 
-/* out += attention_kernel(Q, seg.K, seg.V) * normalizer(seg) (P1 MSA
- * pseudocode), with normalizer read as the log-sum-exp weight.
+/* The sum of per-segment results scaled by a per-segment normaliser (P1 MSA
+ * pseudocode), with the normaliser read as the log-sum-exp weight.
  *
  * Partials of sequence b are rows [part_indptr[b], part_indptr[b+1]) of
  *   o_part  float32 [N, R, H, D]   unnormalised output  sum_j exp(s_j - m) v_j

@@ -48,6 +48,7 @@ constexpr int kNW = kThreads / kWave;
 constexpr int kTileTok = 64;      // tokens per wavefront tile (4 blocks of 16)
 constexpr int kBlk = 16;          // block size the kernels are built for
 constexpr int kMaxSplitBlocks = 512;
+constexpr int kCUs = 256;  // compute units of an MI355X
 constexpr float kLn2 = 0.69314718055994530942f;
 
 template <typename KV, int D>
@@ -155,10 +156,12 @@ __device__ __forceinline__ void store_out<float>(void* out, size_t idx, float v)
 }
 
 // Largest i in [lo, hi) with segs[i].alive_token_start <= x, given that
-// segs[lo] satisfies it.  Workgroup-uniform; every thread must call it.
-__device__ __forceinline__ int wg_search_segment(const msa_segment* segs, int lo, int hi, int x) {
+// segs[lo] satisfies it.  Workgroup-uniform; all THREADS threads of the
+// workgroup must call it.
+template <int THREADS>
+__device__ __forceinline__ int wg_search_segment_n(const msa_segment* segs, int lo, int hi, int x) {
   while (hi - lo > 1) {
-    const int step = (hi - lo + kThreads - 1) / kThreads;
+    const int step = (hi - lo + THREADS - 1) / THREADS;
     const int idx = lo + int(threadIdx.x) * step;
     const bool pred = idx < hi && segs[idx].alive_token_start <= x;
     const int cnt = __syncthreads_count(pred);
@@ -218,7 +221,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   const int last_tokens = min(kBlk, A - kBlk * (nAB - 1));  // tokens in the final alive block
 
   // ---- expand this split's segments into per-block physical ids ----------
-  const int sf = wg_search_segment(p.segs, s0, s1, j0 * kBlk);
+  // (the first split starts at the sequence's first segment: no search)
+  const int sf = j0 == 0 ? s0 : wg_search_segment_n<kThreads>(p.segs, s0, s1, j0 * kBlk);
   const int ns = min(nblk, s1 - sf);
   int32_t* st_start = reinterpret_cast<int32_t*>(&k_lds[0][0]);
   int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
@@ -480,16 +484,27 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
 // split rule, segment walk and cross-wavefront merge as decode_kernel.
 //
 // Per wavefront and 64-token tile (4 blocks):
-//   S[key][head] = K Q^T: A = K rows straight from HBM into VGPRs (lane l:
-//     key l%16 of block kg, d 32 ds + 8(l/16) .. +7: 16 keys x 64 B per
-//     load), B = Q^T (lane l: head l%16, same d), C: lane l holds head l%16
-//     for keys 16 kg + 4(l/16) + r.
+//   S[key][head] = K Q^T: A = K (lane l: key l%16 of block kg, d 32 ds +
+//     8(l/16) .. +7), B = Q^T (lane l: head l%16, same d), C: lane l holds
+//     head l%16 for keys 16 kg + 4(l/16) + r.
 //   online softmax per head over those 16 values x the 4 lanes of the head
 //   O[head][d] += P V: A = P, exactly the lane's own weights (k-slots are
 //     keys 16(2ks + s/4) + 4(l/16) + s%4), B = V from LDS with the gfx950
-//     transpose read (4 keys x 1 d per lane per read); V reaches the
-//     wavefront's LDS tile by DMA in an order that makes those reads
-//     lane-linear.
+//     transpose read (4 keys x 1 d per lane per read).
+// Loads: V reaches the wavefront's LDS tile by DMA, every instruction four
+// whole 256-byte rows (16 lanes per row) with the streaming hint; each
+// 16-byte chunk c of key k lands in slot c ^ (2k mod 16) of the key's row,
+// which keeps the transpose reads free of bank conflicts.  Whole rows matter:
+// the same data fetched as four 64-byte pieces per row from four
+// instructions (which a streaming load never merges) took 88 against 80 us
+// on the 32 x 4k batch with cold caches.  K comes either straight from HBM
+// into the A operand registers (16 keys x 64 B per instruction, default
+// cache policy so the two halves of each 128-byte line meet in the cache),
+// or, when the grid holds at most one workgroup per CU (KDMA: the extra
+// 64 KB of LDS then costs no occupancy), by DMA in whole rows like V
+// (chunk c of key k in slot c ^ k), read back as operands: 78 against 80 us
+// cold on the 32 x 4k batch, while on many-split grids the halved occupancy
+// costs more than the rows gain.
 // K(t+1) is loaded during softmax and PV of tile t, V(t+1) during QK(t+1).
 
 typedef __bf16 mbf16x8_t __attribute__((ext_vector_type(8)));
@@ -500,7 +515,7 @@ typedef __bf16 mbf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kMD = 128, kMRow = 256;
 constexpr int kMTile = kTileTok * kMRow;  // bytes of a K or V tile (16 KB)
-constexpr int kMUnit = 1024;              // one V DMA unit: 16 keys x 64 B of d
+constexpr int kMBlock = kBlk * kMRow;     // one block's 16 rows of one head in a tile (4 KB)
 
 __device__ __forceinline__ mbf16x8_t m_as_bf16x8(uint4 x) { return __builtin_bit_cast(mbf16x8_t, x); }
 __device__ __forceinline__ uint32_t m_cvt_pk_bf16(float a, float b) {
@@ -516,13 +531,15 @@ __device__ __forceinline__ uint2 m_read_tr16(const uint8_t* lds_ptr) {
   return __builtin_bit_cast(uint2, v);
 }
 
-template <int G>
-__global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p) {
+template <int G, bool KDMA>
+__global__ void __launch_bounds__(kThreads, KDMA ? 1 : 2) decode_mfma_kernel(DecodeParams p) {
   static_assert(G == 4 || G == 8, "heads padded to 16 MFMA rows");
   constexpr int D = kMD;
   // per-wavefront V tile; during set-up the same bytes hold the staged
   // segment list, and at the end the per-wavefront states for the merge
   __shared__ __align__(16) uint8_t v_lds[kNW][kMTile];
+  // KDMA: per-wavefront K tile, rows landed whole by DMA
+  __shared__ __align__(16) uint8_t k_lds[KDMA ? kNW : 1][KDMA ? kMTile : 16];
   __shared__ __align__(16) int32_t blk_phys[kMaxSplitBlocks];
   static_assert(sizeof(v_lds) >= 3 * (kMaxSplitBlocks + 1) * sizeof(int32_t), "staging");
   static_assert(sizeof(v_lds) >= (kNW * G * D + 2 * kNW * G) * sizeof(float), "merge");
@@ -531,6 +548,17 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
   const int w = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int T = p.split_blocks;
+  const int hl = lane % 16, q4 = lane / 16;
+
+  // Q^T operand (lane l: head l%16, zero past G, d 32 ds + 8(l/16)): issued
+  // first, so its round trip overlaps the plan reads below
+  uint4 qop[4];
+  {
+    const uint8_t* qsrc = static_cast<const uint8_t*>(p.q) + (size_t(b) * p.Hq + size_t(g) * G + hl) * kMRow;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      qop[ds] = hl < G ? *reinterpret_cast<const uint4*>(qsrc + (4 * ds + q4) * 16) : make_uint4(0, 0, 0, 0);
+  }
 
   const int s0 = p.indptr[b], s1 = p.indptr[b + 1];
   int A = 0;
@@ -559,7 +587,8 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
 
   // ---- expand this split's segments into per-block physical ids ----------
   {
-    const int sf = wg_search_segment(p.segs, s0, s1, j0 * kBlk);
+    // the first split starts at the sequence's first segment: no search
+    const int sf = j0 == 0 ? s0 : wg_search_segment_n<kThreads>(p.segs, s0, s1, j0 * kBlk);
     const int ns = min(nblk, s1 - sf);
     int32_t* st_start = reinterpret_cast<int32_t*>(&v_lds[0][0]);
     int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
@@ -586,16 +615,6 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
     __syncthreads();  // staging dead from here on: the V tiles may overwrite it
   }
 
-  const int hl = lane % 16, q4 = lane / 16;
-  // Q^T operand: lane l holds head l%16 (zero past G), d 32 ds + 8(l/16)
-  uint4 qop[4];
-  {
-    const uint8_t* qsrc = static_cast<const uint8_t*>(p.q) + (size_t(b) * p.Hq + size_t(g) * G + hl) * kMRow;
-#pragma unroll
-    for (int ds = 0; ds < 4; ++ds)
-      qop[ds] = hl < G ? *reinterpret_cast<const uint4*>(qsrc + (4 * ds + q4) * 16) : make_uint4(0, 0, 0, 0);
-  }
-
   // slot, block and KV-head strides of the token-major or head-major pool
   const size_t tok_stride = p.head_major ? size_t(kMRow) : size_t(p.Hkv) * kMRow;
   const size_t blk_stride = size_t(p.Hkv) * kMRow * kBlk;
@@ -604,13 +623,16 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
   const char* vbase = static_cast<const char*>(p.v_pool) + head_off;
   // K operand loads: lane offset inside a block for d step ds (adds 64 B each)
   const uint32_t k_voff = uint32_t(hl * tok_stride + q4 * 16);
-  // V DMA unit (block, quarter dq of d): lane i writes 16 B at 16 i holding
-  // key 4(m/8) + (m%8)/2, d 32 dq + 16 e + 8(m%2) .. +7 (m = i%32, e = i/32):
-  // the transpose reads' words for lanes 2m and 2m+1 of half e
-  const int m32 = lane % 32, e2 = lane / 32;
-  const uint32_t v_voff = uint32_t((4 * (m32 / 8) + (m32 % 8) / 2) * tok_stride +
-                                   2 * (16 * e2 + 8 * (m32 % 2)));
+  // row DMAs: instruction i of a block covers keys 4i .. 4i+3, lane l key
+  // 4i + l/16 and its 16-byte slot l%16
+  const int kq = lane / 16, slot = lane % 16;
   uint8_t* vt = &v_lds[w][0];
+  uint8_t* kt = &k_lds[KDMA ? w : 0][0];
+  // transpose-read word of lane l (j = l%16) for PV step (block, dg): key
+  // 4(l/16) + j/4, d = 16 dg + 4(j%4) .. +3, i.e. chunk 2dg + (j%4)/2
+  const int vr_key = 4 * q4 + hl / 4;
+  const int vr_base = vr_key * kMRow + 8 * (hl % 2);
+  auto vrow_off = [&](int dg) { return vr_base + 16 * ((2 * dg + (hl % 4) / 2) ^ ((2 * vr_key) & 15)); };
 
   mf32x4_t o[8];
 #pragma unroll
@@ -641,22 +663,35 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
       const __amdgpu_buffer_rsrc_t r = rsrc_of(kbase, ph[kg], rows[kg]);
-      // (default cache policy: each 256-byte key row arrives as four 64-byte
-      // pieces from four loads, which must meet in the cache; measured 79 us
-      // against 99 us with the streaming hint on these loads)
+      if constexpr (KDMA) {
+        // chunk slot ^ key of key 4i + kq into slot `slot` of its row
 #pragma unroll
-      for (int ds = 0; ds < 4; ++ds) kreg[kg][ds] = load16_cached(r, k_voff + ds * 64);
+        for (int i = 0; i < 4; ++i) {
+          const int key = 4 * i + kq;
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(
+              r, (__attribute__((address_space(3))) void*)(kt + kg * kMBlock + i * 4 * kMRow), 16,
+              uint32_t(key * tok_stride + 16 * (slot ^ key)), 0, 0, kStreamPolicy);
+        }
+      } else {
+        // default cache policy: each 128-byte line of a key row arrives as
+        // two 64-byte pieces from two loads, which must meet in the cache
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds) kreg[kg][ds] = load16_cached(r, k_voff + ds * 64);
+      }
     }
   };
   auto issue_v = [&](const int* ph, const int* rows) {
 #pragma unroll
     for (int kg = 0; kg < 4; ++kg) {
       const __amdgpu_buffer_rsrc_t r = rsrc_of(vbase, ph[kg], rows[kg]);
+      // chunk slot ^ (2 key mod 16) of key 4i + kq into slot `slot` of its row
 #pragma unroll
-      for (int dq = 0; dq < 4; ++dq)
+      for (int i = 0; i < 4; ++i) {
+        const int key = 4 * i + kq;
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
-            r, (__attribute__((address_space(3))) void*)(vt + (kg * 4 + dq) * kMUnit), 16,
-            v_voff + dq * 64, 0, 0, kStreamPolicy);
+            r, (__attribute__((address_space(3))) void*)(vt + kg * kMBlock + i * 4 * kMRow), 16,
+            uint32_t(key * tok_stride + 16 * (slot ^ ((2 * key) & 15))), 0, 0, kStreamPolicy);
+      }
     }
   };
 
@@ -666,6 +701,17 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
   issue_k(ph, rows);
   issue_v(ph, rows);
   for (; ti < ntiles; ti += kNW) {
+    if constexpr (KDMA) {
+      // K(t) has landed once at most the 16 V DMAs of this tile are in
+      // flight; then the A operands come from the K tile (slot c ^ key)
+      asm volatile("s_waitcnt vmcnt(16)" ::: "memory");
+#pragma unroll
+      for (int kg = 0; kg < 4; ++kg)
+#pragma unroll
+        for (int ds = 0; ds < 4; ++ds)
+          kreg[kg][ds] = *reinterpret_cast<const uint4*>(kt + kg * kMBlock + hl * kMRow +
+                                                         16 * ((4 * ds + q4) ^ hl));
+    }
     // ---- S = K Q^T for the tile's 4 blocks ------------------------------
     mf32x4_t sc[4];
 #pragma unroll
@@ -676,8 +722,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
         sc[kg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(kreg[kg][ds]),
                                                          m_as_bf16x8(qop[ds]), sc[kg], 0, 0, 0);
     }
-    // next tile's K is in flight during softmax and PV of this one
+    // next tile's K is in flight during softmax and PV of this one (KDMA:
+    // once this tile's operand reads have returned)
     tile_blocks(ti + kNW, phn, rowsn);
+    if constexpr (KDMA) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     issue_k(phn, rowsn);
 
     // ---- mask rows that do not exist (padding past ctx_len, missing blocks)
@@ -736,9 +784,9 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
 #pragma unroll
       for (int dg = 0; dg < 8; ++dg) {
         // k-slots 0..3: block 2ks, rows 4(l/16)+0..3; 4..7: block 2ks+1
-        const uint8_t* u0 = vt + ((2 * ks) * 4 + dg / 2) * kMUnit + (dg % 2) * (kMUnit / 2) + lane * 8;
+        const uint8_t* u0 = vt + (2 * ks) * kMBlock + vrow_off(dg);
         const uint2 lo2 = m_read_tr16(u0);
-        const uint2 hi2 = m_read_tr16(u0 + 4 * kMUnit);
+        const uint2 hi2 = m_read_tr16(u0 + kMBlock);
         const uint4 vop = make_uint4(lo2.x, lo2.y, hi2.x, hi2.y);
         o[dg] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(pop), m_as_bf16x8(vop), o[dg],
                                                         0, 0, 0);
@@ -758,7 +806,7 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
   // ---- merge the 4 wavefront states --------------------------------------
   const float l_w = l_lane + __shfl_xor(l_lane, 16);
   const float l_h = l_w + __shfl_xor(l_w, 32);
-  // no DMA may land in the V tiles once they hold the merge states
+  // no DMA may land in the tiles once they hold the merge states
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
   __syncthreads();
   float* mo = reinterpret_cast<float*>(&v_lds[0][0]);  // [kNW][G][D]
@@ -810,23 +858,25 @@ __global__ void __launch_bounds__(kThreads, 2) decode_mfma_kernel(DecodeParams p
 template <typename KV, int D, int G>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   dim3 grid(p.S, p.Hkv, p.B);
-  // MFMA kernel: always for G 8 (the VALU kernel is compute-bound there:
-  // 119 against 81 us on the 32 x 4k batch with 64 query heads, 366 against
-  // 284 us on the 131k-token batch); for G 4 when each sequence takes at most
-  // four splits (79 against 84 us on the 32 x 4k batch), while on long,
-  // many-split contexts the VALU kernel's full-row loads measured faster
-  // (289 against 298 us on the lognormal batch, 241 against 274 us on the
-  // 131k-token layout with 32 query heads).
+  // The MFMA kernel whenever it is built for the shape (bf16, D 128, G 4 or
+  // 8): the VALU kernel is compute-bound at G 8 and, with whole-row V
+  // loads in the MFMA kernel, also slower at G 4 (cold caches: 84 against
+  // 80 us on the 32 x 4k batch, 254 against 241 us on the lognormal batch,
+  // 199 against ~190 us on the 131k-token layout with 32 query heads).
   // A caller may also ask for one kernel explicitly (msa_decode_kernel); the
   // API has checked that the matrix-core kernel exists for the shape.
   bool mfma = false;
   if constexpr (std::is_same<KV, uint16_t>::value && D == kMD && (G == 4 || G == 8))
-    mfma = p.kernel == MSA_DECODE_MATRIX ? true
-         : p.kernel == MSA_DECODE_VECTOR ? false
-         : (G == 8 || p.S <= 4);
+    mfma = p.kernel != MSA_DECODE_VECTOR;
   if (mfma) {
-    if constexpr (std::is_same<KV, uint16_t>::value && D == kMD && (G == 4 || G == 8))
-      hipLaunchKernelGGL((decode_mfma_kernel<G>), grid, dim3(kThreads), 0, stream, p);
+    if constexpr (std::is_same<KV, uint16_t>::value && D == kMD && (G == 4 || G == 8)) {
+      // K by row DMA when the grid is at most one workgroup per CU, where
+      // its extra LDS costs no occupancy
+      if (int64_t(p.S) * p.Hkv * p.B <= kCUs)
+        hipLaunchKernelGGL((decode_mfma_kernel<G, true>), grid, dim3(kThreads), 0, stream, p);
+      else
+        hipLaunchKernelGGL((decode_mfma_kernel<G, false>), grid, dim3(kThreads), 0, stream, p);
+    }
   } else {
     hipLaunchKernelGGL((decode_kernel<KV, D, G>), grid, dim3(kThreads), 0, stream, p);
   }

@@ -1,9 +1,9 @@
 // a5: log-sum-exp merge of attention partials.
 //
-// out += attention_kernel(Q, seg.K, seg.V) * normalizer(seg)  (P1, "Core
-// method 1: MSA" pseudocode).  The pages leave normalizer(seg) undefined;
-// it is read here as the log-sum-exp weight, which makes the stitched result
-// equal to attention over the union of the keys:
+// The MSA pseudocode (P1, "Core method 1: MSA") adds up per-segment
+// attention results, each scaled by a per-segment normaliser that the pages
+// do not define.  It is read here as the log-sum-exp weight, which makes the
+// stitched result equal to attention over the union of the keys:
 //   M = max_i m_i,  w_i = exp(m_i - M) (0 for an empty partial),
 //   L = sum_i w_i l_i,  out = sum_i w_i o_i / L,  lse = M + ln L.
 // Partials are visited in their stored (logical) order, so the result is

@@ -101,9 +101,9 @@ def test_decode_cfg2_full():
 @pytest.mark.parametrize("split_blocks", [64, 16])
 def test_decode_cfg2_full_forced_splits(split_blocks):
     """The headline batch needs no merge under the automatic split rule; forced
-    splits of 64 blocks (4 per sequence, matrix-core kernel + merge) and 16
-    blocks (16 per sequence, vector kernel + merge) cover those paths at full
-    size."""
+    splits of 64 blocks (4 per sequence: 1024 workgroups, so the matrix-core
+    kernel reads K into registers) and 16 blocks (16 per sequence) cover the
+    split and merge paths at full size."""
     w = make_workload(2, seed=0)
     O, L = run_decode(w, split_blocks)
     check(w, O, L)
@@ -164,9 +164,9 @@ def _decode_both_layouts(w, split_blocks):
 def test_decode_head_major_layout(cfg, split_blocks):
     """Pools in head-major blocks [P, Hkv, 16, D] (msa_decode_ex): the same
     values give bitwise the same O and LSE as the token-major layout, and
-    both match the oracle.  Covers the VALU kernel (fp32; grouped heads with
-    many splits), the MFMA kernel for 4 and 8 heads per KV head, and the
-    split merge."""
+    both match the oracle.  Covers the VALU kernel (fp32), the MFMA kernel
+    for 4 and 8 heads per KV head (K by row DMA on one-workgroup-per-CU
+    grids, in registers otherwise), and the split merge."""
     w = make_workload(cfg, seed=6, size="small")
     (o_n, l_n), (o_h, l_h) = _decode_both_layouts(w, split_blocks)
     assert torch.equal(o_n, o_h) and torch.equal(l_n, l_h)
