@@ -199,6 +199,26 @@ int msa_decode_ex(const void* q, const void* k_pool, const void* v_pool, int32_t
                   void* workspace, size_t workspace_bytes, msa_kv_layout kv_layout,
                   msa_decode_kernel kernel, int32_t* dev_error, void* stream);
 
+/* msa_decode for callers that cannot allocate device memory at call time
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid
+ * allocation): no workspace argument; the split partials go to a
+ * library-owned device array of msa_decode_noalloc_capacity() bytes
+ * (32 MiB), one per GPU, held until the process ends.  Everything else --
+ * arguments, kernels, results, errors -- is msa_decode's.  Returns
+ * MSA_ERR_CAPACITY when msa_decode_workspace_size for the same arguments
+ * exceeds the array, MSA_ERR_DEVICE if its device address cannot be looked
+ * up.  The array's address is looked up once per device on the first call
+ * that needs it, for the current device, which must be the device of
+ * `stream`.  No call allocates.  All calls on one GPU share the array:
+ * calls that overlap in time on the same GPU race on it and must be ordered
+ * by the caller (one stream, or events). */
+size_t msa_decode_noalloc_capacity(void);
+int msa_decode_noalloc(const void* q, const void* k_pool, const void* v_pool,
+                       int32_t num_phys_blocks, int32_t block_size, const msa_segment* segs,
+                       const int32_t* seg_indptr, int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
+                       int32_t max_ctx_len, msa_dtype dtype, float scale, int32_t split_blocks,
+                       void* out, float* lse_out, int32_t* dev_error, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* a2+a4(+a5): chunked prefill                                               */
 /* ------------------------------------------------------------------------ */

@@ -50,6 +50,9 @@ SIGNATURES = {
     "msa_decode_ex": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _i32, _i32,
                                      ctypes.c_int, _f, _i32, _p, _p, _p, _sz, ctypes.c_int,
                                      ctypes.c_int, _p, _p]),
+    "msa_decode_noalloc_capacity": (_sz, []),
+    "msa_decode_noalloc": (ctypes.c_int, [_p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32, _i32,
+                                          _i32, ctypes.c_int, _f, _i32, _p, _p, _p, _p]),
     "msa_prefill_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32, _i32]),
     "msa_prefill_chunk": (ctypes.c_int, [_p, _i32, _p, _p, _p, _i32, _i32, _p, _p, _i32, _i32, _i32,
                                          _i32, _i32, ctypes.c_int, _f, _i32, _p, _p, _p, _sz, _p,
