@@ -7,11 +7,12 @@ plan (msa_plan_segments) followed by decode attention with its split-K merge
 heads, head_dim 128, 4096-token contexts, block size 16, 20% of blocks evicted
 in geometric runs).  Inputs are resident in HBM before the timed region.
 
-Timing is cold by default: before every timed step or call a 1 GiB read
-evicts L2 and the 256 MB Infinity Cache (outside the timed region), so each
-call streams its K/V from HBM, as it does in a model where other layers run
-between two attention calls.  Back-to-back (warm) figures are reported beside
-the cold ones.  GPU times come from HIP events on the launch stream.
+Timing is cold by default: before every timed step or call a 512 MiB read
+evicts L2 and the 256 MB Infinity Cache, so each call streams its K/V from
+HBM, as it does in a model where other layers run between two attention
+calls; the flush's own time is taken off (see cold_times).  Back-to-back
+(warm) figures are reported beside the cold ones.  GPU times come from HIP
+events (created without the system-scope fence) on the launch stream.
 
 Printed: ONE JSON line with the decode KV GB/s (value, cold), tokens/s, % of
 HBM peak, a roofline object for the dominant call, the fp64 oracle timed on
@@ -46,7 +47,7 @@ COUNTERS = os.path.join(ROOT, "profiles", "decode_cfg2_counters.json")
 DECODE_SOURCES = ["decode.hip", "merge.hip", "msa_internal.h"]
 PF_COUNTERS = os.path.join(ROOT, "profiles", "prefill_cfg3_counters.json")
 PREFILL_SOURCES = ["prefill.hip", "msa_internal.h"]
-FLUSH_BYTES = 1 << 30  # > L2 + Infinity Cache (256 MB)
+FLUSH_BYTES = 512 << 20  # twice the Infinity Cache (256 MB), far above L2
 
 ONLY = ("decode", "decode-warm", "decode4", "decode5", "prefill", "kernels")
 
@@ -294,23 +295,70 @@ class GatherBaseline:
 # timing
 # --------------------------------------------------------------------------
 
+HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000  # hipEventDisableSystemFence (hip_runtime_api.h)
+
+
+class HipEvent:
+    """A HIP timing event created with hipEventDisableSystemFence.  A default
+    event record performs a system-scope fence (cache write-back and
+    invalidation) that leaves the GPU idle for about 6 us before the next
+    dispatch, which a single-kernel interval would include; timing events
+    need no such fence (elapsed times are read after a stream
+    synchronize)."""
+    _hip = None
+
+    def __init__(self):
+        import ctypes
+        if HipEvent._hip is None:
+            hip = ctypes.CDLL("libamdhip64.so")
+            hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
+            hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+            hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+            hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+            HipEvent._hip = hip
+        self.ev = ctypes.c_void_p()
+        st = HipEvent._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), HIP_EVENT_DISABLE_SYSTEM_FENCE)
+        if st != 0:
+            raise RuntimeError(f"hipEventCreateWithFlags failed: {st}")
+
+    def record(self, stream):
+        import ctypes
+        st = HipEvent._hip.hipEventRecord(self.ev, ctypes.c_void_p(stream.cuda_stream))
+        if st != 0:
+            raise RuntimeError(f"hipEventRecord failed: {st}")
+
+    def elapsed_s(self, end):
+        """Seconds from this event to `end`; the stream must have been
+        synchronized after both were recorded."""
+        import ctypes
+        ms = ctypes.c_float()
+        st = HipEvent._hip.hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        if st != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed: {st}")
+        return ms.value * 1e-3
+
+    def __del__(self):
+        if HipEvent._hip is not None and self.ev:
+            HipEvent._hip.hipEventDestroy(self.ev)
+
+
 def time_calls(fn, n, stream):
     """Average duration (s) of fn() over n back-to-back (warm) calls, from HIP
     events recorded on the launch stream."""
-    import torch
-    e0 = torch.cuda.Event(enable_timing=True)
-    e1 = torch.cuda.Event(enable_timing=True)
+    e0, e1 = HipEvent(), HipEvent()
     e0.record(stream)
     for _ in range(n):
         fn()
     e1.record(stream)
-    e1.synchronize()
-    return e0.elapsed_time(e1) / n * 1e-3
+    stream.synchronize()
+    return e0.elapsed_s(e1) / n
 
 
 class Flush:
-    """A 1 GiB read that evicts L2 and the Infinity Cache.  A read leaves
-    clean lines, so the timed call after it pays no write-back."""
+    """A 512 MiB read that evicts L2 and the Infinity Cache (a 1 GiB read gives
+    the same cold times).  A read leaves clean lines, so the timed call
+    after it pays no write-back."""
 
     def __init__(self):
         import torch
@@ -323,19 +371,51 @@ class Flush:
 
 
 def cold_times(fn, n, stream, flush):
-    """Durations (s) of n calls of fn(), each after a cache flush (outside the
-    events) and timed alone between its own pair of HIP events."""
-    import torch
+    """Durations (s) of n cold calls of fn(): the HIP events bracket [flush,
+    fn()] and, interleaved with it (order alternating), [flush] alone, and the
+    mean flush time is taken off each bracketed pair.  An event record
+    directly before a dispatch leaves the GPU idle for about 4.5 us (against
+    about 1 us between back-to-back kernels), so a bracket around fn() alone
+    would overstate a short call; here that cost sits in both brackets and
+    cancels, while the ordinary kernel-to-kernel transition after the flush
+    stays in, as it would after any kernel of a model."""
     ts = []
+    ev = [HipEvent() for _ in range(4)]
+    for i in range(n):
+        for first in ((True, False) if i % 2 == 0 else (False, True)):
+            a, b = (ev[0], ev[1]) if first else (ev[2], ev[3])
+            a.record(stream)
+            flush()
+            if first:
+                fn()
+            b.record(stream)
+        stream.synchronize()
+        # the two brackets of one pair ran back to back: their difference
+        ts.append(ev[0].elapsed_s(ev[1]) - ev[2].elapsed_s(ev[3]))
+    return ts
+
+
+def tmean(ts, cut=0.1):
+    """Mean of ts without its lowest and highest `cut` fraction (a stray
+    host or clock hiccup in one pair of brackets does not move it)."""
+    s = sorted(ts)
+    k = int(len(s) * cut)
+    return statistics.fmean(s[k:len(s) - k] if len(s) > 2 * k else s)
+
+
+def cold_times_direct(fn, n, stream, flush):
+    """Durations (s) of n calls of fn(), each after a flush, each timed by a
+    pair of HIP events directly around it (includes the event-to-dispatch
+    idle gap; reported beside cold_times for reference)."""
+    ts = []
+    e0, e1 = HipEvent(), HipEvent()
     for _ in range(n):
         flush()
-        e0 = torch.cuda.Event(enable_timing=True)
-        e1 = torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         fn()
         e1.record(stream)
-        e1.synchronize()
-        ts.append(e0.elapsed_time(e1) * 1e-3)
+        stream.synchronize()
+        ts.append(e0.elapsed_s(e1))
     return ts
 
 
@@ -343,7 +423,7 @@ def dist_us(ts):
     s = sorted(ts)
     n = len(s)
     q = lambda f: s[min(n - 1, int(round(f * (n - 1))))] * 1e6
-    return {"mean": round(statistics.fmean(s) * 1e6, 3), "p10": round(q(0.1), 3),
+    return {"mean": round(tmean(s) * 1e6, 3), "p10": round(q(0.1), 3),
             "p50": round(q(0.5), 3), "p90": round(q(0.9), 3), "calls": n}
 
 
@@ -462,7 +542,9 @@ def decode_roofline(alg_bytes, cold_mean_s, warm_s, traffic=None, kernel="msa_de
     a = alg_bytes / cold_mean_s / 1e9
     return {"bound": "hbm", "achieved": round(a, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
             "frac": round(a / HBM_PEAK_GBS, 4), "traffic": traffic, "traffic_unit": "bytes per call",
-            "kernel": kernel, "timing": "cold (1 GiB read flush before each call), mean of the calls",
+            "kernel": kernel,
+            "timing": "cold: HIP events (no system fence) around [512 MiB read flush + call] minus the "
+                      "same around [flush] alone, pairs interleaved; 10%-trimmed mean over the calls",
             "algorithmic_bytes_per_call": int(alg_bytes), "us_per_call": round(cold_mean_s * 1e6, 3),
             "warm": {"achieved": round(alg_bytes / warm_s / 1e9, 2),
                      "frac": round(alg_bytes / warm_s / 1e9 / HBM_PEAK_GBS, 4),
@@ -481,7 +563,7 @@ def decode_leg(w, n, flush, split_blocks=0, kv_layout=0, kernel=0, unique=False,
     cold = cold_times(prep.attention, n, prep.stream, flush)
     warm_s = time_calls(prep.attention, n, prep.stream)
     alg = decode_bytes(w)
-    cold_mean = statistics.fmean(cold)
+    cold_mean = tmean(cold)
     leg = {"us_per_call": round(cold_mean * 1e6, 3), "cold_us": dist_us(cold),
            "warm_us_per_call": round(warm_s * 1e6, 3),
            "GB/s": round(alg / cold_mean / 1e9, 2), "pct_hbm_peak": round(100 * alg / cold_mean / 8e12, 2),
@@ -617,7 +699,7 @@ def eviction_leg(args, flush, w):
         segs = int(prep.indptr[-1].item())
         del prep
         return {"alive_tokens": int(sum(alive_tokens_per_seq(wv))), "segments": segs,
-                "us": round(statistics.fmean(ts) * 1e6, 3)}
+                "us": round(tmean(ts) * 1e6, 3)}
 
     # fit points: extra evictions of single random blocks (more segments) and
     # of whole alive runs (fewer segments) at three fractions each
@@ -799,7 +881,7 @@ def main(argv=None):
     step_ts = cold_times(prep.step, args.steps, stream, flush)
     torch.cuda.synchronize()
     bracket_s = time.perf_counter() - t0
-    step_s = statistics.fmean(step_ts)
+    step_s = tmean(step_ts)
     # the same K steps back to back (warm)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -809,10 +891,11 @@ def main(argv=None):
     warm_step_s = (time.perf_counter() - t0) / args.steps
     prep.check_error()
     # dominant call: msa_decode (decode kernel + split merge), cold and warm
-    dec_cold = cold_times(prep.attention, args.steps, stream, flush)
+    # (at least 60 pairs: each pair difference carries the flush's jitter)
+    dec_cold = cold_times(prep.attention, max(args.steps, 60), stream, flush)
     dec_warm_s = time_calls(prep.attention, args.steps, stream)
     plan_s = time_calls(prep.plan, args.steps, stream)
-    dec_mean = statistics.fmean(dec_cold)
+    dec_mean = tmean(dec_cold)
     out_headline = prep.out.clone()
     traffic = counter_traffic(COUNTERS, DECODE_SOURCES, split_blocks=args.split_blocks,
                               kv_layout=args.kv_layout)
@@ -828,9 +911,10 @@ def main(argv=None):
                    "alive_tokens": int(sum(alive_tokens_per_seq(w2))), "segments": nseg,
                    "kv_layout": "[P, Hkv, 16, D]" if head_major else "[P, 16, Hkv, D]",
                    "step": "msa_plan_segments + msa_decode (decode kernel + split-K merge)",
-                   "timing": "cold: a 1 GiB read evicts L2 and the Infinity Cache before each step "
-                             "(outside the step's HIP events); value and ms_per_step are the mean "
-                             "over the K steps",
+                   "timing": "cold: a 512 MiB read evicts L2 and the Infinity Cache before each step; "
+                             "each step's time is the HIP-event interval of [flush + step] minus that "
+                             "of [flush] alone (pairs interleaved); value and ms_per_step use the "
+                             "10%-trimmed mean over the K steps",
                    "seed": args.seed, "parallelism": "single GPU"},
         "tokens_per_s": round(w2.B / step_s, 1),
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBS, 2),
@@ -854,14 +938,14 @@ def main(argv=None):
             gb.step()
         torch.cuda.synchronize()
         n = max(10, args.steps // 2)
-        g_step = statistics.fmean(cold_times(gb.step, n, stream, flush))
-        g_copy = statistics.fmean(cold_times(gb.gather, n, stream, flush))
+        g_step = tmean(cold_times(gb.step, n, stream, flush))
+        g_copy = tmean(cold_times(gb.gather, n, stream, flush))
         g_attn = time_calls(gb.attention, n, stream)
         result["gather_baseline"] = {
             "us_per_call": round(g_step * 1e6, 3), "gather_us": round(g_copy * 1e6, 3),
             "dense_decode_us_warm": round(g_attn * 1e6, 3), "msa_decode_us": round(dec_mean * 1e6, 3),
             "msa_speedup": round(g_step / dec_mean, 3),
-            "note": "cold: gather alive K/V blocks into dense pools (msa_gather_alive) + msa_decode "
+            "note": "cold (flush-subtracted): gather alive K/V blocks into dense pools (msa_gather_alive) + msa_decode "
                     "over one segment per sequence, vs msa_decode over the segments"}
         del gb
         torch.cuda.empty_cache()
@@ -980,7 +1064,7 @@ def latency_model_leg(args, flush):
             prep.plan()
             prep.attention()
             prep.check_error()
-            t = statistics.fmean(cold_times(prep.attention, 20, prep.stream, flush))
+            t = tmean(cold_times(prep.attention, 20, prep.stream, flush))
             pts.append({"ctx": ctx, "mean_alive_run": run, "alive_tokens": int(sum(alive_tokens_per_seq(w))),
                         "segments": int(prep.indptr[-1].item()), "us": round(t * 1e6, 3)})
             del prep, w
