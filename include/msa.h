@@ -302,10 +302,11 @@ int32_t msa_prefill_chunk_rows(int32_t B, int32_t Hq, int32_t Hkv, int32_t remai
  *   o_part  float32 [N, R, H, D]   unnormalised output  sum_j exp(s_j - m) v_j
  *   m_part  float32 [N, R, H]      running max m (natural-log units; -inf = empty)
  *   l_part  float32 [N, R, H]      sum_j exp(s_j - m)
- * merged in that (logical) order:
+ * merged (in a fixed order, so deterministically):
  *   M = max_i m_i,  w_i = exp(m_i - M) (0 if m_i = -inf),  L = sum_i w_i l_i,
  *   out = sum_i w_i o_i / L,  lse = M + ln L;  all empty -> out 0, lse -inf.
- * o_part of an empty partial is never read.
+ * o_part of an empty partial (m = -inf) may hold anything (NaN included): it
+ * is read but never used.
  *   out  [B, R, H, D] out_dtype      lse_out [B, R, H] float32, may be NULL
  * R is 1 for decode and C for prefill. */
 int msa_merge_partials(const float* o_part, const float* m_part, const float* l_part,

@@ -6,19 +6,26 @@
 // stitched result equal to attention over the union of the keys:
 //   M = max_i m_i,  w_i = exp(m_i - M) (0 for an empty partial),
 //   L = sum_i w_i l_i,  out = sum_i w_i o_i / L,  lse = M + ln L.
-// Partials are visited in their stored (logical) order, so the result is
-// deterministic run to run.
+// The combination order is fixed (below), so the result is deterministic
+// run to run; mathematically it does not depend on the order.
 //
-// One workgroup covers 128 consecutive (head, d) elements of one (sequence,
-// row); every thread folds the sequence's partials for its element in one
-// pass with a running maximum, eight partials' loads in flight at a time.
+// One workgroup covers 256/NG consecutive (head, d) elements of one
+// (sequence, row) with 256 threads: thread (group j, element e) folds
+// partials j, j+NG, j+2NG, ... of element e with a running maximum, and the
+// NG group states of an element are then combined in LDS in group order.
+// The merge is bound by how many loads are in flight, not by arithmetic:
+// one thread per element folding all of a sequence's partials (69 per
+// sequence on the 131k-token batch) kept too few loads outstanding (9.5 us
+// for 9 MB of partials).  NG follows the split count (1 up to 4 partials per
+// sequence, 2 up to 16, 4 up to 32, else 8): more groups than partials only
+// multiply workgroups that have nothing to do.
 #include "msa_internal.h"
 
 namespace msa {
 namespace {
 
-constexpr int kThreads = 128;
-constexpr int kUnroll = 8;  // partials whose loads are issued together
+constexpr int kThreads = 256;
+constexpr int kUnroll = 4;  // a thread's partials loaded together
 constexpr float kLog2e = 1.44269504088896340736f;
 constexpr float kLn2 = 0.69314718055994530942f;
 
@@ -44,10 +51,28 @@ struct MergeArgs {
   float* lse;
 };
 
-template <int MODE>
+// (M, L, O) <- (M, L, O) (+) (m2, l2, o2), log2 units; an empty state has
+// M = -inf and contributes nothing
+__device__ __forceinline__ void fold(float& M, float& L, float& O, float m2, float l2, float o2) {
+  if (m2 == -INFINITY) return;
+  if (m2 > M) {
+    const float sc = M == -INFINITY ? 0.f : exp2f(M - m2);
+    L *= sc;
+    O *= sc;
+    M = m2;
+  }
+  const float w = exp2f(m2 - M);
+  L = fmaf(w, l2, L);
+  O = fmaf(w, o2, O);
+}
+
+template <int MODE, int NG>
 __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
+  constexpr int kGroups = NG, kElems = kThreads / NG;
+  __shared__ float sM[kGroups][kElems], sL[kGroups][kElems], sO[kGroups][kElems];
   const int b = blockIdx.z, r = blockIdx.y;
-  const int e = blockIdx.x * kThreads + threadIdx.x;
+  const int el = threadIdx.x % kElems, grp = threadIdx.x / kElems;
+  const int e = blockIdx.x * kElems + el;
   const int HD = a.H * a.D;
   int lo, n;
   if (MODE == 0) {
@@ -61,41 +86,55 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
     if (n == 1) return;  // the attention kernel wrote this sequence itself
     lo = b * a.S;
   }
-  if (e >= HD) return;
-  const int h = e / a.D, d = e % a.D;
-  const size_t orow = (size_t(b) * a.R + r) * a.H + h;
-  // running (M, L, O) in log2 units; a partial with a larger maximum rescales
-  // what was folded so far, exactly as the two-pass form would weight it
+  const bool valid = e < HD;
+  const int ec = valid ? e : 0;
+  const int h = ec / a.D, d = ec % a.D;
+  const size_t stride = size_t(a.R) * a.H;  // between consecutive partials' (row, head)
+  const size_t first = (size_t(lo) * a.R + r) * a.H + h;
+  // this thread's partials: grp, grp + 8, ... in order, with a running maximum
   float M = -INFINITY, L = 0.f, O = 0.f;
-  for (int i0 = 0; i0 < n; i0 += kUnroll) {
+  for (int i0 = grp; i0 < n; i0 += kGroups * kUnroll) {
     float mi[kUnroll], li[kUnroll], oi[kUnroll];
 #pragma unroll
     for (int k = 0; k < kUnroll; ++k) {
-      const bool in = i0 + k < n;
-      const size_t pr = (size_t(lo + (in ? i0 + k : 0)) * a.R + r) * a.H + h;
+      const int i = i0 + k * kGroups;
+      const bool in = valid && i < n;
+      const size_t pr = first + size_t(in ? i : 0) * stride;
       mi[k] = in ? a.m_part[pr] : -INFINITY;
       li[k] = in ? a.l_part[pr] : 0.f;
-      oi[k] = in ? a.o_part[pr * a.D + d] : 0.f;
+      oi[k] = in ? a.o_part[pr * a.D + d] : 0.f;  // used only if m_i > -inf
     }
 #pragma unroll
-    for (int k = 0; k < kUnroll; ++k) {
-      if (mi[k] == -INFINITY) continue;  // empty partial: its o is never used
-      const float m2 = mi[k] * kLog2e;
-      if (m2 > M) {
-        const float sc = M == -INFINITY ? 0.f : exp2f(M - m2);
-        L *= sc;
-        O *= sc;
-        M = m2;
-      }
-      const float wi = exp2f(m2 - M);
-      L = fmaf(wi, li[k], L);
-      O = fmaf(wi, oi[k], O);
-    }
+    for (int k = 0; k < kUnroll; ++k)
+      fold(M, L, O, mi[k] == -INFINITY ? -INFINITY : mi[k] * kLog2e, li[k], oi[k]);
   }
+  sM[grp][el] = M;
+  sL[grp][el] = L;
+  sO[grp][el] = O;
+  __syncthreads();
+  if (grp != 0 || !valid) return;
+  // combine the groups in order (deterministic run to run)
+#pragma unroll
+  for (int j = 1; j < kGroups; ++j) fold(M, L, O, sM[j][el], sL[j][el], sO[j][el]);
+  const size_t orow = (size_t(b) * a.R + r) * a.H + h;
   const bool ok = L > 0.f;
   store_o(a.out, orow * a.D + d, ok ? O / L : 0.f, a.out_dtype);
   if (a.lse && d == 0) a.lse[orow] = ok ? (M + log2f(L)) * kLn2 : -INFINITY;
 }
+
+template <int MODE>
+hipError_t launch_ng(const MergeArgs& a, int groups, hipStream_t stream) {
+  const int HD = a.H * a.D;
+  switch (groups) {
+    case 1: hipLaunchKernelGGL((merge_kernel<MODE, 1>), dim3((HD + 255) / 256, a.R, a.B), dim3(kThreads), 0, stream, a); break;
+    case 2: hipLaunchKernelGGL((merge_kernel<MODE, 2>), dim3((HD + 127) / 128, a.R, a.B), dim3(kThreads), 0, stream, a); break;
+    case 4: hipLaunchKernelGGL((merge_kernel<MODE, 4>), dim3((HD + 63) / 64, a.R, a.B), dim3(kThreads), 0, stream, a); break;
+    default: hipLaunchKernelGGL((merge_kernel<MODE, 8>), dim3((HD + 31) / 32, a.R, a.B), dim3(kThreads), 0, stream, a); break;
+  }
+  return hipGetLastError();
+}
+
+int groups_for(int partials) { return partials <= 4 ? 1 : partials <= 16 ? 2 : partials <= 32 ? 4 : 8; }
 
 }  // namespace
 
@@ -106,9 +145,7 @@ hipError_t launch_merge_from_plan(const float* o_part, const float* m_part, cons
                                   float* lse, hipStream_t stream) {
   MergeArgs a{o_part, m_part, l_part, nullptr, segs, indptr, S, split_blocks,
               B, R, H, D, out_dtype, out, lse};
-  dim3 grid((H * D + kThreads - 1) / kThreads, R, B);
-  hipLaunchKernelGGL(merge_kernel<1>, grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  return launch_ng<1>(a, groups_for(S), stream);
 }
 
 hipError_t launch_merge_indptr(const float* o_part, const float* m_part, const float* l_part,
@@ -117,9 +154,8 @@ hipError_t launch_merge_indptr(const float* o_part, const float* m_part, const f
                                hipStream_t stream) {
   MergeArgs a{o_part, m_part, l_part, part_indptr, nullptr, nullptr, 0, 0,
               B, R, H, D, out_dtype, out, lse};
-  dim3 grid((H * D + kThreads - 1) / kThreads, R, B);
-  hipLaunchKernelGGL(merge_kernel<0>, grid, dim3(kThreads), 0, stream, a);
-  return hipGetLastError();
+  // the partial counts are on the device: four groups of partials
+  return launch_ng<0>(a, 4, stream);
 }
 
 }  // namespace msa
