@@ -86,9 +86,17 @@ typedef enum { MSA_LAYOUT_NHD = 0, MSA_LAYOUT_HND = 1 } msa_kv_layout;
 
 /* Which decode kernel runs (msa_decode_ex).  AUTO picks per shape and split
  * count; VECTOR is the vector-ALU kernel (every supported shape); MATRIX the
- * matrix-core kernel, built for bf16 with D 128 and Hq/Hkv 4 or 8 only
- * (MSA_ERR_UNSUPPORTED otherwise). */
-typedef enum { MSA_DECODE_AUTO = 0, MSA_DECODE_VECTOR = 1, MSA_DECODE_MATRIX = 2 } msa_decode_kernel;
+ * matrix-core kernel with one workgroup per (sequence, KV head, split),
+ * built for bf16 with D 128 and Hq/Hkv 4 or 8 only; BLOCK the matrix-core
+ * kernel with one workgroup per (sequence, split) that streams whole KV
+ * blocks for all KV heads, built for bf16, D 128, Hkv 8, Hq/Hkv 4 or 8 and
+ * B <= 1024 (MSA_ERR_UNSUPPORTED otherwise). */
+typedef enum {
+  MSA_DECODE_AUTO = 0,
+  MSA_DECODE_VECTOR = 1,
+  MSA_DECODE_MATRIX = 2,
+  MSA_DECODE_BLOCK = 3
+} msa_decode_kernel;
 
 /* One segment: a maximal run of alive blocks of one sequence that are
  * consecutive both in logical index and in physical id.  24 bytes, plain

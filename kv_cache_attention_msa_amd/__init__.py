@@ -21,14 +21,15 @@ import torch
 from . import _lib
 from ._lib import (MsaError, MSA_F32, MSA_BF16, MSA_DEVERR_PHYS_RANGE, MSA_DEVERR_CAPACITY,
                    MSA_DEVERR_CTX_RANGE, MSA_DEVERR_TRUNCATED, MSA_LAYOUT_NHD, MSA_LAYOUT_HND,
-                   MSA_DECODE_AUTO, MSA_DECODE_VECTOR, MSA_DECODE_MATRIX)
+                   MSA_DECODE_AUTO, MSA_DECODE_VECTOR, MSA_DECODE_MATRIX,
+                   MSA_DECODE_BLOCK)
 
 __all__ = ["msa_plan_segments", "msa_decode", "msa_prefill_chunk", "msa_merge_partials",
            "msa_prefill_chunk_rows",
            "msa_plan_workspace_size", "msa_decode_workspace_size", "msa_prefill_workspace_size",
            "MsaError", "MSA_F32", "MSA_BF16", "MSA_DEVERR_PHYS_RANGE", "MSA_DEVERR_CAPACITY",
            "MSA_DEVERR_CTX_RANGE", "MSA_DEVERR_TRUNCATED", "MSA_LAYOUT_NHD", "MSA_LAYOUT_HND",
-           "MSA_DECODE_AUTO", "MSA_DECODE_VECTOR", "MSA_DECODE_MATRIX", "SEG_FIELDS",
+           "MSA_DECODE_AUTO", "MSA_DECODE_VECTOR", "MSA_DECODE_MATRIX", "MSA_DECODE_BLOCK", "SEG_FIELDS",
            "library_path", "prefill_available", "decode_available"]
 
 SEG_FIELDS = ("seq", "logical_block", "phys_block", "num_blocks", "num_tokens",
@@ -113,7 +114,8 @@ def _nbytes(t):
 
 
 _LAYOUTS = {"NHD": MSA_LAYOUT_NHD, "HND": MSA_LAYOUT_HND}
-_KERNELS = {"auto": MSA_DECODE_AUTO, "vector": MSA_DECODE_VECTOR, "matrix": MSA_DECODE_MATRIX}
+_KERNELS = {"auto": MSA_DECODE_AUTO, "vector": MSA_DECODE_VECTOR, "matrix": MSA_DECODE_MATRIX,
+            "block": MSA_DECODE_BLOCK}
 
 
 def _pool_dims(k_pool, kv_layout):
@@ -197,8 +199,8 @@ def msa_decode(q: torch.Tensor, k_pool: torch.Tensor, v_pool: torch.Tensor, segs
                want_lse: bool = True, kv_layout: str = "NHD", kernel: str = "auto",
                dev_error: torch.Tensor | None = None, stream=None):
     """Decode attention.  q [B, Hq, D]; pools [P, 16, Hkv, D] (kv_layout "NHD")
-    or [P, Hkv, 16, D] ("HND"), same dtype as q.  kernel: "auto", "vector" or
-    "matrix" (msa_decode_kernel).  dev_error: optional int32 [1] device word
+    or [P, Hkv, 16, D] ("HND"), same dtype as q.  kernel: "auto", "vector",
+    "matrix" or "block" (msa_decode_kernel).  dev_error: optional int32 [1] device word
     into which MSA_DEVERR_TRUNCATED is ORed (pass the plan's).
     Returns (out [B, Hq, D], lse [B, Hq] float32 or None)."""
     lib = _lib_handle()

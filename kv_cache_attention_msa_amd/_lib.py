@@ -31,6 +31,7 @@ MSA_DEVERR_TRUNCATED = 8
 MSA_DECODE_AUTO = 0    # decode kernel chosen per shape and split count
 MSA_DECODE_VECTOR = 1  # vector-ALU decode kernel
 MSA_DECODE_MATRIX = 2  # matrix-core decode kernel (bf16, D 128, Hq/Hkv 4 or 8)
+MSA_DECODE_BLOCK = 3   # matrix-core decode kernel streaming whole KV blocks (bf16, D 128, Hkv 8, Hq/Hkv 4 or 8, B <= 1024)
 
 # every symbol include/msa.h declares, with (restype, argtypes)
 _i32 = ctypes.c_int32

@@ -48,6 +48,39 @@ int check_attn_shape(const void* q, const void* k_pool, const void* v_pool, int3
   return MSA_OK;
 }
 
+// The decode kernel a call runs: true for the block kernel.  Automatic
+// choice: the block kernel when the (sequence, KV head) pairs do not fill
+// the chip, so that the per-head kernels would split every sequence many
+// ways (4 x 131k tokens: 174 against 196 us cold).  With 256 pairs or more
+// the per-head kernels keep each pair in one workgroup or a few, and the
+// block kernel's per-workgroup set-up (about 10 us: plan reads, split
+// search, segment expansion, first block) and merge cost more than its
+// faster stream gains (32 x 4k: 80 against 76 us; 64 lognormal contexts:
+// 251 against 244 us).
+bool decode_uses_block(msa_decode_kernel kernel, msa_dtype dtype, int32_t B, int32_t Hq,
+                       int32_t Hkv, int32_t D) {
+  if (kernel == MSA_DECODE_BLOCK) return true;
+  if (kernel != MSA_DECODE_AUTO) return false;
+  return decode_block_supported(dtype, D, Hkv, Hq / Hkv, B) && int64_t(B) * Hkv < 256;
+}
+
+// block kernel workspace: partials of every workgroup of its grid, then the
+// per-sequence partial ranges
+struct BlockLayout {
+  PartLayout parts;
+  size_t indptr_off, total;
+  int64_t nwg;
+};
+inline BlockLayout block_layout(int32_t B, int32_t Hq, int32_t D, int32_t cap_blocks,
+                                int32_t split_blocks) {
+  BlockLayout L;
+  L.nwg = decode_block_grid(B, cap_blocks, split_blocks);
+  L.parts = part_layout(L.nwg, 1, Hq, D);
+  L.indptr_off = L.parts.total;
+  L.total = L.indptr_off + align_up(size_t(B + 1) * sizeof(int32_t));
+  return L;
+}
+
 inline float resolve_scale(float scale, int32_t D) {
   return scale > 0.f ? scale : 1.0f / sqrtf(float(D));
 }
@@ -117,8 +150,13 @@ size_t msa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                  int32_t max_ctx_len, int32_t block_size, int32_t split_blocks) {
   if (B <= 0 || Hq <= 0 || Hkv <= 0 || D <= 0 || block_size <= 0 || max_ctx_len < 0) return 0;
   const SplitPlan sp = decode_split(B, Hkv, max_ctx_len, block_size, split_blocks);
-  if (sp.S <= 1) return 0;
-  return part_layout(int64_t(B) * sp.S, 1, Hq, D).total;
+  size_t need = sp.S <= 1 ? 0 : part_layout(int64_t(B) * sp.S, 1, Hq, D).total;
+  // the block kernel may run for this shape (the dtype is not an argument)
+  if (Hq % Hkv == 0 && decode_block_supported(MSA_BF16, D, Hkv, Hq / Hkv, B)) {
+    const BlockLayout L = block_layout(B, Hq, D, sp.S * sp.split_blocks, split_blocks);
+    if (L.total > need) need = L.total;
+  }
+  return need;
 }
 
 int msa_decode_ex(const void* q, const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
@@ -131,17 +169,20 @@ int msa_decode_ex(const void* q, const void* k_pool, const void* v_pool, int32_t
                             Hq, Hkv, D, max_ctx_len, dtype, scale, split_blocks, out);
   if (st != MSA_OK) return st;
   if (kv_layout != MSA_LAYOUT_NHD && kv_layout != MSA_LAYOUT_HND) return MSA_ERR_INVALID_ARG;
-  if (kernel != MSA_DECODE_AUTO && kernel != MSA_DECODE_VECTOR && kernel != MSA_DECODE_MATRIX)
+  if (kernel != MSA_DECODE_AUTO && kernel != MSA_DECODE_VECTOR && kernel != MSA_DECODE_MATRIX &&
+      kernel != MSA_DECODE_BLOCK)
     return MSA_ERR_INVALID_ARG;
   if (!decode_supported(dtype, D, Hq / Hkv)) return MSA_ERR_UNSUPPORTED;
   if (kernel == MSA_DECODE_MATRIX && !decode_matrix_supported(dtype, D, Hq / Hkv))
+    return MSA_ERR_UNSUPPORTED;
+  if (kernel == MSA_DECODE_BLOCK && !decode_block_supported(dtype, D, Hkv, Hq / Hkv, B))
     return MSA_ERR_UNSUPPORTED;
   if (split_blocks > decode_max_split_blocks()) return MSA_ERR_INVALID_ARG;
   const SplitPlan sp = decode_split(B, Hkv, max_ctx_len, block_size, split_blocks);
   const size_t need = msa_decode_workspace_size(B, Hq, Hkv, D, max_ctx_len, block_size, split_blocks);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MSA_ERR_CAPACITY;
 
-  DecodeParams p;
+  DecodeParams p{};
   p.q = q;
   p.k_pool = k_pool;
   p.v_pool = v_pool;
@@ -162,6 +203,29 @@ int msa_decode_ex(const void* q, const void* k_pool, const void* v_pool, int32_t
   p.out = out;
   p.lse = lse_out;
   p.o_part = p.m_part = p.l_part = nullptr;
+  p.use_block = 0;
+  p.part_indptr = nullptr;
+  p.cap_blocks = sp.S * sp.split_blocks;
+  if (decode_uses_block(kernel, dtype, B, Hq, Hkv, D)) {
+    const BlockLayout L = block_layout(B, Hq, D, p.cap_blocks, split_blocks);
+    if (L.nwg > INT32_MAX) return MSA_ERR_UNSUPPORTED;
+    char* ws = static_cast<char*>(workspace);
+    p.use_block = 1;
+    p.nwg = int32_t(L.nwg);
+    p.block_auto = split_blocks == 0 ? 1 : 0;
+    p.block_target = decode_block_target(B);
+    p.o_part = reinterpret_cast<float*>(ws + L.parts.o_off);
+    p.m_part = reinterpret_cast<float*>(ws + L.parts.m_off);
+    p.l_part = reinterpret_cast<float*>(ws + L.parts.l_off);
+    p.part_indptr = reinterpret_cast<int32_t*>(ws + L.indptr_off);
+    hipError_t e = launch_decode(p, as_stream(stream));
+    if (e != hipSuccess) return MSA_ERR_DEVICE;
+    const int64_t per_seq = (L.nwg - B + B - 1) / B;
+    e = launch_merge_block(p.o_part, p.m_part, p.l_part, p.part_indptr, B, Hq, D,
+                           int32_t(per_seq < 1 ? 1 : per_seq), dtype, out, lse_out,
+                           as_stream(stream));
+    return e == hipSuccess ? MSA_OK : MSA_ERR_DEVICE;
+  }
   if (sp.S > 1) {
     const PartLayout L = part_layout(int64_t(B) * sp.S, 1, Hq, D);
     char* ws = static_cast<char*>(workspace);

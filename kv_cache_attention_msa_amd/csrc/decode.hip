@@ -855,6 +855,365 @@ __global__ void __launch_bounds__(kThreads, KDMA ? 1 : 2) decode_mfma_kernel(Dec
   }
 }
 
+// ---------------------------------------------------------------------------
+// decode_block_kernel: the matrix-core decode with one workgroup per
+// (sequence, split) that streams whole KV blocks, all KV heads at once.
+//
+// In the token-major pool a block of K (or V) is one contiguous 32 KB run
+// (16 slots x Hkv heads x 256 B).  The per-KV-head kernels above read one
+// head's 256-byte pieces of it, 2 KB apart, at times unrelated to the other
+// heads' workgroups; here eight wavefronts, one per KV head, pull the eight
+// pieces of every row within a few hundred cycles, so the DRAM sees the
+// whole block.  A streaming probe of the two orders (same bytes, no
+// attention math, cold caches) moved 6.5 against 4.1-5.8 TB/s on the 32 x 4k
+// batch and 6.9 against 3.9-5.6 TB/s on the 131k-token batch.
+//
+//   * Each wavefront owns one KV head and a two-stage ring of (K, V) blocks
+//     of that head (4 KB each) in LDS, filled by DMA in whole 256-byte rows
+//     (16 lanes per row, the slot swizzles of decode_mfma_kernel).  Block
+//     j+1 is requested before block j is waited for, so two blocks per
+//     wavefront are in flight; the ring is wavefront-private, so the loop
+//     has no barrier.  128 KB of ring: one workgroup per CU.
+//   * S = K Q^T per block on v_mfma_f32_16x16x32_bf16 (heads padded to 16
+//     rows); the lane's four weights are exactly the A operand of
+//     v_mfma_f32_16x16x16_bf16 for O += P V (k = the block's 16 keys).
+//   * Work split, on the device: every workgroup reads all B sequences'
+//     alive-token counts from the plan (one load pair per sequence) and
+//     picks the smallest split length T (at least kBMinSplit blocks) for
+//     which the splits, ceil(nA / T) near-equal ones per sequence, number at
+//     most `target` (one workgroup per CU): the host knows only max_ctx_len,
+//     not the eviction rate or the length mix.  An exclusive scan of the
+//     split counts numbers the splits; workgroup i takes split i, and
+//     workgroup 0 publishes the scan for the merge.
+// ---------------------------------------------------------------------------
+constexpr int kBThreads = 512;  // one wavefront per KV head
+constexpr int kBHkv = kBThreads / kWave;
+constexpr int kBMinSplit = 8;  // blocks: shorter splits cost more set-up than they balance
+
+__device__ __forceinline__ int wave_sum(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+// sum of one value per thread over the workgroup (red: kBHkv ints of LDS)
+__device__ __forceinline__ int block_sum(int v, int* red) {
+  v = wave_sum(v);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
+  __syncthreads();
+  int t = 0;
+#pragma unroll
+  for (int i = 0; i < kBHkv; ++i) t += red[i];
+  __syncthreads();
+  return t;
+}
+
+// exclusive prefix sum of one value per thread over the workgroup; `total`
+// gets the sum (red: kBHkv ints of LDS)
+__device__ __forceinline__ int block_excl_scan(int v, int* red, int& total) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  int x = v;
+#pragma unroll
+  for (int o = 1; o < kWave; o <<= 1) {
+    const int y = __shfl_up(x, o);
+    if (lane >= o) x += y;
+  }
+  if (lane == kWave - 1) red[w] = x;
+  __syncthreads();
+  int base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kBHkv; ++i) {
+    const int t = red[i];
+    base += i < w ? t : 0;
+    tot += t;
+  }
+  __syncthreads();
+  total = tot;
+  return base + x - v;
+}
+
+template <int G>
+__global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams p) {
+  static_assert(G == 4 || G == 8, "heads padded to 16 MFMA rows");
+  constexpr int D = kMD;
+  // [stage][K, V][wavefront] blocks of one head; during set-up the same
+  // bytes hold the staged segment list
+  __shared__ __align__(16) uint8_t kv_lds[2][2][kBHkv][kMBlock];
+  __shared__ __align__(16) int32_t blk_phys[kMaxSplitBlocks];
+  __shared__ int32_t s_alive[kDecodeBlockMaxSeq];      // alive tokens per sequence
+  __shared__ int32_t s_first[kDecodeBlockMaxSeq + 1];  // first split of each sequence
+  __shared__ int32_t s_red[kBHkv];
+  static_assert(sizeof(kv_lds) >= 3 * (kMaxSplitBlocks + 1) * sizeof(int32_t), "staging");
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int g = __builtin_amdgcn_readfirstlane(tid / kWave);  // this wavefront's KV head
+  const int hl = lane % 16, q4 = lane / 16;
+  const int B = p.B, id = blockIdx.x;
+
+  // ---- split counts of all sequences --------------------------------------
+  // thread t holds sequences [i0, i1)
+  const int per = (B + kBThreads - 1) / kBThreads;
+  const int i0 = min(B, tid * per), i1 = min(B, i0 + per);
+  int wsum = 0, nz = 0, cut = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int a0 = p.indptr[i], a1 = p.indptr[i + 1];
+    int A = 0;
+    if (a1 > a0) {
+      const msa_segment l = p.segs[a1 - 1];
+      A = max(0, l.alive_token_start + l.num_tokens);
+    }
+    s_alive[i] = A;
+    const int nb = (A + kBlk - 1) / kBlk;
+    const int nbc = min(nb, p.cap_blocks);
+    cut |= nb > nbc;
+    wsum += nbc;
+    nz += nbc > 0;
+  }
+  // splits of this thread's sequences at length T (an empty sequence still
+  // gets one workgroup: it writes O = 0)
+  auto splits_of = [&](int T) {
+    int n = 0;
+    for (int i = i0; i < i1; ++i) n += max(1, (min((s_alive[i] + kBlk - 1) / kBlk, p.cap_blocks) + T - 1) / T);
+    return n;
+  };
+  int T = p.split_blocks;
+  if (p.block_auto) {
+    const int W = block_sum(wsum, s_red);
+    const int NZ = block_sum(nz, s_red);
+    const int target = p.block_target;
+    // T_hi = ceil(W / (target - NZ)) always gives at most target + (B - NZ)
+    // splits (target >= 2B on the host); the smallest T that gives at most
+    // target lies in [ceil(W / target), T_hi]
+    int lo = max(kBMinSplit, (W + target - 1) / target);
+    int hi = max(kBMinSplit, (W + (target - NZ) - 1) / (target - NZ));
+    lo = min(lo, kMaxSplitBlocks);
+    hi = min(max(hi, lo), kMaxSplitBlocks);
+    while (lo < hi) {
+      const int mid = (lo + hi) >> 1;
+      if (block_sum(splits_of(mid), s_red) <= target) hi = mid; else lo = mid + 1;
+    }
+    T = lo;
+  }
+  int total;
+  int run = block_excl_scan(splits_of(T), s_red, total);
+  for (int i = i0; i < i1; ++i) {
+    s_first[i] = run;
+    run += max(1, (min((s_alive[i] + kBlk - 1) / kBlk, p.cap_blocks) + T - 1) / T);
+  }
+  if (tid == 0) s_first[B] = total;
+  const bool any_cut = __syncthreads_or(cut) != 0;
+  if (id == 0) {
+    // the merge reads these; clamped to the grid so that it can never read
+    // a partial outside the workspace (the sizing rule keeps total <= grid)
+    for (int i = tid; i <= B; i += kBThreads) p.part_indptr[i] = min(s_first[i], int(gridDim.x));
+    if (tid == 0 && p.dev_error && (any_cut || total > int(gridDim.x)))
+      atomicOr(p.dev_error, MSA_DEVERR_TRUNCATED);
+  }
+  if (id >= total) return;
+  int b = 0;
+  {
+    int hi = B;
+    while (hi - b > 1) {
+      const int mid = (b + hi) >> 1;
+      if (s_first[mid] <= id) b = mid; else hi = mid;
+    }
+  }
+  const int Sb = s_first[b + 1] - s_first[b], s = id - s_first[b];
+  const int A = s_alive[b];
+  const int nAB = min((A + kBlk - 1) / kBlk, p.cap_blocks);
+
+  // Q^T operand of this KV head's G query rows (lane l: head l%16, zero past
+  // G, d 32 ds + 8(l/16))
+  uint4 qop[4];
+  {
+    const uint8_t* qsrc = static_cast<const uint8_t*>(p.q) + (size_t(b) * p.Hq + size_t(g) * G + hl) * kMRow;
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      qop[ds] = hl < G ? *reinterpret_cast<const uint4*>(qsrc + (4 * ds + q4) * 16) : make_uint4(0, 0, 0, 0);
+  }
+  if (nAB == 0) {  // no alive token at all: O = 0, LSE = -inf
+    for (int i = tid; i < p.Hq * D; i += kBThreads) {
+      store_out<uint16_t>(p.out, size_t(b) * p.Hq * D + i, 0.f);
+      if (p.lse && i % D == 0) p.lse[size_t(b) * p.Hq + i / D] = -INFINITY;
+    }
+    return;
+  }
+  const int j0 = int(int64_t(s) * nAB / Sb);
+  const int nblk = int(int64_t(s + 1) * nAB / Sb) - j0;
+  const int last_tokens = min(kBlk, A - kBlk * (nAB - 1));
+  const int last_local = nAB - 1 - j0;
+
+  // ---- expand this split's segments into per-block physical ids ----------
+  {
+    const int s0 = p.indptr[b], s1 = p.indptr[b + 1];
+    const int sf = j0 == 0 ? s0 : wg_search_segment_n<kBThreads>(p.segs, s0, s1, j0 * kBlk);
+    const int ns = min(nblk, s1 - sf);
+    int32_t* st_start = reinterpret_cast<int32_t*>(&kv_lds[0][0][0][0]);
+    int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
+    int32_t* st_nblk = st_phys + kMaxSplitBlocks + 1;
+    for (int i = tid; i < ns; i += kBThreads) {
+      const msa_segment sg = p.segs[sf + i];
+      st_start[i] = sg.alive_token_start / kBlk;
+      const bool in_pool = sg.phys_block >= 0 && sg.num_blocks >= 0 &&
+                           int64_t(sg.phys_block) + sg.num_blocks <= p.P;
+      st_phys[i] = in_pool ? sg.phys_block : -1;
+      st_nblk[i] = in_pool ? sg.num_blocks : 0;
+    }
+    __syncthreads();
+    for (int jj = tid; jj < nblk; jj += kBThreads) {
+      const int j = j0 + jj;
+      int lo = 0, hi = ns;
+      while (hi - lo > 1) {
+        const int mid = (lo + hi) >> 1;
+        if (st_start[mid] <= j) lo = mid; else hi = mid;
+      }
+      const int off = j - st_start[lo];
+      blk_phys[jj] = (st_phys[lo] >= 0 && off >= 0 && off < st_nblk[lo]) ? st_phys[lo] + off : -1;
+    }
+    __syncthreads();  // staging dead from here on: the ring may overwrite it
+  }
+
+  const size_t tok_stride = p.head_major ? size_t(kMRow) : size_t(p.Hkv) * kMRow;
+  const size_t blk_stride = size_t(p.Hkv) * kMRow * kBlk;
+  const size_t head_off = p.head_major ? size_t(g) * kMRow * kBlk : size_t(g) * kMRow;
+  const char* kbase = static_cast<const char*>(p.k_pool) + head_off;
+  const char* vbase = static_cast<const char*>(p.v_pool) + head_off;
+  const int kq = lane / 16, slot = lane % 16;
+  // transpose-read word of lane l for d group dg: key 4(l/16) + (l%16)/4,
+  // d = 16 dg + 4(l%4) .. +3 (see decode_mfma_kernel)
+  const int vr_key = 4 * q4 + hl / 4;
+  const int vr_base = vr_key * kMRow + 8 * (hl % 2);
+  auto vrow_off = [&](int dg) { return vr_base + 16 * ((2 * dg + (hl % 4) / 2) ^ ((2 * vr_key) & 15)); };
+  const int k_off = hl * kMRow;  // + 16 ((4 ds + q4) ^ hl)
+
+  // (K, V) of block jj of the split into ring stage jj % 2: the wave-uniform
+  // physical id and readable rows (past the split or a dropped segment: an
+  // empty range, so the DMAs land zeros)
+  auto issue = [&](int jj) {
+    const int ph = jj < nblk ? __builtin_amdgcn_readfirstlane(blk_phys[jj]) : -1;
+    const int rows = ph < 0 ? 0 : (jj == last_local ? last_tokens : kBlk);
+    const size_t boff = size_t(ph < 0 ? 0 : ph) * blk_stride;
+    const uint32_t nrec = uint32_t(rows * tok_stride);
+    const __amdgpu_buffer_rsrc_t rk = block_rsrc(kbase + boff, nrec);
+    const __amdgpu_buffer_rsrc_t rv = block_rsrc(vbase + boff, nrec);
+    uint8_t* kt = &kv_lds[jj & 1][0][g][0];
+    uint8_t* vt = &kv_lds[jj & 1][1][g][0];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 4 * i + kq;  // K: chunk slot ^ key into slot `slot`
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rk, (__attribute__((address_space(3))) void*)(kt + i * 4 * kMRow),
+                                               16, uint32_t(key * tok_stride + 16 * (slot ^ key)), 0, 0,
+                                               kStreamPolicy);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = 4 * i + kq;  // V: chunk slot ^ (2 key mod 16) into slot `slot`
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rv, (__attribute__((address_space(3))) void*)(vt + i * 4 * kMRow),
+                                               16, uint32_t(key * tok_stride + 16 * (slot ^ ((2 * key) & 15))),
+                                               0, 0, kStreamPolicy);
+    }
+    return rows;
+  };
+
+  mf32x4_t o[8];
+#pragma unroll
+  for (int dg = 0; dg < 8; ++dg) o[dg] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_lane = 0.f;
+  const float c = p.scale_log2;
+
+  int rows = issue(0);
+  for (int jj = 0; jj < nblk; ++jj) {
+    // block jj+1 into the other stage, whose reads of block jj-1 have
+    // returned (the wait at the end of the previous step)
+    const int rows_next = issue(jj + 1);
+    // block jj has landed once at most the 8 DMAs of block jj+1 are in flight
+    asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+    const uint8_t* kt = &kv_lds[jj & 1][0][g][0];
+    const uint8_t* vt = &kv_lds[jj & 1][1][g][0];
+    uint4 kr[4];
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds) kr[ds] = *reinterpret_cast<const uint4*>(kt + k_off + 16 * ((4 * ds + q4) ^ hl));
+    uint2 vr[8];
+#pragma unroll
+    for (int dg = 0; dg < 8; ++dg) vr[dg] = m_read_tr16(vt + vrow_off(dg));
+    // ---- S = K Q^T: lane l holds head l%16, keys 4(l/16) .. +3 ------------
+    mf32x4_t sc = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ds = 0; ds < 4; ++ds)
+      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(kr[ds]), m_as_bf16x8(qop[ds]), sc, 0, 0, 0);
+    if (rows < kBlk) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) sc[r] = 4 * q4 + r < rows ? sc[r] : -INFINITY;
+    }
+    // ---- online softmax per head (lane l%16), lazy rescale ----------------
+    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const bool bump = (mx - m_run) * c > 8.f;
+    const float m_use = bump ? mx : m_run;
+    const float nm = m_use == -INFINITY ? 0.f : -m_use * c;
+    const float alpha = (m_use == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_use) * c);
+    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+      // O rows are heads 4(l/16) + r: fetch those heads' factors
+      float ar[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r);
+#pragma unroll
+      for (int dg = 0; dg < 8; ++dg)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) o[dg][r] *= ar[r];
+    }
+    m_run = m_use;
+    float pw[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) pw[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, nm));
+    l_lane = l_lane * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
+    // ---- O += P V -----------------------------------------------------------
+    const ms16x4_t pop = __builtin_bit_cast(ms16x4_t, make_uint2(m_cvt_pk_bf16(pw[0], pw[1]),
+                                                                 m_cvt_pk_bf16(pw[2], pw[3])));
+#pragma unroll
+    for (int dg = 0; dg < 8; ++dg)
+      o[dg] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop, __builtin_bit_cast(ms16x4_t, vr[dg]), o[dg],
+                                                        0, 0, 0);
+    // this stage is refilled by the next step's DMA: its reads must be back
+    asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+    rows = rows_next;
+  }
+  // no DMA may be left in flight when the workgroup ends
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- write this wavefront's G heads --------------------------------------
+  const float l_w = l_lane + __shfl_xor(l_lane, 16);
+  const float l_h = l_w + __shfl_xor(l_w, 32);  // head hl's sum over the split
+  float lr[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) lr[r] = __shfl(l_h, 4 * q4 + r);
+#pragma unroll
+  for (int dg = 0; dg < 8; ++dg)
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      const int hh = 4 * q4 + r;
+      if (hh < G) {
+        const size_t h = size_t(g) * G + hh;
+        const int d = dg * 16 + hl;
+        if (Sb == 1)
+          store_out<uint16_t>(p.out, (size_t(b) * p.Hq + h) * D + d, lr[r] > 0.f ? o[dg][r] / lr[r] : 0.f);
+        else
+          p.o_part[(size_t(id) * p.Hq + h) * D + d] = o[dg][r];
+      }
+    }
+  if (q4 == 0 && hl < G) {
+    const size_t h = size_t(g) * G + hl;
+    const float Mc = m_run * c;  // log2 units
+    if (Sb == 1) {
+      if (p.lse) p.lse[size_t(b) * p.Hq + h] = l_h > 0.f ? (Mc + log2f(l_h)) * kLn2 : -INFINITY;
+    } else {
+      p.m_part[size_t(id) * p.Hq + h] = m_run == -INFINITY ? -INFINITY : Mc * kLn2;
+      p.l_part[size_t(id) * p.Hq + h] = l_h;
+    }
+  }
+}
+
 template <typename KV, int D, int G>
 hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
   dim3 grid(p.S, p.Hkv, p.B);
@@ -885,6 +1244,15 @@ hipError_t launch_t(const DecodeParams& p, hipStream_t stream) {
 
 template <typename KV, int D>
 hipError_t launch_g(const DecodeParams& p, hipStream_t stream) {
+  if constexpr (std::is_same<KV, uint16_t>::value && D == kMD) {
+    if (p.use_block) {
+      if (p.Hq / p.Hkv == 4)
+        hipLaunchKernelGGL((decode_block_kernel<4>), dim3(p.nwg), dim3(kBThreads), 0, stream, p);
+      else
+        hipLaunchKernelGGL((decode_block_kernel<8>), dim3(p.nwg), dim3(kBThreads), 0, stream, p);
+      return hipGetLastError();
+    }
+  }
   switch (p.Hq / p.Hkv) {
     case 1: return launch_t<KV, D, 1>(p, stream);
     case 2: return launch_t<KV, D, 2>(p, stream);
@@ -945,6 +1313,30 @@ bool decode_matrix_supported(msa_dtype dtype, int32_t D, int32_t G) {
 }
 
 int32_t decode_max_split_blocks() { return kMaxSplitBlocks; }
+
+bool decode_block_supported(msa_dtype dtype, int32_t D, int32_t Hkv, int32_t G, int32_t B) {
+  return dtype == MSA_BF16 && D == kMD && Hkv == kBHkv && (G == 4 || G == 8) && B >= 1 &&
+         B <= kDecodeBlockMaxSeq;
+}
+
+int32_t decode_block_target(int32_t B) { return kCUs > 2 * B ? kCUs : 2 * B; }
+
+// Workgroups of the block kernel's grid: at least the number of splits its
+// device-side rule can make.  With T = ceil(W / (target - NZ)) the splits
+// number at most W / T + B <= target + B; a T capped at the longest split
+// gives at most cap * B / kMaxSplitBlocks + B; a caller's split_blocks T at
+// most cap * B / T + B.
+int64_t decode_block_grid(int32_t B, int32_t cap_blocks, int32_t split_blocks) {
+  const int64_t work = int64_t(cap_blocks) * B;
+  int64_t n;
+  if (split_blocks > 0) {
+    n = (work + split_blocks - 1) / split_blocks;
+  } else {
+    n = (work + kMaxSplitBlocks - 1) / kMaxSplitBlocks;
+    if (n < decode_block_target(B)) n = decode_block_target(B);
+  }
+  return n + B;
+}
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.dtype == MSA_BF16) {

@@ -36,7 +36,9 @@ __device__ __forceinline__ void store_o(void* out, size_t idx, float v, msa_dtyp
     static_cast<float*>(out)[idx] = v;
 }
 
-// mode 0: partials [indptr[b], indptr[b+1]); mode 1: derived from the plan
+// mode 0: partials [indptr[b], indptr[b+1]); mode 1: derived from the plan;
+// mode 2: as mode 0, but a sequence with one partial is skipped (the
+// attention kernel wrote it)
 struct MergeArgs {
   const float* o_part;
   const float* m_part;
@@ -75,9 +77,10 @@ __global__ void __launch_bounds__(kThreads) merge_kernel(MergeArgs a) {
   const int e = blockIdx.x * kElems + el;
   const int HD = a.H * a.D;
   int lo, n;
-  if (MODE == 0) {
+  if (MODE != 1) {
     lo = a.part_indptr[b];
     n = a.part_indptr[b + 1] - lo;
+    if (MODE == 2 && n <= 1) return;
   } else {
     const int A = plan_alive_tokens(a.segs, a.seg_indptr, b);
     // same clamp as the attention kernels: never more partials than the grid had
@@ -156,6 +159,15 @@ hipError_t launch_merge_indptr(const float* o_part, const float* m_part, const f
               B, R, H, D, out_dtype, out, lse};
   // the partial counts are on the device: four groups of partials
   return launch_ng<0>(a, 4, stream);
+}
+
+hipError_t launch_merge_block(const float* o_part, const float* m_part, const float* l_part,
+                              const int32_t* part_indptr, int32_t B, int32_t H, int32_t D,
+                              int32_t parts_per_seq, msa_dtype out_dtype, void* out, float* lse,
+                              hipStream_t stream) {
+  MergeArgs a{o_part, m_part, l_part, part_indptr, nullptr, nullptr, 0, 0,
+              B, 1, H, D, out_dtype, out, lse};
+  return launch_ng<2>(a, groups_for(parts_per_seq), stream);
 }
 
 }  // namespace msa

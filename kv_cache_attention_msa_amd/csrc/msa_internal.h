@@ -97,6 +97,13 @@ struct DecodeParams {
   int32_t S;             // splits per sequence in the grid
   int32_t kernel;        // msa_decode_kernel: automatic, vector or matrix-core kernel
   int32_t* dev_error;    // nullable: MSA_DEVERR_TRUNCATED is ORed in
+  // block kernel (one workgroup per split streaming whole KV blocks)
+  int32_t use_block;     // 1: decode_block_kernel over nwg workgroups
+  int32_t nwg;           // its grid
+  int32_t block_auto;    // 1: split length from the device rule, 0: split_blocks
+  int32_t block_target;  // workgroups the device rule aims at
+  int32_t cap_blocks;    // alive blocks a sequence may use (S * split_blocks)
+  int32_t* part_indptr;  // [B+1] first partial of each sequence (written by workgroup 0)
   void* out;
   float* lse;
   float* o_part;  // [B*S, Hq, D]
@@ -155,6 +162,11 @@ SplitPlan prefill_split(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t m
 bool decode_supported(msa_dtype dtype, int32_t D, int32_t G);
 bool decode_matrix_supported(msa_dtype dtype, int32_t D, int32_t G);
 int32_t decode_max_split_blocks();
+// block kernel: shapes it is built for, its split rule's target and its grid
+constexpr int kDecodeBlockMaxSeq = 1024;
+bool decode_block_supported(msa_dtype dtype, int32_t D, int32_t Hkv, int32_t G, int32_t B);
+int32_t decode_block_target(int32_t B);
+int64_t decode_block_grid(int32_t B, int32_t cap_blocks, int32_t split_blocks);
 int32_t prefill_max_split_blocks();
 bool prefill_supported(msa_dtype dtype, int32_t D, int32_t G);
 int32_t prefill_chunk_rows(int32_t B, int32_t Hq, int32_t Hkv, int32_t remaining,
@@ -178,6 +190,13 @@ hipError_t launch_merge_indptr(const float* o_part, const float* m_part, const f
                                const int32_t* part_indptr, int32_t B, int32_t R, int32_t H,
                                int32_t D, msa_dtype out_dtype, void* out, float* lse,
                                hipStream_t stream);
+// Merge after the decode block kernel: partial ranges from its part_indptr;
+// a sequence with one partial was written by the attention kernel itself.
+// parts_per_seq: the expected partials per sequence (sets the group count).
+hipError_t launch_merge_block(const float* o_part, const float* m_part, const float* l_part,
+                              const int32_t* part_indptr, int32_t B, int32_t H, int32_t D,
+                              int32_t parts_per_seq, msa_dtype out_dtype, void* out, float* lse,
+                              hipStream_t stream);
 
 // Number of alive tokens of sequence b according to the plan (device).
 __device__ __forceinline__ int32_t plan_alive_tokens(const msa_segment* segs, const int32_t* indptr,

@@ -117,28 +117,52 @@ def test_decode_kernel_choice_is_validated():
     the matrix-core kernel exists only for bf16 with D 128 and 4 or 8 query
     heads per KV head; the vector kernel for every supported shape."""
     lib = _lib.load()
-    assert _decode_ex(lib, kernel=3) == _lib.MSA_ERR_INVALID_ARG
+    assert _decode_ex(lib, kernel=4) == _lib.MSA_ERR_INVALID_ARG
     assert _decode_ex(lib, kernel=-1) == _lib.MSA_ERR_INVALID_ARG
     for hq, d, dt in ((16, 128, _lib.MSA_BF16), (8, 128, _lib.MSA_BF16), (32, 64, _lib.MSA_BF16),
                       (32, 64, _lib.MSA_F32)):
         assert _decode_ex(lib, kernel=_lib.MSA_DECODE_MATRIX, Hq=hq, D=d,
                           dtype=dt) == _lib.MSA_ERR_UNSUPPORTED, (hq, d, dt)
+    # the block kernel: bf16, D 128, 8 KV heads, 4 or 8 query heads per KV
+    # head, at most 1024 sequences
+    for kw in (dict(Hq=16, Hkv=4), dict(Hq=64, Hkv=16), dict(D=64), dict(dtype=_lib.MSA_F32, D=64),
+               dict(Hq=16), dict(B=1025)):
+        assert _decode_ex(lib, kernel=_lib.MSA_DECODE_BLOCK, **kw) == _lib.MSA_ERR_UNSUPPORTED, kw
     # the shape checks still come first
     assert _decode_ex(lib, kernel=_lib.MSA_DECODE_VECTOR, Hq=24) == _lib.MSA_ERR_UNSUPPORTED
     assert _decode_ex(lib, kernel=_lib.MSA_DECODE_MATRIX, B=0) == _lib.MSA_ERR_INVALID_ARG
+    assert _decode_ex(lib, kernel=_lib.MSA_DECODE_BLOCK, B=0) == _lib.MSA_ERR_INVALID_ARG
+
+
+def _aligned(*nbytes):
+    return sum(-(-n // 256) * 256 for n in nbytes)
 
 
 def test_decode_workspace_arithmetic():
     lib = _lib.load()
     # one split covers the context -> no workspace at all
     assert lib.msa_decode_workspace_size(1, 8, 2, 64, 1024, 16, 64) == 0
-    # explicit split: B*S partials of Hq*(D+2) floats (each array 256-B aligned)
-    B, Hq, D, ctx, T = 3, 32, 128, 4096, 32
+    # explicit split, a shape the block kernel does not cover (4 KV heads):
+    # B*S partials of Hq*(D+2) floats (each array 256-B aligned)
+    B, Hq, D, ctx, T = 3, 16, 128, 4096, 32
     S = -(-(ctx // 16) // T)
-    want = 0
-    for n in (B * S * Hq * D, B * S * Hq, B * S * Hq):
-        want += -(-n * 4 // 256) * 256
-    assert lib.msa_decode_workspace_size(B, Hq, 8, D, ctx, 16, T) == want
+    per_head = _aligned(4 * B * S * Hq * D, 4 * B * S * Hq, 4 * B * S * Hq)
+    assert lib.msa_decode_workspace_size(B, Hq, 4, D, ctx, 16, T) == per_head
+    # 8 KV heads (the block kernel may run): the larger of that and the block
+    # kernel's, which holds a partial per workgroup of its grid -- at most
+    # cap*B/T + B splits, cap = S*T alive blocks per sequence -- and B+1
+    # partial offsets
+    Hq = 32
+    per_head = _aligned(4 * B * S * Hq * D, 4 * B * S * Hq, 4 * B * S * Hq)
+    nwg = -(-(S * T * B) // T) + B
+    block = _aligned(4 * nwg * Hq * D, 4 * nwg * Hq, 4 * nwg * Hq, 4 * (B + 1))
+    assert lib.msa_decode_workspace_size(B, Hq, 8, D, ctx, 16, T) == max(per_head, block)
+    # automatic split: the grid aims at max(256, 2B) workgroups (+ B)
+    for B in (1, 32, 300):
+        nwg = max(256, 2 * B) + B
+        block = _aligned(4 * nwg * Hq * D, 4 * nwg * Hq, 4 * nwg * Hq, 4 * (B + 1))
+        assert lib.msa_decode_workspace_size(B, Hq, 8, D, 4096, 16, 0) >= block
+        assert lib.msa_decode_workspace_size(B, Hq, 8, 64, 4096, 16, 0) < block
 
 
 def test_merge_rejects_bad_args():
@@ -162,21 +186,24 @@ def _splits_from_workspace(lib, B, Hq, Hkv, D, ctx):
 
 
 def test_decode_automatic_split_rule():
+    # The per-KV-head kernels' split rule (it also sets how many alive blocks
+    # a sequence may use), read back at D 64, where the workspace is theirs
+    # alone; the rule does not depend on D.
     lib = _lib.load()
     # the (sequence, KV head) pairs fill the 256 CUs and contexts are short:
     # one split, no merge workspace
-    assert _splits_from_workspace(lib, 32, 32, 8, 128, 4096) == 1
+    assert _splits_from_workspace(lib, 32, 32, 8, 64, 4096) == 1
     # long contexts: splits of at most 128 blocks (192 when the pairs alone
     # cover the 256 CUs), never a multiple of 8
     for B, Hq, ctx in ((4, 64, 131072), (64, 32, 32768), (4, 32, 65536), (2, 16, 20000)):
-        S = _splits_from_workspace(lib, B, Hq, 8, 128, ctx)
+        S = _splits_from_workspace(lib, B, Hq, 8, 64, ctx)
         nbm = -(-ctx // 16)
         assert S > 1 and S % 8 != 0
         assert -(-nbm // S) <= (192 if B * 8 >= 256 else 128)
     # the 64-sequence batch with contexts up to 32k: 192-block splits
-    assert _splits_from_workspace(lib, 64, 32, 8, 128, 32768) == 11
+    assert _splits_from_workspace(lib, 64, 32, 8, 64, 32768) == 11
     # the 4-sequence 131k batch keeps 120-block splits (128 would give 64 splits)
-    assert _splits_from_workspace(lib, 4, 64, 8, 128, 131072) == 69
+    assert _splits_from_workspace(lib, 4, 64, 8, 64, 131072) == 69
 
 
 def test_gather_rejects_bad_args():

@@ -144,7 +144,7 @@ def test_decode_max_batch(split_blocks):
     check(w, O, L, seqs=[0, 1, 2, 31337, 65533, 65534])
 
 
-def _decode_both_layouts(w, split_blocks):
+def _decode_both_layouts(w, split_blocks, kernel="auto"):
     d = to_device(w, DEV)
     segs, indptr, err = msa.msa_plan_segments(d["block_table"], d["alive"], d["ctx_len"],
                                               w.block_size, w.num_phys_blocks)
@@ -154,7 +154,8 @@ def _decode_both_layouts(w, split_blocks):
         if layout == "HND":
             k, v = k.permute(0, 2, 1, 3).contiguous(), v.permute(0, 2, 1, 3).contiguous()
         outs.append(msa.msa_decode(d["q"], k, v, segs, indptr, max_ctx_len=int(w.ctx_len.max()),
-                                   scale=w.scale, split_blocks=split_blocks, kv_layout=layout))
+                                   scale=w.scale, split_blocks=split_blocks, kv_layout=layout,
+                                   kernel=kernel))
     torch.cuda.synchronize()
     assert int(err.item()) == 0
     return outs
@@ -326,29 +327,115 @@ def test_decode_understated_max_ctx_len_truncates_safely(cfg):
                                                  (5, 32, 0), (4, 32, 0)])
 def test_decode_vector_and_matrix_kernels(cfg, Hq, split_blocks):
     """msa_decode_ex with the kernel chosen explicitly: the vector-ALU kernel
-    (fp32 softmax weights) and the matrix-core kernel (weights rounded to
-    bf16 for P x V) on the same small batches, 4 and 8 query heads per KV
-    head, with and without splits.  Both match the oracle within the bf16
-    tolerance, and agree with each other within it too."""
+    (fp32 softmax weights), the per-KV-head matrix-core kernel and the block
+    kernel (both round the weights to bf16 for P x V) on the same small
+    batches, 4 and 8 query heads per KV head, with and without splits.  All
+    match the oracle within the bf16 tolerance, and agree with each other
+    within it too."""
     w = make_workload(cfg, seed=8, size="small", Hq=Hq)
     d = to_device(w, DEV)
     res = {}
-    for kern in ("vector", "matrix"):
+    for kern in ("vector", "matrix", "block"):
         O, L = run_decode(w, split_blocks, d, kernel=kern)
         res[kern] = check(w, O, L) + (O, L)
     assert np.max(np.abs(res["vector"][2] - res["matrix"][2])) <= TOL["bf16"]
+    assert np.max(np.abs(res["vector"][2] - res["block"][2])) <= TOL["bf16"]
 
 
-@pytest.mark.parametrize("cfg", [2, 5])
+@pytest.mark.parametrize("cfg", [2, 4, 5])
 def test_decode_vector_and_matrix_kernels_full(cfg):
-    """Full-size headline batch (4 query heads per KV head) and the
-    131k-token batch (8 per KV head): each kernel against the oracle on
-    sampled (sequence, head) pairs."""
+    """Full-size headline batch (4 query heads per KV head), the lognormal
+    shared-prefix batch and the 131k-token batch (8 per KV head): each
+    kernel against the oracle on sampled (sequence, head) pairs."""
     w = make_workload(cfg, seed=0)
     d = to_device(w, DEV)
     rng = np.random.default_rng(20 + cfg)
     seqs = sorted(rng.choice(w.B, size=min(w.B, 3), replace=False).tolist())
     heads = sorted(rng.choice(w.Hq, size=4, replace=False).tolist())
-    for kern in ("vector", "matrix"):
+    for kern in ("vector", "matrix", "block"):
         O, L = run_decode(w, 0, d, kernel=kern)
         check(w, O, L, seqs=seqs, heads=heads)
+
+
+# ---- the block kernel (one workgroup per split, whole blocks of all KV heads)
+
+@pytest.mark.parametrize("cfg,split_blocks", [(2, 0), (2, 16), (4, 0), (5, 0), (5, 1)])
+def test_decode_block_kernel_head_major(cfg, split_blocks):
+    """The block kernel on head-major pool blocks gives bitwise the
+    token-major result, and both match the oracle (split_blocks 1: every
+    alive block its own split, the merge over the most partials)."""
+    w = make_workload(cfg, seed=6, size="small")
+    (o_n, l_n), (o_h, l_h) = _decode_both_layouts(w, split_blocks, kernel="block")
+    assert torch.equal(o_n, o_h) and torch.equal(l_n, l_h)
+    check(w, from_device(o_h), l_h.cpu().numpy().astype(np.float64))
+
+
+def test_decode_block_kernel_empty_and_tiny_sequences():
+    """Sequences with no alive token (all evicted, ctx_len 0) get O = 0 and
+    LSE = -inf from their one workgroup; one-token and one-block-plus-one
+    sequences end mid-block; automatic and forced split lengths."""
+    w = make_workload(2, seed=2, size="small", B=5, ctx=700)
+    w.alive[0, :] = 0
+    w.ctx_len[1] = 1
+    w.ctx_len[2] = 17
+    w.ctx_len[3] = 0
+    for split in (0, 1, 16):
+        O, L = run_decode(w, split, kernel="block")
+        for b in (0, 3):
+            assert np.all(O[b] == 0) and np.all(np.isneginf(L[b]))
+        check(w, O, L, seqs=[1, 2, 4])
+
+
+@pytest.mark.parametrize("B,ctx", [(1, 5000), (3, 900), (97, 300), (1024, 100)])
+def test_decode_block_kernel_batch_sizes(B, ctx):
+    """From one sequence (every workgroup on one sequence) to the 1024 the
+    block kernel takes (one or two splits each); the device split rule sees
+    every count."""
+    w = make_workload(2, seed=4, size="small", B=B, ctx=ctx, pool_factor=2.0)
+    O, L = run_decode(w, 0, kernel="block")
+    seqs = sorted(set([0, B // 2, B - 1]))
+    check(w, O, L, seqs=seqs)
+
+
+def test_decode_block_kernel_understated_max_ctx_len():
+    """Understated max_ctx_len with the block kernel: the same cut as the
+    per-head kernels (the first splits x split_blocks alive blocks of each
+    sequence), reported by MSA_DEVERR_TRUNCATED, equal to the oracle over
+    that prefix."""
+    w = make_workload(2, seed=3, size="small")
+    T, max_ctx = 16, 512
+    cap_blocks = -(-max_ctx // 16)
+    d = to_device(w, DEV)
+    segs, indptr, err = msa.msa_plan_segments(d["block_table"], d["alive"], d["ctx_len"],
+                                              w.block_size, w.num_phys_blocks)
+    torch.cuda.synchronize()
+    assert int(err.item()) == 0
+    for split in (T, 0):
+        err.zero_()
+        out, lse = msa.msa_decode(d["q"], d["k_pool"], d["v_pool"], segs, indptr,
+                                  max_ctx_len=max_ctx, scale=w.scale, split_blocks=split,
+                                  kernel="block", dev_error=err)
+        torch.cuda.synchronize()
+        assert int(err.item()) == msa.MSA_DEVERR_TRUNCATED
+        if split == T:
+            kept = w.alive.copy()
+            for b in range(w.B):
+                nb = -(-int(w.ctx_len[b]) // w.block_size)
+                idx = [l for l in range(nb) if w.alive[b, l]]
+                for l in idx[cap_blocks:]:
+                    kept[b, l] = 0
+            Or, Lr = oracle.decode_ref(w.q, w.k_pool, w.v_pool, w.block_table, kept, w.ctx_len,
+                                       w.block_size, w.scale)
+            assert np.max(np.abs(from_device(out) - Or)) <= TOL["bf16"]
+            assert np.max(np.abs(lse.cpu().numpy().astype(np.float64) - Lr)) <= TOL["bf16"]
+
+
+def test_decode_block_kernel_determinism_full():
+    """The 131k-token batch (automatic choice: the block kernel), three
+    calls: identical bits every time."""
+    w = make_workload(5, seed=0)
+    d = to_device(w, DEV)
+    O1, L1 = run_decode(w, 0, d)
+    for _ in range(2):
+        O2, L2 = run_decode(w, 0, d)
+        assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
