@@ -618,10 +618,11 @@ def prefill_leg(w, n, warm, flush=None):
     return rec
 
 
-def kernel_cases(args, w2, w5):
+def kernel_cases(args, w2, w5, w4=None):
     """Batches for the decode-kernel comparison: the headline batch as drawn
     (G 4) and with 64 query heads (G 8: 32 more rows drawn N(0,1)); the
-    131k-token batch as drawn (G 8) and with its first 32 query heads (G 4)."""
+    131k-token batch as drawn (G 8) and with its first 32 query heads (G 4);
+    the lognormal shared-prefix batch (G 4) when given."""
     import copy
     import numpy as np
     from workloads import f32_to_bf16_bits
@@ -633,14 +634,19 @@ def kernel_cases(args, w2, w5):
     w5g4 = copy.copy(w5)
     w5g4.q = np.ascontiguousarray(w5.q[:, :w5.Hq // 2])
     w5g4.Hq = w5.Hq // 2
-    return (("headline batch, G 4", w2), ("headline batch, G 8", w2g8),
-            ("131k-token batch, G 8", w5), ("131k-token batch, G 4", w5g4))
+    cases = (("headline batch, G 4", w2), ("headline batch, G 8", w2g8),
+             ("131k-token batch, G 8", w5), ("131k-token batch, G 4", w5g4))
+    if w4 is not None:
+        cases += (("lognormal shared-prefix batch, G 4", w4),)
+    return cases
 
 
-def kernels_leg(args, flush, w2, w5):
-    """The vector-ALU and the matrix-core decode kernel on the same batches
-    (4 and 8 query heads per KV head): cold time and max error against the
-    oracle on sampled (sequence, head) pairs."""
+def kernels_leg(args, flush, w2, w5, w4=None):
+    """The three decode kernels -- vector-ALU, per-KV-head matrix-core, and
+    the block kernel (whole KV blocks of all heads per workgroup, shared
+    prefixes streamed once per sub-group) -- on the same batches (4 and 8
+    query heads per KV head): cold time and max error against the oracle on
+    sampled (sequence, head) pairs."""
     import numpy as np
     import torch
     import oracle
@@ -648,13 +654,14 @@ def kernels_leg(args, flush, w2, w5):
     from workloads.device import from_device
     rng = np.random.default_rng(args.seed + 31)
     cases = []
-    for name, w in kernel_cases(args, w2, w5):
+    for name, w in kernel_cases(args, w2, w5, w4):
         seqs = sorted(rng.choice(w.B, size=min(2, w.B), replace=False).tolist())
         heads = sorted(rng.choice(w.Hq, size=3, replace=False).tolist())
         Or, Lr = oracle.decode_ref(w.q, w.k_pool, w.v_pool, w.block_table, w.alive, w.ctx_len,
                                    w.block_size, w.scale, seqs=seqs, heads=heads)
         row = {"batch": name, "G": w.Hq // w.Hkv}
-        for kname, k in (("vector", _lib.MSA_DECODE_VECTOR), ("matrix", _lib.MSA_DECODE_MATRIX)):
+        for kname, k in (("vector", _lib.MSA_DECODE_VECTOR), ("matrix", _lib.MSA_DECODE_MATRIX),
+                         ("block", _lib.MSA_DECODE_BLOCK)):
             leg, out = decode_leg(w, max(10, args.steps // 2), flush, kernel=k)
             O = from_device(out)
             sel = np.ix_(seqs, heads)
@@ -671,8 +678,9 @@ def kernels_leg(args, flush, w2, w5):
 def eviction_leg(args, flush, w):
     """Kernel-aware eviction (keep-score = hit probability + recompute cost +
     the decode time a block costs, from a latency model of msa_decode fitted
-    here) against hit-only eviction, at the same number of evicted blocks, on
-    the headline batch.  Only the alive mask changes, so the same device pools
+    here over alive tokens, segments and the longest sequence's alive tokens)
+    against hit-only eviction, at the same number of evicted blocks, on the
+    headline batch.  Only the alive mask changes, so the same device pools
     serve every point; each point re-plans and times msa_decode cold."""
     import numpy as np
     import torch
@@ -695,11 +703,24 @@ def eviction_leg(args, flush, w):
         prep.plan()
         prep.attention()
         prep.check_error()
-        ts = cold_times(prep.attention, max(10, args.steps // 2), prep.stream, flush)
+        ts = cold_times(prep.attention, max(30, args.steps), prep.stream, flush)
         segs = int(prep.indptr[-1].item())
         del prep
-        return {"alive_tokens": int(sum(alive_tokens_per_seq(wv))), "segments": segs,
+        per = alive_tokens_per_seq(wv)
+        return {"alive_tokens": int(sum(per)), "max_seq_tokens": int(max(per)), "segments": segs,
                 "us": round(tmean(ts) * 1e6, 3)}
+
+    def level(al, n, longest):
+        # n more evictions, each from the sequence with the most (longest) or
+        # fewest alive tokens, a random evictable block of it
+        al = al.copy()
+        for _ in range(n):
+            per = [int(al[b, :nb[b] - 1].sum()) for b in range(B)]
+            cand = [b for b in range(B) if per[b] > 0]
+            b = max(cand, key=lambda x: per[x]) if longest else min(cand, key=lambda x: per[x])
+            ls = np.nonzero(al[b, :nb[b] - 1])[0]
+            al[b, int(rng.choice(ls))] = 0
+        return al
 
     # fit points: extra evictions of single random blocks (more segments) and
     # of whole alive runs (fewer segments) at three fractions each
@@ -731,33 +752,49 @@ def eviction_leg(args, flush, w):
             al[b, s:e] = 0
             done += e - s
         pts.append(dict(kind=f"whole runs {frac:.0%}", **measure(al)))
-    m = DecodeLatencyModel.fit([p["alive_tokens"] for p in pts], [p["segments"] for p in pts],
-                               [p["us"] for p in pts])
+    # the longest sequence apart from the total: blocks from the longest
+    # sequences only, or from the shortest only
+    for frac in (0.05, 0.1):
+        k = int(frac * len(evictable))
+        pts.append(dict(kind=f"longest first {frac:.0%}", **measure(level(w.alive, k, True))))
+        pts.append(dict(kind=f"shortest first {frac:.0%}", **measure(level(w.alive, k, False))))
+    cols = lambda key: [p[key] for p in pts]
+    m = DecodeLatencyModel.fit(cols("alive_tokens"), cols("segments"), cols("us"),
+                               max_seq_tokens=cols("max_seq_tokens"))
     meas = np.array([p["us"] for p in pts])
-    pred = m.predict([p["alive_tokens"] for p in pts], [p["segments"] for p in pts])
+    pred = m.predict(cols("alive_tokens"), cols("segments"), cols("max_seq_tokens"))
     r2 = 1.0 - float(((meas - pred) ** 2).sum() / max(((meas - meas.mean()) ** 2).sum(), 1e-30))
     hit = rng.random(w.alive.shape)
     rec = [recompute_cost_us(w.alive[b], w.ctx_len[b], w.block_size, w.D, w.Hq, 1000.0)
            for b in range(B)]
     n_ev = int(0.1 * len(evictable))
     policies = {}
-    for name, kw in (("kernel_aware", dict(alpha=float(np.mean([r.mean() for r in rec])), beta=1.0,
-                                           gamma=1000.0)),
+    # kernel_aware: the pages' full score (hit probability, recompute cost,
+    # decode cost over 1000 steps); latency_aware: hit probability and the
+    # decode cost only (1 us of decode time per step weighs as much as a hit
+    # probability of 10); hit_only: hit probability alone
+    rec_mean = float(np.mean([r.mean() for r in rec]))
+    for name, kw in (("kernel_aware", dict(alpha=rec_mean, beta=1.0, gamma=1000.0)),
+                     ("latency_aware", dict(alpha=1.0, beta=0.0, gamma=10.0 * B)),
                      ("hit_only", dict(alpha=1.0, beta=0.0, gamma=0.0))):
         al, ev = choose_evictions(w.block_table, w.alive, w.ctx_len, w.block_size, n_ev, hit, rec, m,
                                   batch_seqs=B, **kw)
         r = measure(al)
-        r["predicted_us"] = round(float(m.predict(r["alive_tokens"], r["segments"])), 3)
+        r["predicted_us"] = round(float(m.predict(r["alive_tokens"], r["segments"],
+                                                  r["max_seq_tokens"])), 3)
         r["evicted_blocks"] = len(ev)
         r["mean_hit_prob_evicted"] = round(float(np.mean([hit[b, l] for b, l in ev])), 4)
+        r["recompute_us_evicted"] = round(float(sum(rec[b][l] for b, l in ev)), 1)
         policies[name] = r
     del base
     torch.cuda.empty_cache()
     return {"model": {"c0_us": round(m.c0, 3), "c_tok_us": m.c_tok, "c_seg_us": m.c_seg,
-                      "r2": round(r2, 4), "points": pts},
+                      "c_max_us": m.c_max, "r2": round(r2, 4), "points": pts},
             "evicted_blocks": n_ev, "policies": policies,
             "decode_us_saved_by_kernel_aware": round(policies["hit_only"]["us"]
-                                                     - policies["kernel_aware"]["us"], 3)}
+                                                     - policies["kernel_aware"]["us"], 3),
+            "decode_us_saved_by_latency_aware": round(policies["hit_only"]["us"]
+                                                      - policies["latency_aware"]["us"], 3)}
 
 
 def chunk_sweep_leg(args, flush):
@@ -826,10 +863,13 @@ def main(argv=None):
             else:
                 result["cold_us"] = dist_us(cold_times(prep.attention, n, prep.stream, flush))
         elif args.only == "kernels":
-            # each batch with the vector kernel, then the matrix-core kernel
-            cases = kernel_cases(args, make_workload(2, seed=args.seed), make_workload(5, seed=args.seed))
+            # each batch with the vector kernel, the per-KV-head matrix-core
+            # kernel and the block kernel
+            cases = kernel_cases(args, make_workload(2, seed=args.seed), make_workload(5, seed=args.seed),
+                                 make_workload(4, seed=args.seed))
             for name, w in cases:
-                for kname, k in (("vector", _lib.MSA_DECODE_VECTOR), ("matrix", _lib.MSA_DECODE_MATRIX)):
+                for kname, k in (("vector", _lib.MSA_DECODE_VECTOR), ("matrix", _lib.MSA_DECODE_MATRIX),
+                                 ("block", _lib.MSA_DECODE_BLOCK)):
                     prep = Prepared(w, kernel=k)
                     for _ in range(args.warmup):
                         prep.step()

@@ -84,13 +84,15 @@ typedef enum { MSA_LAYOUT_NHD = 0, MSA_LAYOUT_HND = 1 } msa_kv_layout;
 #define MSA_DEVERR_TRUNCATED 8  /* decode/prefill: a sequence has more alive tokens than max_ctx_len
                                    allows for; its keys were cut at the grid's capacity */
 
-/* Which decode kernel runs (msa_decode_ex).  AUTO picks per shape and split
- * count; VECTOR is the vector-ALU kernel (every supported shape); MATRIX the
- * matrix-core kernel with one workgroup per (sequence, KV head, split),
- * built for bf16 with D 128 and Hq/Hkv 4 or 8 only; BLOCK the matrix-core
- * kernel with one workgroup per (sequence, split) that streams whole KV
- * blocks for all KV heads, built for bf16, D 128, Hkv 8, Hq/Hkv 4 or 8 and
- * B <= 1024 (MSA_ERR_UNSUPPORTED otherwise). */
+/* Which decode kernel runs (msa_decode_ex).  AUTO picks per shape (see
+ * msa_decode); VECTOR is the vector-ALU kernel (every supported shape);
+ * MATRIX the matrix-core kernel with one workgroup per (sequence, KV head,
+ * split), built for bf16 with D 128 and Hq/Hkv 4 or 8 only; BLOCK the
+ * matrix-core kernel with one workgroup per work item that streams whole KV
+ * blocks for all KV heads and, for up to 256 sequences, streams a prefix
+ * that several sequences share (same first physical block at logical block
+ * 0) once for up to 8 of them; built for bf16, D 128, Hkv 8, Hq/Hkv 4 or 8
+ * and B <= 512 (MSA_ERR_UNSUPPORTED otherwise). */
 typedef enum {
   MSA_DECODE_AUTO = 0,
   MSA_DECODE_VECTOR = 1,
@@ -152,7 +154,9 @@ int msa_plan_segments(const int32_t* block_table, const uint8_t* alive, const in
 /* ------------------------------------------------------------------------ */
 
 /* Workspace bytes for msa_decode with the same shape arguments.  Zero when
- * one split covers max_ctx_len (then no partials and no merge launch). */
+ * one split covers max_ctx_len and the block kernel cannot run for the shape
+ * (then no partials and no merge launch); where it can, enough for either
+ * kernel. */
 size_t msa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
                                  int32_t max_ctx_len, int32_t block_size, int32_t split_blocks);
 
@@ -162,12 +166,17 @@ size_t msa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  * The query of sequence b attends to every alive token of b (it sits after
  * all of them: no mask).  Work split: each sequence's nA alive blocks are
  * cut into ceil(nA / split_blocks) near-equal splits of at most split_blocks
- * blocks (0 = chosen by the library from B, Hkv and max_ctx_len); each
- * (sequence, KV head, split) is one workgroup
- * that walks its segments in logical order and folds them into a running
- * (max, sum-exp, unnormalised output).  When a sequence needs more than one
- * split the partials go to `workspace` and a merge kernel stitches them by
- * log-sum-exp (same as msa_merge_partials).
+ * blocks (0 = chosen by the library); every split walks its segments in
+ * logical order and folds them into a running (max, sum-exp, unnormalised
+ * output).  The per-head kernels run one workgroup per (sequence, KV head,
+ * split) and choose split_blocks on the host from B, Hkv and max_ctx_len;
+ * the block kernel runs one workgroup per split for all KV heads and, with
+ * split_blocks 0, chooses the split length on the device from the plan's
+ * alive counts.  The automatic choice (msa_decode, MSA_DECODE_AUTO) is the
+ * block kernel where it is built and B <= 256, except when one workgroup per
+ * (sequence, KV head) fills the 256 CUs and no context exceeds 256 blocks.
+ * When a sequence has more than one partial they go to `workspace` and a
+ * merge kernel stitches them by log-sum-exp (as msa_merge_partials).
  *
  *   q            [B, Hq, D] dtype           k_pool, v_pool  [P, 16, Hkv, D] dtype
  *   segs, seg_indptr   a plan from msa_plan_segments over the same pool
@@ -196,10 +205,11 @@ int msa_decode(const void* q, const void* k_pool, const void* v_pool, int32_t nu
  * kernel chosen by `kernel` (msa_decode itself is this call with
  * MSA_LAYOUT_NHD and MSA_DECODE_AUTO).  Same arguments, results and errors;
  * a kv_layout or kernel value other than those above returns
- * MSA_ERR_INVALID_ARG, MSA_DECODE_MATRIX on a shape it was not built for
- * MSA_ERR_UNSUPPORTED.  Both layouts give bitwise-identical results on the
- * same values; the two kernels agree within the bf16 tolerance (the matrix
- * kernel rounds the softmax weights to bf16 for P x V). */
+ * MSA_ERR_INVALID_ARG, MSA_DECODE_MATRIX or MSA_DECODE_BLOCK on a shape it
+ * was not built for MSA_ERR_UNSUPPORTED.  Both layouts give bitwise-identical
+ * results on the same values with the same kernel; the kernels agree within
+ * the bf16 tolerance (the matrix-core kernels round the softmax weights to
+ * bf16 for P x V, and split differently). */
 int msa_decode_ex(const void* q, const void* k_pool, const void* v_pool, int32_t num_phys_blocks,
                   int32_t block_size, const msa_segment* segs, const int32_t* seg_indptr,
                   int32_t B, int32_t Hq, int32_t Hkv, int32_t D, int32_t max_ctx_len,

@@ -49,33 +49,34 @@ int check_attn_shape(const void* q, const void* k_pool, const void* v_pool, int3
 }
 
 // The decode kernel a call runs: true for the block kernel.  Automatic
-// choice: the block kernel when the (sequence, KV head) pairs do not fill
-// the chip, so that the per-head kernels would split every sequence many
-// ways (4 x 131k tokens: 174 against 196 us cold).  With 256 pairs or more
-// the per-head kernels keep each pair in one workgroup or a few, and the
-// block kernel's per-workgroup set-up (about 10 us: plan reads, split
-// search, segment expansion, first block) and merge cost more than its
-// faster stream gains (32 x 4k: 80 against 76 us; 64 lognormal contexts:
-// 251 against 244 us).
+// choice: the block kernel for up to 256 sequences (the range in which it
+// looks for shared prefixes), unless one workgroup per (sequence, KV head)
+// already fills the chip with no split (every context within 256 blocks):
+// there the per-head kernel needs no merge and no device-side set-up, and
+// wins (32 x 4k tokens, cold: 75.5 against 85 us).  Elsewhere the block
+// kernel's whole-block stream wins: 4 x 131k tokens 179 against 197 us, 64
+// lognormal contexts with shared prefixes 201 against 245 us.
 bool decode_uses_block(msa_decode_kernel kernel, msa_dtype dtype, int32_t B, int32_t Hq,
-                       int32_t Hkv, int32_t D) {
+                       int32_t Hkv, int32_t D, int32_t max_ctx_len, int32_t block_size) {
   if (kernel == MSA_DECODE_BLOCK) return true;
   if (kernel != MSA_DECODE_AUTO) return false;
-  return decode_block_supported(dtype, D, Hkv, Hq / Hkv, B) && int64_t(B) * Hkv < 256;
+  if (!decode_block_supported(dtype, D, Hkv, Hq / Hkv, B) || B > kDecodeBlockMaxShareSeq) return false;
+  const int64_t nbm = (int64_t(max_ctx_len) + block_size - 1) / block_size;
+  return !(int64_t(B) * Hkv >= 256 && nbm <= 256);
 }
 
-// block kernel workspace: partials of every workgroup of its grid, then the
-// per-sequence partial ranges
+// block kernel workspace: its partial capacity, then the per-sequence
+// partial ranges
 struct BlockLayout {
   PartLayout parts;
   size_t indptr_off, total;
-  int64_t nwg;
+  BlockSizes n;
 };
 inline BlockLayout block_layout(int32_t B, int32_t Hq, int32_t D, int32_t cap_blocks,
                                 int32_t split_blocks) {
   BlockLayout L;
-  L.nwg = decode_block_grid(B, cap_blocks, split_blocks);
-  L.parts = part_layout(L.nwg, 1, Hq, D);
+  L.n = decode_block_sizes(B, cap_blocks, split_blocks);
+  L.parts = part_layout(L.n.parts, 1, Hq, D);
   L.indptr_off = L.parts.total;
   L.total = L.indptr_off + align_up(size_t(B + 1) * sizeof(int32_t));
   return L;
@@ -206,21 +207,23 @@ int msa_decode_ex(const void* q, const void* k_pool, const void* v_pool, int32_t
   p.use_block = 0;
   p.part_indptr = nullptr;
   p.cap_blocks = sp.S * sp.split_blocks;
-  if (decode_uses_block(kernel, dtype, B, Hq, Hkv, D)) {
+  if (decode_uses_block(kernel, dtype, B, Hq, Hkv, D, max_ctx_len, block_size)) {
     const BlockLayout L = block_layout(B, Hq, D, p.cap_blocks, split_blocks);
-    if (L.nwg > INT32_MAX) return MSA_ERR_UNSUPPORTED;
+    if (L.n.items > INT32_MAX || L.n.parts > INT32_MAX) return MSA_ERR_UNSUPPORTED;
     char* ws = static_cast<char*>(workspace);
     p.use_block = 1;
-    p.nwg = int32_t(L.nwg);
+    p.nwg = int32_t(L.n.items);
     p.block_auto = split_blocks == 0 ? 1 : 0;
     p.block_target = decode_block_target(B);
+    p.block_parts = int32_t(L.n.parts);
+    p.block_share = decode_block_shares(B) ? 1 : 0;
     p.o_part = reinterpret_cast<float*>(ws + L.parts.o_off);
     p.m_part = reinterpret_cast<float*>(ws + L.parts.m_off);
     p.l_part = reinterpret_cast<float*>(ws + L.parts.l_off);
     p.part_indptr = reinterpret_cast<int32_t*>(ws + L.indptr_off);
     hipError_t e = launch_decode(p, as_stream(stream));
     if (e != hipSuccess) return MSA_ERR_DEVICE;
-    const int64_t per_seq = (L.nwg - B + B - 1) / B;
+    const int64_t per_seq = (L.n.items - B + B - 1) / B;
     e = launch_merge_block(p.o_part, p.m_part, p.l_part, p.part_indptr, B, Hq, D,
                            int32_t(per_seq < 1 ? 1 : per_seq), dtype, out, lse_out,
                            as_stream(stream));

@@ -856,8 +856,8 @@ __global__ void __launch_bounds__(kThreads, KDMA ? 1 : 2) decode_mfma_kernel(Dec
 }
 
 // ---------------------------------------------------------------------------
-// decode_block_kernel: the matrix-core decode with one workgroup per
-// (sequence, split) that streams whole KV blocks, all KV heads at once.
+// decode_block_kernel: the matrix-core decode with one workgroup per work
+// item that streams whole KV blocks, all KV heads at once.
 //
 // In the token-major pool a block of K (or V) is one contiguous 32 KB run
 // (16 slots x Hkv heads x 256 B).  The per-KV-head kernels above read one
@@ -874,203 +874,148 @@ __global__ void __launch_bounds__(kThreads, KDMA ? 1 : 2) decode_mfma_kernel(Dec
 //     j+1 is requested before block j is waited for, so two blocks per
 //     wavefront are in flight; the ring is wavefront-private, so the loop
 //     has no barrier.  128 KB of ring: one workgroup per CU.
-//   * S = K Q^T per block on v_mfma_f32_16x16x32_bf16 (heads padded to 16
-//     rows); the lane's four weights are exactly the A operand of
-//     v_mfma_f32_16x16x16_bf16 for O += P V (k = the block's 16 keys).
-//   * Work split, on the device: every workgroup reads all B sequences'
-//     alive-token counts from the plan (one load pair per sequence) and
-//     picks the smallest split length T (at least kBMinSplit blocks) for
-//     which the splits, ceil(nA / T) near-equal ones per sequence, number at
-//     most `target` (one workgroup per CU): the host knows only max_ctx_len,
-//     not the eviction rate or the length mix.  An exclusive scan of the
-//     split counts numbers the splits; workgroup i takes split i, and
-//     workgroup 0 publishes the scan for the merge.
+//   * S = K Q^T per block on v_mfma_f32_16x16x32_bf16: the 16 columns of a
+//     tile are (sequence, query head) pairs; the lane's four weights are
+//     exactly the A operand of v_mfma_f32_16x16x16_bf16 for O += P V (k =
+//     the block's 16 keys).
+//   * Work items.  A private item is a split of one sequence's alive-block
+//     stream.  With prefix sharing on, sequences whose first segment starts
+//     at logical block 0 on the same physical block hold the same blocks up
+//     to the shortest such segment (full blocks only); when two or more do,
+//     that common prefix becomes shared items, each attending for up to
+//     kBShareTiles * 16 / G member sequences at once (one column tile per 16
+//     / G members), so the group's prefix is streamed once per sub-group
+//     instead of once per member, and the members' private items start
+//     after it.  Every item writes one partial per sequence it serves, and
+//     a sequence's partials are merged by log-sum-exp like any split's.
+//   * The split length, on the device: every workgroup reads all B
+//     sequences' plan ends (and first segments, with sharing) and picks the
+//     smallest T (at least kBMinSplit blocks) for which the items number at
+//     most `target` (one workgroup per CU) and the partials fit the
+//     workspace; the host knows only max_ctx_len, not the eviction rate,
+//     the length mix or the sharing.  Exclusive scans number items and
+//     partials; workgroup i takes item i, and workgroup 0 publishes the
+//     partial ranges for the merge.
 // ---------------------------------------------------------------------------
 constexpr int kBThreads = 512;  // one wavefront per KV head
 constexpr int kBHkv = kBThreads / kWave;
-constexpr int kBMinSplit = 8;  // blocks: shorter splits cost more set-up than they balance
+constexpr int kBMinSplit = 8;   // blocks: shorter splits cost more set-up than they balance
+constexpr int kBShareTiles = 2;  // column tiles of a shared item
+constexpr int kBMinShare = 8;   // a common prefix shorter than this is not shared
+
+// inclusive prefix sum over the 64 lanes with DPP row shifts and row
+// broadcasts (no LDS round trips): shifts 1, 2, 4, 8 scan each row of 16
+// lanes, then lane 15 is added to row 1 (and row 3), lane 31 to rows 2, 3
+__device__ __forceinline__ int wave_incl_scan(int x) {
+  x += __builtin_amdgcn_update_dpp(0, x, 0x111, 0xf, 0xf, false);  // row_shr:1
+  x += __builtin_amdgcn_update_dpp(0, x, 0x112, 0xf, 0xf, false);  // row_shr:2
+  x += __builtin_amdgcn_update_dpp(0, x, 0x114, 0xf, 0xf, false);  // row_shr:4
+  x += __builtin_amdgcn_update_dpp(0, x, 0x118, 0xf, 0xf, false);  // row_shr:8
+  x += __builtin_amdgcn_update_dpp(0, x, 0x142, 0xa, 0xf, false);  // row_bcast:15
+  x += __builtin_amdgcn_update_dpp(0, x, 0x143, 0xc, 0xf, false);  // row_bcast:31
+  return x;
+}
 
 __device__ __forceinline__ int wave_sum(int v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+  return __builtin_amdgcn_readlane(wave_incl_scan(v), kWave - 1);
 }
 
-// sum of one value per thread over the workgroup (red: kBHkv ints of LDS)
-__device__ __forceinline__ int block_sum(int v, int* red) {
+// sums of two values per thread over the workgroup (red: 2 kBHkv ints)
+__device__ __forceinline__ void block_sum2(int u, int v, int* red, int& su, int& sv) {
+  u = wave_sum(u);
   v = wave_sum(v);
-  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = v;
-  __syncthreads();
-  int t = 0;
-#pragma unroll
-  for (int i = 0; i < kBHkv; ++i) t += red[i];
-  __syncthreads();
-  return t;
-}
-
-// exclusive prefix sum of one value per thread over the workgroup; `total`
-// gets the sum (red: kBHkv ints of LDS)
-__device__ __forceinline__ int block_excl_scan(int v, int* red, int& total) {
-  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    red[threadIdx.x / kWave] = u;
+    red[kBHkv + threadIdx.x / kWave] = v;
   }
-  if (lane == kWave - 1) red[w] = x;
   __syncthreads();
-  int base = 0, tot = 0;
+  su = sv = 0;
 #pragma unroll
   for (int i = 0; i < kBHkv; ++i) {
-    const int t = red[i];
-    base += i < w ? t : 0;
-    tot += t;
+    su += red[i];
+    sv += red[kBHkv + i];
   }
   __syncthreads();
-  total = tot;
-  return base + x - v;
 }
 
-template <int G>
-__global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams p) {
-  static_assert(G == 4 || G == 8, "heads padded to 16 MFMA rows");
+// exclusive prefix sums of three values per thread over the workgroup, and
+// their totals (red: 3 kBHkv ints of LDS)
+__device__ __forceinline__ void block_excl_scan3(int u, int v, int x, int* red, int& eu, int& ev, int& ex,
+                                                 int& tu, int& tv, int& tx) {
+  const int lane = threadIdx.x & (kWave - 1), w = threadIdx.x / kWave;
+  const int a = wave_incl_scan(u), b = wave_incl_scan(v), c = wave_incl_scan(x);
+  if (lane == kWave - 1) {
+    red[w] = a;
+    red[kBHkv + w] = b;
+    red[2 * kBHkv + w] = c;
+  }
+  __syncthreads();
+  int ba = 0, bb = 0, bc = 0;
+  tu = tv = tx = 0;
+#pragma unroll
+  for (int i = 0; i < kBHkv; ++i) {
+    const int ra = red[i], rb = red[kBHkv + i], rc = red[2 * kBHkv + i];
+    ba += i < w ? ra : 0;
+    bb += i < w ? rb : 0;
+    bc += i < w ? rc : 0;
+    tu += ra;
+    tv += rb;
+    tx += rc;
+  }
+  __syncthreads();
+  eu = ba + a - u;
+  ev = bb + b - v;
+  ex = bc + c - x;
+}
+
+// largest i in [0, n) with a[i] <= x (a ascending, a[0] <= x)
+__device__ __forceinline__ int lds_upper(const int32_t* a, int n, int x) {
+  int lo = 0, hi = n;
+  while (hi - lo > 1) {
+    const int mid = (lo + hi) >> 1;
+    if (a[mid] <= x) lo = mid; else hi = mid;
+  }
+  return lo;
+}
+
+struct BlockItemLds {
+  int32_t alive[kDecodeBlockMaxSeq];       // alive tokens per sequence
+  int32_t key[kDecodeBlockMaxSeq + 4];     // first segment's physical block (sharing), else -1
+  int32_t fb[kDecodeBlockMaxSeq + 4];      // full blocks of the first segment
+  int32_t lc[kDecodeBlockMaxSeq];          // shared prefix blocks (0: none)
+  int32_t sub[kDecodeBlockMaxSeq];         // sub-group id: leader * 64 + rank / members-per-item
+  int32_t rank[kDecodeBlockMaxSeq];        // rank among the sequences of its group
+  int32_t pfirst[kDecodeBlockMaxSeq + 1];  // first partial of each sequence
+  int32_t ifirst[kDecodeBlockMaxSeq + 1];  // first private item of each sequence
+  int32_t sfirst[kDecodeBlockMaxSeq + 1];  // first shared item of each sub-group head
+  int32_t red[3 * kBHkv];
+  int32_t mem[16];   // this item's sequences
+  int32_t pidx[16];  // their partial index (-1: the item writes the output itself)
+};
+
+template <int G, int NT>
+__device__ __forceinline__ void block_stream(const DecodeParams& p, int nmem, const int32_t* mem,
+                                             const int32_t* pidx, int nblk, const int32_t* blk_phys,
+                                             int last_local, int last_tokens,
+                                             uint8_t (*kv_lds)[2][kBHkv][kMBlock]) {
   constexpr int D = kMD;
-  // [stage][K, V][wavefront] blocks of one head; during set-up the same
-  // bytes hold the staged segment list
-  __shared__ __align__(16) uint8_t kv_lds[2][2][kBHkv][kMBlock];
-  __shared__ __align__(16) int32_t blk_phys[kMaxSplitBlocks];
-  __shared__ int32_t s_alive[kDecodeBlockMaxSeq];      // alive tokens per sequence
-  __shared__ int32_t s_first[kDecodeBlockMaxSeq + 1];  // first split of each sequence
-  __shared__ int32_t s_red[kBHkv];
-  static_assert(sizeof(kv_lds) >= 3 * (kMaxSplitBlocks + 1) * sizeof(int32_t), "staging");
-
+  constexpr int kMPT = 16 / G;  // member sequences per column tile
   const int tid = threadIdx.x, lane = tid & (kWave - 1);
-  const int g = __builtin_amdgcn_readfirstlane(tid / kWave);  // this wavefront's KV head
+  const int g = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int hl = lane % 16, q4 = lane / 16;
-  const int B = p.B, id = blockIdx.x;
 
-  // ---- split counts of all sequences --------------------------------------
-  // thread t holds sequences [i0, i1)
-  const int per = (B + kBThreads - 1) / kBThreads;
-  const int i0 = min(B, tid * per), i1 = min(B, i0 + per);
-  int wsum = 0, nz = 0, cut = 0;
-  for (int i = i0; i < i1; ++i) {
-    const int a0 = p.indptr[i], a1 = p.indptr[i + 1];
-    int A = 0;
-    if (a1 > a0) {
-      const msa_segment l = p.segs[a1 - 1];
-      A = max(0, l.alive_token_start + l.num_tokens);
-    }
-    s_alive[i] = A;
-    const int nb = (A + kBlk - 1) / kBlk;
-    const int nbc = min(nb, p.cap_blocks);
-    cut |= nb > nbc;
-    wsum += nbc;
-    nz += nbc > 0;
-  }
-  // splits of this thread's sequences at length T (an empty sequence still
-  // gets one workgroup: it writes O = 0)
-  auto splits_of = [&](int T) {
-    int n = 0;
-    for (int i = i0; i < i1; ++i) n += max(1, (min((s_alive[i] + kBlk - 1) / kBlk, p.cap_blocks) + T - 1) / T);
-    return n;
-  };
-  int T = p.split_blocks;
-  if (p.block_auto) {
-    const int W = block_sum(wsum, s_red);
-    const int NZ = block_sum(nz, s_red);
-    const int target = p.block_target;
-    // T_hi = ceil(W / (target - NZ)) always gives at most target + (B - NZ)
-    // splits (target >= 2B on the host); the smallest T that gives at most
-    // target lies in [ceil(W / target), T_hi]
-    int lo = max(kBMinSplit, (W + target - 1) / target);
-    int hi = max(kBMinSplit, (W + (target - NZ) - 1) / (target - NZ));
-    lo = min(lo, kMaxSplitBlocks);
-    hi = min(max(hi, lo), kMaxSplitBlocks);
-    while (lo < hi) {
-      const int mid = (lo + hi) >> 1;
-      if (block_sum(splits_of(mid), s_red) <= target) hi = mid; else lo = mid + 1;
-    }
-    T = lo;
-  }
-  int total;
-  int run = block_excl_scan(splits_of(T), s_red, total);
-  for (int i = i0; i < i1; ++i) {
-    s_first[i] = run;
-    run += max(1, (min((s_alive[i] + kBlk - 1) / kBlk, p.cap_blocks) + T - 1) / T);
-  }
-  if (tid == 0) s_first[B] = total;
-  const bool any_cut = __syncthreads_or(cut) != 0;
-  if (id == 0) {
-    // the merge reads these; clamped to the grid so that it can never read
-    // a partial outside the workspace (the sizing rule keeps total <= grid)
-    for (int i = tid; i <= B; i += kBThreads) p.part_indptr[i] = min(s_first[i], int(gridDim.x));
-    if (tid == 0 && p.dev_error && (any_cut || total > int(gridDim.x)))
-      atomicOr(p.dev_error, MSA_DEVERR_TRUNCATED);
-  }
-  if (id >= total) return;
-  int b = 0;
-  {
-    int hi = B;
-    while (hi - b > 1) {
-      const int mid = (b + hi) >> 1;
-      if (s_first[mid] <= id) b = mid; else hi = mid;
-    }
-  }
-  const int Sb = s_first[b + 1] - s_first[b], s = id - s_first[b];
-  const int A = s_alive[b];
-  const int nAB = min((A + kBlk - 1) / kBlk, p.cap_blocks);
-
-  // Q^T operand of this KV head's G query rows (lane l: head l%16, zero past
-  // G, d 32 ds + 8(l/16))
-  uint4 qop[4];
-  {
-    const uint8_t* qsrc = static_cast<const uint8_t*>(p.q) + (size_t(b) * p.Hq + size_t(g) * G + hl) * kMRow;
+  // Q^T operand of tile t (lane l: column l%16 = member t*kMPT + (l%16)/G,
+  // query head g*G + (l%16)%G; zero past the members; d 32 ds + 8(l/16))
+  uint4 qop[NT][4];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    const int m = t * kMPT + hl / G;
+    const bool on = m < nmem;
+    const size_t row = on ? (size_t(mem[m]) * p.Hq + size_t(g) * G + hl % G) : 0;
+    const uint8_t* qsrc = static_cast<const uint8_t*>(p.q) + row * kMRow;
 #pragma unroll
     for (int ds = 0; ds < 4; ++ds)
-      qop[ds] = hl < G ? *reinterpret_cast<const uint4*>(qsrc + (4 * ds + q4) * 16) : make_uint4(0, 0, 0, 0);
-  }
-  if (nAB == 0) {  // no alive token at all: O = 0, LSE = -inf
-    for (int i = tid; i < p.Hq * D; i += kBThreads) {
-      store_out<uint16_t>(p.out, size_t(b) * p.Hq * D + i, 0.f);
-      if (p.lse && i % D == 0) p.lse[size_t(b) * p.Hq + i / D] = -INFINITY;
-    }
-    return;
-  }
-  const int j0 = int(int64_t(s) * nAB / Sb);
-  const int nblk = int(int64_t(s + 1) * nAB / Sb) - j0;
-  const int last_tokens = min(kBlk, A - kBlk * (nAB - 1));
-  const int last_local = nAB - 1 - j0;
-
-  // ---- expand this split's segments into per-block physical ids ----------
-  {
-    const int s0 = p.indptr[b], s1 = p.indptr[b + 1];
-    const int sf = j0 == 0 ? s0 : wg_search_segment_n<kBThreads>(p.segs, s0, s1, j0 * kBlk);
-    const int ns = min(nblk, s1 - sf);
-    int32_t* st_start = reinterpret_cast<int32_t*>(&kv_lds[0][0][0][0]);
-    int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
-    int32_t* st_nblk = st_phys + kMaxSplitBlocks + 1;
-    for (int i = tid; i < ns; i += kBThreads) {
-      const msa_segment sg = p.segs[sf + i];
-      st_start[i] = sg.alive_token_start / kBlk;
-      const bool in_pool = sg.phys_block >= 0 && sg.num_blocks >= 0 &&
-                           int64_t(sg.phys_block) + sg.num_blocks <= p.P;
-      st_phys[i] = in_pool ? sg.phys_block : -1;
-      st_nblk[i] = in_pool ? sg.num_blocks : 0;
-    }
-    __syncthreads();
-    for (int jj = tid; jj < nblk; jj += kBThreads) {
-      const int j = j0 + jj;
-      int lo = 0, hi = ns;
-      while (hi - lo > 1) {
-        const int mid = (lo + hi) >> 1;
-        if (st_start[mid] <= j) lo = mid; else hi = mid;
-      }
-      const int off = j - st_start[lo];
-      blk_phys[jj] = (st_phys[lo] >= 0 && off >= 0 && off < st_nblk[lo]) ? st_phys[lo] + off : -1;
-    }
-    __syncthreads();  // staging dead from here on: the ring may overwrite it
+      qop[t][ds] = on ? *reinterpret_cast<const uint4*>(qsrc + (4 * ds + q4) * 16) : make_uint4(0, 0, 0, 0);
   }
 
   const size_t tok_stride = p.head_major ? size_t(kMRow) : size_t(p.Hkv) * kMRow;
@@ -1086,8 +1031,8 @@ __global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams
   auto vrow_off = [&](int dg) { return vr_base + 16 * ((2 * dg + (hl % 4) / 2) ^ ((2 * vr_key) & 15)); };
   const int k_off = hl * kMRow;  // + 16 ((4 ds + q4) ^ hl)
 
-  // (K, V) of block jj of the split into ring stage jj % 2: the wave-uniform
-  // physical id and readable rows (past the split or a dropped segment: an
+  // (K, V) of block jj of the item into ring stage jj % 2: the wave-uniform
+  // physical id and readable rows (past the item or a dropped segment: an
   // empty range, so the DMAs land zeros)
   auto issue = [&](int jj) {
     const int ph = jj < nblk ? __builtin_amdgcn_readfirstlane(blk_phys[jj]) : -1;
@@ -1115,10 +1060,17 @@ __global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams
     return rows;
   };
 
-  mf32x4_t o[8];
+  mf32x4_t o[NT][8];
 #pragma unroll
-  for (int dg = 0; dg < 8; ++dg) o[dg] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_lane = 0.f;
+  for (int t = 0; t < NT; ++t)
+#pragma unroll
+    for (int dg = 0; dg < 8; ++dg) o[t][dg] = mf32x4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run[NT], l_lane[NT];
+#pragma unroll
+  for (int t = 0; t < NT; ++t) {
+    m_run[t] = -INFINITY;
+    l_lane[t] = 0.f;
+  }
   const float c = p.scale_log2;
 
   int rows = issue(0);
@@ -1136,45 +1088,48 @@ __global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams
     uint2 vr[8];
 #pragma unroll
     for (int dg = 0; dg < 8; ++dg) vr[dg] = m_read_tr16(vt + vrow_off(dg));
-    // ---- S = K Q^T: lane l holds head l%16, keys 4(l/16) .. +3 ------------
-    mf32x4_t sc = mf32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int ds = 0; ds < 4; ++ds)
-      sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(kr[ds]), m_as_bf16x8(qop[ds]), sc, 0, 0, 0);
-    if (rows < kBlk) {
+    for (int t = 0; t < NT; ++t) {
+      // ---- S = K Q^T: lane l holds column l%16, keys 4(l/16) .. +3 --------
+      mf32x4_t sc = mf32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int r = 0; r < 4; ++r) sc[r] = 4 * q4 + r < rows ? sc[r] : -INFINITY;
-    }
-    // ---- online softmax per head (lane l%16), lazy rescale ----------------
-    float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
-    mx = fmaxf(mx, __shfl_xor(mx, 16));
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const bool bump = (mx - m_run) * c > 8.f;
-    const float m_use = bump ? mx : m_run;
-    const float nm = m_use == -INFINITY ? 0.f : -m_use * c;
-    const float alpha = (m_use == m_run) ? 1.f : __builtin_amdgcn_exp2f((m_run - m_use) * c);
-    if (__builtin_amdgcn_ballot_w64(bump) != 0) {
-      // O rows are heads 4(l/16) + r: fetch those heads' factors
-      float ar[4];
+      for (int ds = 0; ds < 4; ++ds)
+        sc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(m_as_bf16x8(kr[ds]), m_as_bf16x8(qop[t][ds]), sc, 0, 0, 0);
+      if (rows < kBlk) {
 #pragma unroll
-      for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r);
+        for (int r = 0; r < 4; ++r) sc[r] = 4 * q4 + r < rows ? sc[r] : -INFINITY;
+      }
+      // ---- online softmax per column, lazy rescale -------------------------
+      float mx = fmaxf(fmaxf(sc[0], sc[1]), fmaxf(sc[2], sc[3]));
+      mx = fmaxf(mx, __shfl_xor(mx, 16));
+      mx = fmaxf(mx, __shfl_xor(mx, 32));
+      const bool bump = (mx - m_run[t]) * c > 8.f;
+      const float m_use = bump ? mx : m_run[t];
+      const float nm = m_use == -INFINITY ? 0.f : -m_use * c;
+      const float alpha = (m_use == m_run[t]) ? 1.f : __builtin_amdgcn_exp2f((m_run[t] - m_use) * c);
+      if (__builtin_amdgcn_ballot_w64(bump) != 0) {
+        // O rows are columns 4(l/16) + r: fetch those columns' factors
+        float ar[4];
+#pragma unroll
+        for (int r = 0; r < 4; ++r) ar[r] = __shfl(alpha, 4 * q4 + r);
+#pragma unroll
+        for (int dg = 0; dg < 8; ++dg)
+#pragma unroll
+          for (int r = 0; r < 4; ++r) o[t][dg][r] *= ar[r];
+      }
+      m_run[t] = m_use;
+      float pw[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) pw[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, nm));
+      l_lane[t] = l_lane[t] * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
+      // ---- O += P V ---------------------------------------------------------
+      const ms16x4_t pop = __builtin_bit_cast(ms16x4_t, make_uint2(m_cvt_pk_bf16(pw[0], pw[1]),
+                                                                   m_cvt_pk_bf16(pw[2], pw[3])));
 #pragma unroll
       for (int dg = 0; dg < 8; ++dg)
-#pragma unroll
-        for (int r = 0; r < 4; ++r) o[dg][r] *= ar[r];
+        o[t][dg] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop, __builtin_bit_cast(ms16x4_t, vr[dg]),
+                                                             o[t][dg], 0, 0, 0);
     }
-    m_run = m_use;
-    float pw[4];
-#pragma unroll
-    for (int r = 0; r < 4; ++r) pw[r] = __builtin_amdgcn_exp2f(fmaf(sc[r], c, nm));
-    l_lane = l_lane * alpha + ((pw[0] + pw[1]) + (pw[2] + pw[3]));
-    // ---- O += P V -----------------------------------------------------------
-    const ms16x4_t pop = __builtin_bit_cast(ms16x4_t, make_uint2(m_cvt_pk_bf16(pw[0], pw[1]),
-                                                                 m_cvt_pk_bf16(pw[2], pw[3])));
-#pragma unroll
-    for (int dg = 0; dg < 8; ++dg)
-      o[dg] = __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(pop, __builtin_bit_cast(ms16x4_t, vr[dg]), o[dg],
-                                                        0, 0, 0);
     // this stage is refilled by the next step's DMA: its reads must be back
     asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     rows = rows_next;
@@ -1182,36 +1137,313 @@ __global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams
   // no DMA may be left in flight when the workgroup ends
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- write this wavefront's G heads --------------------------------------
-  const float l_w = l_lane + __shfl_xor(l_lane, 16);
-  const float l_h = l_w + __shfl_xor(l_w, 32);  // head hl's sum over the split
-  float lr[4];
+  // ---- write: column hh of tile t is member t*kMPT + hh/G, head hh%G -------
 #pragma unroll
-  for (int r = 0; r < 4; ++r) lr[r] = __shfl(l_h, 4 * q4 + r);
+  for (int t = 0; t < NT; ++t) {
+    const float l_w = l_lane[t] + __shfl_xor(l_lane[t], 16);
+    const float l_h = l_w + __shfl_xor(l_w, 32);  // column hl's sum over the item
+    float lr[4];
 #pragma unroll
-  for (int dg = 0; dg < 8; ++dg)
+    for (int r = 0; r < 4; ++r) lr[r] = __shfl(l_h, 4 * q4 + r);
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
-      const int hh = 4 * q4 + r;
-      if (hh < G) {
-        const size_t h = size_t(g) * G + hh;
-        const int d = dg * 16 + hl;
-        if (Sb == 1)
-          store_out<uint16_t>(p.out, (size_t(b) * p.Hq + h) * D + d, lr[r] > 0.f ? o[dg][r] / lr[r] : 0.f);
-        else
-          p.o_part[(size_t(id) * p.Hq + h) * D + d] = o[dg][r];
+      const int hh = 4 * q4 + r, m = t * kMPT + hh / G;
+      if (m < nmem) {
+        const int b = mem[m], pi = pidx[m];
+        const size_t h = size_t(g) * G + hh % G;
+#pragma unroll
+        for (int dg = 0; dg < 8; ++dg) {
+          const int d = dg * 16 + hl;
+          if (pi < 0)
+            store_out<uint16_t>(p.out, (size_t(b) * p.Hq + h) * D + d, lr[r] > 0.f ? o[t][dg][r] / lr[r] : 0.f);
+          else if (pi < p.block_parts)
+            p.o_part[(size_t(pi) * p.Hq + h) * D + d] = o[t][dg][r];
+        }
       }
     }
-  if (q4 == 0 && hl < G) {
-    const size_t h = size_t(g) * G + hl;
-    const float Mc = m_run * c;  // log2 units
-    if (Sb == 1) {
-      if (p.lse) p.lse[size_t(b) * p.Hq + h] = l_h > 0.f ? (Mc + log2f(l_h)) * kLn2 : -INFINITY;
-    } else {
-      p.m_part[size_t(id) * p.Hq + h] = m_run == -INFINITY ? -INFINITY : Mc * kLn2;
-      p.l_part[size_t(id) * p.Hq + h] = l_h;
+    const int m = t * kMPT + hl / G;
+    if (q4 == 0 && m < nmem) {
+      const int b = mem[m], pi = pidx[m];
+      const size_t h = size_t(g) * G + hl % G;
+      const float Mc = m_run[t] * c;  // log2 units
+      if (pi < 0) {
+        if (p.lse) p.lse[size_t(b) * p.Hq + h] = l_h > 0.f ? (Mc + log2f(l_h)) * kLn2 : -INFINITY;
+      } else if (pi < p.block_parts) {
+        p.m_part[size_t(pi) * p.Hq + h] = m_run[t] == -INFINITY ? -INFINITY : Mc * kLn2;
+        p.l_part[size_t(pi) * p.Hq + h] = l_h;
+      }
     }
   }
+}
+
+template <int G>
+__global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams p) {
+  static_assert(G == 4 || G == 8, "heads padded to 16 MFMA rows");
+  constexpr int D = kMD;
+  constexpr int kMPI = kBShareTiles * 16 / G;  // member sequences per shared item
+  // [stage][K, V][wavefront] blocks of one head; during set-up the same
+  // bytes hold the staged segment list
+  __shared__ __align__(16) uint8_t kv_lds[2][2][kBHkv][kMBlock];
+  __shared__ __align__(16) int32_t blk_phys[kMaxSplitBlocks];
+  __shared__ __align__(16) BlockItemLds sh;
+  static_assert(sizeof(kv_lds) >= 3 * (kMaxSplitBlocks + 1) * sizeof(int32_t), "staging");
+
+  const int tid = threadIdx.x;
+  const int B = p.B, id = blockIdx.x;
+  const bool share = p.block_share != 0;
+
+  // ---- per sequence: alive tokens, first segment ---------------------------
+  // thread t holds sequences [i0, i1)
+  const int per = (B + kBThreads - 1) / kBThreads;
+  const int i0 = min(B, tid * per), i1 = min(B, i0 + per);
+  int cut = 0;
+  for (int i = i0; i < i1; ++i) {
+    const int a0 = p.indptr[i], a1 = p.indptr[i + 1];
+    int A = 0, key = -1, fb = 0;
+    if (a1 > a0) {
+      const msa_segment l = p.segs[a1 - 1];
+      A = max(0, l.alive_token_start + l.num_tokens);
+      if (share) {
+        const msa_segment f = p.segs[a0];
+        if (f.logical_block == 0 && f.phys_block >= 0 && f.num_blocks > 0 &&
+            int64_t(f.phys_block) + f.num_blocks <= p.P) {
+          key = f.phys_block;
+          fb = min(f.num_tokens / kBlk, f.num_blocks);
+        }
+      }
+    }
+    const int nb = (A + kBlk - 1) / kBlk;
+    const int nbc = min(nb, p.cap_blocks);
+    cut |= nb > nbc;
+    sh.alive[i] = A;
+    sh.key[i] = key;
+    sh.fb[i] = min(fb, nbc);
+  }
+  if (tid < 4 && B + tid < kDecodeBlockMaxSeq + 4) {
+    sh.key[B + tid] = -1;
+    sh.fb[B + tid] = 0;
+  }
+  __syncthreads();
+  // ---- sharing: groups of equal first physical block, their common prefix --
+  for (int i = i0; i < i1; ++i) {
+    int lc = 0, sub = -1, rank = 0;
+    const int key = sh.key[i];
+    if (key >= 0) {
+      int size = 0, lmin = sh.fb[i], lead = i;
+      // four sequences per LDS read (the arrays are padded with key -1)
+      for (int j4 = 0; j4 < B; j4 += 4) {
+        const int4 k4 = *reinterpret_cast<const int4*>(&sh.key[j4]);
+        const int4 f4 = *reinterpret_cast<const int4*>(&sh.fb[j4]);
+        const int kk[4] = {k4.x, k4.y, k4.z, k4.w}, ff[4] = {f4.x, f4.y, f4.z, f4.w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const int j = j4 + u;
+          const bool same = kk[u] == key;
+          size += same;
+          rank += same && j < i;
+          lead = same ? min(lead, j) : lead;
+          lmin = same ? min(lmin, ff[u]) : lmin;
+        }
+      }
+      if (size >= 2 && lmin >= kBMinShare) {
+        lc = lmin;
+        sub = lead * 64 + rank / kMPI;
+      }
+    }
+    sh.lc[i] = lc;
+    sh.sub[i] = sub;
+    sh.rank[i] = rank;
+  }
+  __syncthreads();
+  // members join sub-groups in index order: the head is rank 0 of its sub-group
+  auto is_head = [&](int i) { return sh.lc[i] > 0 && sh.rank[i] % kMPI == 0; };
+  // items at split length T: private ones of a sequence, shared ones of a
+  // sub-group (counted at its head); each is one partial per sequence served
+  auto nbc_of = [&](int i) { return min((sh.alive[i] + kBlk - 1) / kBlk, p.cap_blocks); };
+  auto priv_items = [&](int i, int T) {
+    const int rest = nbc_of(i) - sh.lc[i];
+    return rest > 0 ? (rest + T - 1) / T : (sh.lc[i] == 0 ? 1 : 0);
+  };
+  auto shared_items = [&](int lc, int T) { return lc > 0 ? (lc + T - 1) / T : 0; };
+  int heads_mask = 0;  // bit k: sequence i0 + k heads its sub-group (per <= 2)
+  for (int i = i0; i < i1; ++i)
+    if (is_head(i)) heads_mask |= 1 << (i - i0);
+  int T = p.split_blocks;
+  if (p.block_auto) {
+    // blocks actually read and the ranges they come in
+    int wsum = 0, ranges = 0;
+    for (int i = i0; i < i1; ++i) {
+      const int rest = nbc_of(i) - sh.lc[i];
+      wsum += max(rest, 0);
+      ranges += rest > 0;
+      if ((heads_mask >> (i - i0)) & 1) {
+        wsum += sh.lc[i];
+        ranges += 1;
+      }
+    }
+    int W, NR;
+    block_sum2(wsum, ranges, sh.red, W, NR);
+    const int target = p.block_target;
+    // smallest T in [lo, hi] with at most target items and the partials
+    // within the workspace; both counts fall as T grows, and T =
+    // kMaxSplitBlocks always fits (the host sized grid and workspace for
+    // it).  Each round tests eight points of the interval, one per
+    // wavefront, each summing over all sequences in its own lanes.
+    int lo = min(max(kBMinSplit, (W + target - 1) / target), kMaxSplitBlocks);
+    int hi = kMaxSplitBlocks;
+    const int w = tid / kWave, lane = tid & (kWave - 1);
+    while (lo < hi) {
+      const int cand = lo + ((hi - lo) * (w + 1)) / 9;
+      int it = 0, pa = 0;
+      for (int i = lane; i < B; i += kWave) {
+        const int pv = priv_items(i, cand), sv = shared_items(sh.lc[i], cand);
+        it += pv + (is_head(i) ? sv : 0);
+        pa += pv + sv;
+      }
+      it = wave_sum(it);
+      pa = wave_sum(pa);
+      if (lane == 0) sh.red[w] = it <= target && pa <= p.block_parts;
+      __syncthreads();
+      int nlo = lo + ((hi - lo) * 8) / 9 + 1, nhi = hi;
+#pragma unroll
+      for (int k = kBHkv - 1; k >= 0; --k) {
+        if (sh.red[k]) {
+          nhi = lo + ((hi - lo) * (k + 1)) / 9;
+          nlo = k == 0 ? lo : lo + ((hi - lo) * k) / 9 + 1;
+        }
+      }
+      __syncthreads();
+      lo = min(nlo, nhi);
+      hi = nhi;
+    }
+    T = lo;
+  }
+  // ---- number items and partials -------------------------------------------
+  {
+    int pv_mine = 0, sv_mine = 0, pa_mine = 0;
+    for (int i = i0; i < i1; ++i) {
+      const int pv = priv_items(i, T), sv = shared_items(sh.lc[i], T);
+      pv_mine += pv;
+      sv_mine += ((heads_mask >> (i - i0)) & 1) ? sv : 0;
+      pa_mine += pv + sv;
+    }
+    int np, ns, npa;
+    int rp, rs, ra;
+    block_excl_scan3(pv_mine, sv_mine, pa_mine, sh.red, rp, rs, ra, np, ns, npa);
+    for (int i = i0; i < i1; ++i) {
+      const int pv = priv_items(i, T), sv = shared_items(sh.lc[i], T);
+      sh.ifirst[i] = rp;
+      sh.sfirst[i] = np + rs;  // shared items follow the private ones
+      sh.pfirst[i] = ra;
+      rp += pv;
+      rs += ((heads_mask >> (i - i0)) & 1) ? sv : 0;
+      ra += pv + sv;
+    }
+    if (tid == 0) {
+      sh.ifirst[B] = np;
+      sh.sfirst[B] = np + ns;
+      sh.pfirst[B] = npa;
+    }
+  }
+  const bool any_cut = __syncthreads_or(cut) != 0;
+  const int n_items = sh.sfirst[B], n_parts = sh.pfirst[B];
+  if (id == 0) {
+    // the merge reads these; clamped to the workspace so that it can never
+    // read a partial outside it (the sizing rule keeps n_parts within it)
+    for (int i = tid; i <= B; i += kBThreads) p.part_indptr[i] = min(sh.pfirst[i], p.block_parts);
+    if (tid == 0 && p.dev_error && (any_cut || n_items > int(gridDim.x) || n_parts > p.block_parts))
+      atomicOr(p.dev_error, MSA_DEVERR_TRUNCATED);
+  }
+  if (id >= n_items || n_parts > p.block_parts) return;
+
+  // ---- this item: its sequences, their partials, its blocks ---------------
+  int nmem, j0, nblk, last_local, last_tokens;
+  bool shared_item;
+  if (id < sh.ifirst[B]) {
+    // private item s of sequence b: blocks [lc + s*rest/Sp, ...)
+    shared_item = false;
+    const int b = lds_upper(sh.ifirst, B, id);
+    const int Sp = max(1, sh.ifirst[b + 1] - sh.ifirst[b]), s = min(id - sh.ifirst[b], Sp - 1);
+    const int A = sh.alive[b], nbc = nbc_of(b), lc = sh.lc[b];
+    const int rest = nbc - lc;
+    nmem = 1;
+    if (tid == 0) {
+      sh.mem[0] = b;
+      // one partial in all: the item writes the output itself
+      sh.pidx[0] = sh.pfirst[b + 1] - sh.pfirst[b] == 1 ? -1 : sh.pfirst[b] + s;
+    }
+    if (rest <= 0) {
+      nblk = 0;  // no alive block at all (a sequence with a shared prefix always has rest > 0 here)
+      j0 = 0;
+    } else {
+      j0 = lc + int(int64_t(s) * rest / Sp);
+      nblk = lc + int(int64_t(s + 1) * rest / Sp) - j0;
+    }
+    last_local = nbc - 1 - j0;
+    last_tokens = nbc > 0 ? min(kBlk, A - kBlk * (nbc - 1)) : 0;
+    if (nblk > 0) {
+      // expand the item's segments into per-block physical ids
+      const int s0 = p.indptr[b], s1 = p.indptr[b + 1];
+      const int sf = j0 == 0 ? s0 : wg_search_segment_n<kBThreads>(p.segs, s0, s1, j0 * kBlk);
+      const int ns = min(nblk, s1 - sf);
+      int32_t* st_start = reinterpret_cast<int32_t*>(&kv_lds[0][0][0][0]);
+      int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
+      int32_t* st_nblk = st_phys + kMaxSplitBlocks + 1;
+      for (int i = tid; i < ns; i += kBThreads) {
+        const msa_segment sg = p.segs[sf + i];
+        st_start[i] = sg.alive_token_start / kBlk;
+        const bool in_pool = sg.phys_block >= 0 && sg.num_blocks >= 0 &&
+                             int64_t(sg.phys_block) + sg.num_blocks <= p.P;
+        st_phys[i] = in_pool ? sg.phys_block : -1;
+        st_nblk[i] = in_pool ? sg.num_blocks : 0;
+      }
+      __syncthreads();
+      for (int jj = tid; jj < nblk; jj += kBThreads) {
+        const int j = j0 + jj;
+        const int lo = lds_upper(st_start, ns, j);
+        const int off = j - st_start[lo];
+        blk_phys[jj] = (st_phys[lo] >= 0 && off >= 0 && off < st_nblk[lo]) ? st_phys[lo] + off : -1;
+      }
+    }
+  } else {
+    // shared item s of the sub-group headed by sequence hd: blocks
+    // [s*lc/Ss, (s+1)*lc/Ss) of the common prefix, all in the first segment
+    shared_item = true;
+    const int hd = lds_upper(sh.sfirst, B, id);
+    const int lc = sh.lc[hd], sub = sh.sub[hd];
+    const int Ss = max(1, (lc + T - 1) / T), s = min(id - sh.sfirst[hd], Ss - 1);
+    j0 = int(int64_t(s) * lc / Ss);
+    nblk = int(int64_t(s + 1) * lc / Ss) - j0;
+    last_local = -1;  // full blocks only
+    last_tokens = kBlk;
+    // the members, in index order: slot rank % kMPI
+    int mine = 0;
+    for (int j = hd + tid; j < B; j += kBThreads) {
+      if (sh.sub[j] == sub) {
+        const int slot = sh.rank[j] % kMPI;
+        sh.mem[slot] = j;
+        sh.pidx[slot] = sh.pfirst[j + 1] - sh.pfirst[j] == 1 ? -1 : sh.pfirst[j] + priv_items(j, T) + s;
+        ++mine;
+      }
+    }
+    const int ph0 = sh.key[hd] + j0;
+    for (int jj = tid; jj < nblk; jj += kBThreads) blk_phys[jj] = ph0 + jj;
+    nmem = __syncthreads_count(mine);
+  }
+  __syncthreads();  // staging dead from here on: the ring may overwrite it
+
+  if (nblk == 0) {  // no alive token at all: O = 0, LSE = -inf
+    const int b = sh.mem[0];
+    for (int i = tid; i < p.Hq * D; i += kBThreads) {
+      store_out<uint16_t>(p.out, size_t(b) * p.Hq * D + i, 0.f);
+      if (p.lse && i % D == 0) p.lse[size_t(b) * p.Hq + i / D] = -INFINITY;
+    }
+    return;
+  }
+  if (shared_item)
+    block_stream<G, kBShareTiles>(p, nmem, sh.mem, sh.pidx, nblk, blk_phys, last_local, last_tokens, kv_lds);
+  else
+    block_stream<G, 1>(p, nmem, sh.mem, sh.pidx, nblk, blk_phys, last_local, last_tokens, kv_lds);
 }
 
 template <typename KV, int D, int G>
@@ -1321,22 +1553,27 @@ bool decode_block_supported(msa_dtype dtype, int32_t D, int32_t Hkv, int32_t G, 
 
 int32_t decode_block_target(int32_t B) { return kCUs > 2 * B ? kCUs : 2 * B; }
 
-// Workgroups of the block kernel's grid: at least the number of splits its
-// device-side rule can make.  With T = ceil(W / (target - NZ)) the splits
-// number at most W / T + B <= target + B; a T capped at the longest split
-// gives at most cap * B / kMaxSplitBlocks + B; a caller's split_blocks T at
-// most cap * B / T + B.
-int64_t decode_block_grid(int32_t B, int32_t cap_blocks, int32_t split_blocks) {
+// Workgroups and partials of the block kernel.  A sequence's alive blocks
+// (at most cap) come in at most two ranges, a shared prefix and the rest, so
+// at split length T there are at most cap * B / T + 2B items and as many
+// partials.  The device rule keeps the items within target and the partials
+// within its capacity whenever some T <= kMaxSplitBlocks does, and T =
+// kMaxSplitBlocks always does with these sizes; a caller's T sizes both.
+BlockSizes decode_block_sizes(int32_t B, int32_t cap_blocks, int32_t split_blocks) {
   const int64_t work = int64_t(cap_blocks) * B;
-  int64_t n;
+  BlockSizes z;
   if (split_blocks > 0) {
-    n = (work + split_blocks - 1) / split_blocks;
+    z.items = z.parts = (work + split_blocks - 1) / split_blocks + 2 * int64_t(B);
   } else {
-    n = (work + kMaxSplitBlocks - 1) / kMaxSplitBlocks;
-    if (n < decode_block_target(B)) n = decode_block_target(B);
+    const int64_t at_max = (work + kMaxSplitBlocks - 1) / kMaxSplitBlocks;
+    const int64_t target = decode_block_target(B);
+    z.items = (at_max > target ? at_max : target) + 2 * int64_t(B);
+    z.parts = (at_max > 2 * target ? at_max : 2 * target) + 2 * int64_t(B);
   }
-  return n + B;
+  return z;
 }
+
+bool decode_block_shares(int32_t B) { return B >= 2 && B <= kDecodeBlockMaxShareSeq; }
 
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
   if (p.dtype == MSA_BF16) {

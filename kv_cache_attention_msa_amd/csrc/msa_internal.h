@@ -102,6 +102,8 @@ struct DecodeParams {
   int32_t nwg;           // its grid
   int32_t block_auto;    // 1: split length from the device rule, 0: split_blocks
   int32_t block_target;  // workgroups the device rule aims at
+  int32_t block_parts;   // partials the workspace holds
+  int32_t block_share;   // 1: common prefixes of sequences are streamed once per sub-group
   int32_t cap_blocks;    // alive blocks a sequence may use (S * split_blocks)
   int32_t* part_indptr;  // [B+1] first partial of each sequence (written by workgroup 0)
   void* out;
@@ -162,11 +164,17 @@ SplitPlan prefill_split(int32_t B, int32_t C, int32_t Hq, int32_t Hkv, int32_t m
 bool decode_supported(msa_dtype dtype, int32_t D, int32_t G);
 bool decode_matrix_supported(msa_dtype dtype, int32_t D, int32_t G);
 int32_t decode_max_split_blocks();
-// block kernel: shapes it is built for, its split rule's target and its grid
-constexpr int kDecodeBlockMaxSeq = 1024;
+// block kernel: shapes it is built for, its split rule's target, its grid
+// and partial capacity, and when it shares common prefixes
+constexpr int kDecodeBlockMaxSeq = 512;
+constexpr int kDecodeBlockMaxShareSeq = 256;
+struct BlockSizes {
+  int64_t items, parts;
+};
 bool decode_block_supported(msa_dtype dtype, int32_t D, int32_t Hkv, int32_t G, int32_t B);
 int32_t decode_block_target(int32_t B);
-int64_t decode_block_grid(int32_t B, int32_t cap_blocks, int32_t split_blocks);
+BlockSizes decode_block_sizes(int32_t B, int32_t cap_blocks, int32_t split_blocks);
+bool decode_block_shares(int32_t B);
 int32_t prefill_max_split_blocks();
 bool prefill_supported(msa_dtype dtype, int32_t D, int32_t G);
 int32_t prefill_chunk_rows(int32_t B, int32_t Hq, int32_t Hkv, int32_t remaining,

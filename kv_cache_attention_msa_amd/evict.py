@@ -12,9 +12,14 @@ around the kernels of this library:
   need to rebuild the block, from its measured throughput;
 * kernel cost: what keeping the block costs every decode step, from a
   latency model of our decode kernel fitted to measurements
-  (time = c0 + c_tok * alive tokens + c_seg * segments).  Evicting a block
-  removes its tokens and changes the segment count by -1, 0 or +1 depending
-  on whether its logical neighbours are alive and physically adjacent.
+  (time = c0 + c_tok * alive tokens + c_seg * segments + c_max * the longest
+  sequence's alive tokens).  Evicting a block removes its tokens, changes
+  the segment count by -1, 0 or +1 depending on whether its logical
+  neighbours are alive and physically adjacent, and shortens the longest
+  sequence if it is taken from it: when every (sequence, KV head) pair is
+  one workgroup and the pairs fill the chip, the call lasts as long as the
+  longest sequence's workgroups, so tokens of shorter sequences cost the
+  step almost nothing.
 
 Readings of the pages (they state the formula with a minus sign on the cost
 term and, in the same passage, say that costly positions are kept; the
@@ -44,24 +49,31 @@ import numpy as np
 @dataclass
 class DecodeLatencyModel:
     """Predicted msa_decode time (microseconds) of one batch:
-    c0 + c_tok * alive_tokens + c_seg * segments."""
+    c0 + c_tok * alive_tokens + c_seg * segments + c_max * max_seq_tokens
+    (alive tokens of the batch's longest sequence)."""
     c0: float
     c_tok: float
     c_seg: float
+    c_max: float = 0.0
 
-    def predict(self, alive_tokens, segments):
+    def predict(self, alive_tokens, segments, max_seq_tokens=0):
         return self.c0 + self.c_tok * np.asarray(alive_tokens, dtype=np.float64) + \
-            self.c_seg * np.asarray(segments, dtype=np.float64)
+            self.c_seg * np.asarray(segments, dtype=np.float64) + \
+            self.c_max * np.asarray(max_seq_tokens, dtype=np.float64)
 
     @staticmethod
-    def fit(alive_tokens, segments, times_us) -> "DecodeLatencyModel":
-        """Least-squares fit to measured (alive tokens, segments, time) triples."""
+    def fit(alive_tokens, segments, times_us, max_seq_tokens=None) -> "DecodeLatencyModel":
+        """Least-squares fit to measured (alive tokens, segments[, longest
+        sequence's alive tokens], time) points."""
         a = np.asarray(alive_tokens, dtype=np.float64)
         s = np.asarray(segments, dtype=np.float64)
         t = np.asarray(times_us, dtype=np.float64)
-        X = np.stack([np.ones_like(a), a, s], axis=1)
-        coef, *_ = np.linalg.lstsq(X, t, rcond=None)
-        return DecodeLatencyModel(float(coef[0]), float(coef[1]), float(coef[2]))
+        cols = [np.ones_like(a), a, s]
+        if max_seq_tokens is not None:
+            cols.append(np.asarray(max_seq_tokens, dtype=np.float64))
+        coef, *_ = np.linalg.lstsq(np.stack(cols, axis=1), t, rcond=None)
+        return DecodeLatencyModel(float(coef[0]), float(coef[1]), float(coef[2]),
+                                  float(coef[3]) if max_seq_tokens is not None else 0.0)
 
 
 def _block_tokens(ctx_len, nb, bs):
@@ -107,6 +119,37 @@ def recompute_cost_us(alive_row, ctx_len, bs, D, Hq, prefill_tflops, mode="suffi
     return pairs.astype(np.float64) * 4.0 * D * Hq / (prefill_tflops * 1e12) * 1e6
 
 
+def alive_tokens(alive, ctx_len, block_size):
+    """Alive tokens of every sequence (the last block holds ctx_len mod bs)."""
+    al = np.asarray(alive)
+    bs = int(block_size)
+    out = np.zeros(al.shape[0], dtype=np.int64)
+    for b in range(al.shape[0]):
+        nb = -(-int(ctx_len[b]) // bs)
+        out[b] = int(np.dot(al[b, :nb] != 0, _block_tokens(ctx_len[b], nb, bs)))
+    return out
+
+
+def max_seq_gain(seq_tokens, b, tokens):
+    """How much the batch's longest alive-token count falls when `tokens`
+    alive tokens of sequence b go: nothing unless b is the only longest
+    sequence, then at most down to the second longest."""
+    A = np.asarray(seq_tokens)
+    top = A[b]
+    if len(A) > 1:
+        others = np.delete(A, b)
+        second = int(others.max())
+    else:
+        second = 0
+    if top < second or (top == second and len(A) > 1):
+        return 0
+    return int(min(tokens, top - second))
+
+
+def _saving(model, tok, ds, max_gain):
+    return model.c_tok * tok - model.c_seg * ds + model.c_max * max_gain
+
+
 def eviction_scores(block_table, alive, ctx_len, block_size, hit_prob, recompute_us,
                     model: DecodeLatencyModel, alpha=1.0, beta=1.0, gamma=1.0, batch_seqs=1):
     """Keep-scores of every block (higher = keep); +inf where a block cannot be
@@ -115,12 +158,14 @@ def eviction_scores(block_table, alive, ctx_len, block_size, hit_prob, recompute
 
     score = alpha * hit_prob + beta * recompute_us - gamma * saving_us, where
     saving_us is the decode time one step saves when the block is gone,
-    predicted by the latency model (tokens removed, segments changed) and
-    shared over batch_seqs sequences per decode batch."""
+    predicted by the latency model (tokens removed, segments changed, the
+    longest sequence shortened) and shared over batch_seqs sequences per
+    decode batch."""
     table = np.asarray(block_table)
     al = np.asarray(alive)
     B, mb = table.shape
     bs = int(block_size)
+    seq_tok = alive_tokens(al, ctx_len, bs)
     scores = np.full((B, mb), np.inf)
     for b in range(B):
         nb = -(-int(ctx_len[b]) // bs)
@@ -129,38 +174,60 @@ def eviction_scores(block_table, alive, ctx_len, block_size, hit_prob, recompute
             if not al[b, l]:
                 continue
             ds = segment_delta(table[b], al[b], l)
-            saving = model.c_tok * tok[l] - model.c_seg * ds
-            scores[b, l] = alpha * hit_prob[b, l] + beta * recompute_us[b][l] - gamma * saving / batch_seqs
+            gain = max_seq_gain(seq_tok, b, tok[l]) if model.c_max else 0
+            scores[b, l] = alpha * hit_prob[b, l] + beta * recompute_us[b][l] - \
+                gamma * _saving(model, tok[l], ds, gain) / batch_seqs
     return scores
 
 
 def choose_evictions(block_table, alive, ctx_len, block_size, n_evict, hit_prob, recompute_us,
                      model: DecodeLatencyModel, alpha=1.0, beta=1.0, gamma=1.0, batch_seqs=1):
     """Evict n_evict blocks, lowest score first.  After each eviction the
-    neighbours' segment deltas (and so their scores) are recomputed, since
-    whether they split or end a segment has changed.  Returns the new alive
+    scores that changed are recomputed: the neighbours' (whether they split
+    or end a segment has changed) and, with a longest-sequence term, every
+    block of the sequences that were or now are among the two longest (their
+    share of the longest sequence's time has moved).  Returns the new alive
     mask (uint8, same shape) and the list of evicted (b, l) in order."""
     table = np.asarray(block_table)
     al = np.array(alive, dtype=np.uint8, copy=True)
     bs = int(block_size)
+    B = table.shape[0]
+    seq_tok = alive_tokens(al, ctx_len, bs)
     sc = eviction_scores(table, al, ctx_len, bs, hit_prob, recompute_us, model, alpha, beta,
                          gamma, batch_seqs)
     heap = [(sc[b, l], b, l) for b, l in zip(*np.nonzero(np.isfinite(sc)))]
     heapq.heapify(heap)
     evicted = []
+
+    def rescore(b, l):
+        nb = -(-int(ctx_len[b]) // bs)
+        tok = _block_tokens(ctx_len[b], nb, bs)
+        ds = segment_delta(table[b], al[b], l)
+        gain = max_seq_gain(seq_tok, b, tok[l]) if model.c_max else 0
+        sc[b, l] = alpha * hit_prob[b, l] + beta * recompute_us[b][l] - \
+            gamma * _saving(model, tok[l], ds, gain) / batch_seqs
+        heapq.heappush(heap, (sc[b, l], b, l))
+
+    def top2():
+        return set(np.argsort(-seq_tok, kind="stable")[:2].tolist()) if B else set()
+
     while heap and len(evicted) < n_evict:
         s, b, l = heapq.heappop(heap)
         if not al[b, l] or s != sc[b, l]:
             continue  # stale entry
+        before = top2() if model.c_max else set()
         al[b, l] = 0
         sc[b, l] = np.inf
         evicted.append((int(b), int(l)))
         nb = -(-int(ctx_len[b]) // bs)
-        tok = _block_tokens(ctx_len[b], nb, bs)
+        seq_tok[b] -= int(_block_tokens(ctx_len[b], nb, bs)[l])
         for nl in (l - 1, l + 1):
             if 0 <= nl < nb - 1 and al[b, nl]:
-                ds = segment_delta(table[b], al[b], nl)
-                saving = model.c_tok * tok[nl] - model.c_seg * ds
-                sc[b, nl] = alpha * hit_prob[b, nl] + beta * recompute_us[b][nl] - gamma * saving / batch_seqs
-                heapq.heappush(heap, (sc[b, nl], b, nl))
+                rescore(b, nl)
+        if model.c_max:
+            for bb in before | top2() | {b}:
+                nbb = -(-int(ctx_len[bb]) // bs)
+                for ll in range(nbb - 1):
+                    if al[bb, ll]:
+                        rescore(bb, ll)
     return al, evicted

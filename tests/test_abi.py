@@ -124,9 +124,9 @@ def test_decode_kernel_choice_is_validated():
         assert _decode_ex(lib, kernel=_lib.MSA_DECODE_MATRIX, Hq=hq, D=d,
                           dtype=dt) == _lib.MSA_ERR_UNSUPPORTED, (hq, d, dt)
     # the block kernel: bf16, D 128, 8 KV heads, 4 or 8 query heads per KV
-    # head, at most 1024 sequences
+    # head, at most 512 sequences
     for kw in (dict(Hq=16, Hkv=4), dict(Hq=64, Hkv=16), dict(D=64), dict(dtype=_lib.MSA_F32, D=64),
-               dict(Hq=16), dict(B=1025)):
+               dict(Hq=16), dict(B=513)):
         assert _decode_ex(lib, kernel=_lib.MSA_DECODE_BLOCK, **kw) == _lib.MSA_ERR_UNSUPPORTED, kw
     # the shape checks still come first
     assert _decode_ex(lib, kernel=_lib.MSA_DECODE_VECTOR, Hq=24) == _lib.MSA_ERR_UNSUPPORTED
@@ -149,18 +149,18 @@ def test_decode_workspace_arithmetic():
     per_head = _aligned(4 * B * S * Hq * D, 4 * B * S * Hq, 4 * B * S * Hq)
     assert lib.msa_decode_workspace_size(B, Hq, 4, D, ctx, 16, T) == per_head
     # 8 KV heads (the block kernel may run): the larger of that and the block
-    # kernel's, which holds a partial per workgroup of its grid -- at most
-    # cap*B/T + B splits, cap = S*T alive blocks per sequence -- and B+1
-    # partial offsets
+    # kernel's, which holds its partials -- at most cap*B/T + 2B, cap = S*T
+    # alive blocks per sequence in at most two ranges -- and B+1 offsets
     Hq = 32
     per_head = _aligned(4 * B * S * Hq * D, 4 * B * S * Hq, 4 * B * S * Hq)
-    nwg = -(-(S * T * B) // T) + B
+    nwg = -(-(S * T * B) // T) + 2 * B
     block = _aligned(4 * nwg * Hq * D, 4 * nwg * Hq, 4 * nwg * Hq, 4 * (B + 1))
     assert lib.msa_decode_workspace_size(B, Hq, 8, D, ctx, 16, T) == max(per_head, block)
-    # automatic split: the grid aims at max(256, 2B) workgroups (+ B)
+    # automatic split: the grid aims at max(256, 2B) workgroups; the partials
+    # hold twice that (+ 2B: a shared prefix and the rest per sequence)
     for B in (1, 32, 300):
-        nwg = max(256, 2 * B) + B
-        block = _aligned(4 * nwg * Hq * D, 4 * nwg * Hq, 4 * nwg * Hq, 4 * (B + 1))
+        nparts = 2 * max(256, 2 * B) + 2 * B
+        block = _aligned(4 * nparts * Hq * D, 4 * nparts * Hq, 4 * nparts * Hq, 4 * (B + 1))
         assert lib.msa_decode_workspace_size(B, Hq, 8, D, 4096, 16, 0) >= block
         assert lib.msa_decode_workspace_size(B, Hq, 8, 64, 4096, 16, 0) < block
 

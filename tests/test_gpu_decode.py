@@ -386,11 +386,11 @@ def test_decode_block_kernel_empty_and_tiny_sequences():
         check(w, O, L, seqs=[1, 2, 4])
 
 
-@pytest.mark.parametrize("B,ctx", [(1, 5000), (3, 900), (97, 300), (1024, 100)])
+@pytest.mark.parametrize("B,ctx", [(1, 5000), (3, 900), (97, 300), (257, 200), (512, 100)])
 def test_decode_block_kernel_batch_sizes(B, ctx):
-    """From one sequence (every workgroup on one sequence) to the 1024 the
-    block kernel takes (one or two splits each); the device split rule sees
-    every count."""
+    """From one sequence (every workgroup on one sequence) to the 512 the
+    block kernel takes (one or two splits each), across the 256 up to which
+    it looks for shared prefixes; the device split rule sees every count."""
     w = make_workload(2, seed=4, size="small", B=B, ctx=ctx, pool_factor=2.0)
     O, L = run_decode(w, 0, kernel="block")
     seqs = sorted(set([0, B // 2, B - 1]))
@@ -439,3 +439,70 @@ def test_decode_block_kernel_determinism_full():
     for _ in range(2):
         O2, L2 = run_decode(w, 0, d)
         assert np.array_equal(O1, O2) and np.array_equal(L1, L2)
+
+
+def _shared_prefix_batch(Hq, seed=0):
+    """Twenty-one sequences over one pool of finite bf16 values, built so that
+    the block kernel's prefix sharing meets its edge cases:
+      * sequences 0-17 start on the same 20 physical blocks (17 members with
+        sequence 8 left out below: a sub-group with a single member is left
+        over); their private blocks follow, some evicted;
+      * sequence 3 lies entirely inside 12 of those blocks, and sequence 5
+        ends in a partial block inside its first segment (9 full blocks), so
+        the common prefix of the group is 9 blocks;
+      * sequence 8 has block 0 evicted: its first segment does not start at
+        logical block 0, so it is not a member;
+      * sequences 18 and 19 share only 5 blocks (fewer than the kernel
+        shares);
+      * sequence 20 shares nothing."""
+    from workloads.gen import Workload, f32_to_bf16_bits
+    rng = np.random.default_rng(seed)
+    B, Hkv, D, bs, P = 21, 8, 128, 16, 640
+    nbmax = 48
+    table = np.full((B, nbmax), -1, np.int32)
+    alive = np.zeros((B, nbmax), np.uint8)
+    ctx = np.zeros(B, np.int32)
+    free = list(rng.permutation(np.arange(40, P)))
+    for b in range(B):
+        nb = int(rng.integers(24, nbmax + 1))
+        if b < 18:
+            shared = list(range(0, 20))
+        elif b < 20:
+            shared = list(range(20, 25))
+        else:
+            shared = []
+        priv = [int(free.pop()) for _ in range(nb - len(shared))]
+        ids = shared + priv
+        table[b, :nb] = ids
+        alive[b, :nb] = 1
+        ctx[b] = nb * bs - int(rng.integers(0, bs))
+        # a few private evictions (never the last block)
+        for l in rng.choice(np.arange(len(shared), nb - 1), size=3, replace=False):
+            alive[b, l] = 0
+    ctx[3] = 12 * bs
+    alive[3, 12:] = 0
+    ctx[5] = 9 * bs + 7
+    alive[5, 10:] = 0
+    alive[8, 0] = 0
+    q = f32_to_bf16_bits(rng.standard_normal((B, Hq, D), dtype=np.float32))
+    k = f32_to_bf16_bits(rng.standard_normal((P, bs, Hkv, D), dtype=np.float32))
+    v = f32_to_bf16_bits(rng.standard_normal((P, bs, Hkv, D), dtype=np.float32))
+    return Workload(name="shared-prefix edge cases", kind="decode", dtype="bf16", B=B, Hq=Hq,
+                    Hkv=Hkv, D=D, block_size=bs, block_table=table, alive=alive, ctx_len=ctx,
+                    q=q, k_pool=k, v_pool=v, scale=1.0 / np.sqrt(D))
+
+
+@pytest.mark.parametrize("Hq", [32, 64])
+@pytest.mark.parametrize("split_blocks", [0, 4, 16])
+def test_decode_block_kernel_shared_prefixes(Hq, split_blocks):
+    """Prefix sharing in the block kernel (4 and 8 query heads per KV head:
+    8 and 4 member sequences per shared item): every sequence matches the
+    oracle, and the per-head kernel within the bf16 tolerance."""
+    w = _shared_prefix_batch(Hq)
+    d = to_device(w, DEV)
+    Ob, Lb = run_decode(w, split_blocks, d, kernel="block")
+    check(w, Ob, Lb)
+    Om, Lm = run_decode(w, split_blocks, d, kernel="matrix")
+    assert np.max(np.abs(Ob - Om)) <= TOL["bf16"]
+    (o_n, l_n), (o_h, l_h) = _decode_both_layouts(w, split_blocks, kernel="block")
+    assert torch.equal(o_n, o_h) and torch.equal(l_n, l_h)
