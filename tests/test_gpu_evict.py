@@ -1,9 +1,10 @@
 """Kernel-aware eviction on the GPU path: evictions chosen by the scorer
-(hit probability + recompute cost + decode cost from a latency model) and by
-hit probability alone are applied to a decode batch, then re-planned with
-msa_plan_segments and attended with msa_decode; both results must match the
-fp64 oracle over the surviving tokens, and the device plan must equal the
-oracle's plan of the new alive mask byte for byte."""
+(hit probability + recompute cost + decode cost from a latency model), by
+hit probability and a longest-sequence latency model, and by hit probability
+alone are applied to a decode batch, then re-planned with msa_plan_segments
+and attended with msa_decode; every result must match the fp64 oracle over
+the surviving tokens, and the device plan must equal the oracle's plan of
+the new alive mask byte for byte."""
 import numpy as np
 import pytest
 import torch
@@ -22,6 +23,8 @@ TOL = 2e-2
 # a latency model of the shape the decode kernel measures (per-token cost an
 # order of magnitude above the per-segment cost)
 MODEL = DecodeLatencyModel(c0=1.0, c_tok=8.0e-4, c_seg=6.7e-4)
+# the fitted shape on a one-split grid: the longest sequence sets the time
+MODEL_MAX = DecodeLatencyModel(c0=12.0, c_tok=4.3e-4, c_seg=0.0, c_max=5.2e-3)
 
 
 def _policies(w, frac):
@@ -33,11 +36,12 @@ def _policies(w, frac):
     n_alive = sum(int(w.alive[b, :nb[b] - 1].sum()) for b in range(w.B))
     n_ev = int(frac * n_alive)
     out = {}
-    for name, kw in (("kernel_aware", dict(alpha=float(np.mean([r.mean() for r in rec])), beta=1.0,
-                                           gamma=1000.0)),
-                     ("hit_only", dict(alpha=1.0, beta=0.0, gamma=0.0))):
+    for name, model, kw in (("kernel_aware", MODEL, dict(alpha=float(np.mean([r.mean() for r in rec])),
+                                                         beta=1.0, gamma=1000.0)),
+                            ("latency_aware", MODEL_MAX, dict(alpha=1.0, beta=0.0, gamma=10.0 * w.B)),
+                            ("hit_only", MODEL, dict(alpha=1.0, beta=0.0, gamma=0.0))):
         al, ev = choose_evictions(w.block_table, w.alive, w.ctx_len, w.block_size, n_ev, hit, rec,
-                                  MODEL, batch_seqs=w.B, **kw)
+                                  model, batch_seqs=w.B, **kw)
         assert len(ev) == n_ev
         out[name] = al
     return out
@@ -68,3 +72,9 @@ def test_scorer_evictions_through_plan_and_decode(cfg, frac):
     # the decode-cost term steers the scorer towards blocks whose eviction
     # does not split a segment
     assert segs_seen["kernel_aware"] <= segs_seen["hit_only"]
+    # the longest-sequence term shortens the longest sequence at least as
+    # much as hit probability alone
+    from kv_cache_attention_msa_amd.evict import alive_tokens
+    pol = _policies(w, frac)
+    assert alive_tokens(pol["latency_aware"], w.ctx_len, w.block_size).max() <= \
+        alive_tokens(pol["hit_only"], w.ctx_len, w.block_size).max()
