@@ -46,6 +46,8 @@ MFMA_BF16_PEAK_TFS = 2500.0  # MI355X dense bf16 MFMA, published
 COUNTERS = os.path.join(ROOT, "profiles", "decode_cfg2_counters.json")
 DECODE_SOURCES = ["decode.hip", "merge.hip", "msa_internal.h"]
 PF_COUNTERS = os.path.join(ROOT, "profiles", "prefill_cfg3_counters.json")
+COUNTERS4 = os.path.join(ROOT, "profiles", "decode_lognormal_counters.json")
+COUNTERS5 = os.path.join(ROOT, "profiles", "decode_131k_counters.json")
 PREFILL_SOURCES = ["prefill.hip", "msa_internal.h"]
 FLUSH_BYTES = 512 << 20  # twice the Infinity Cache (256 MB), far above L2
 
@@ -1021,6 +1023,8 @@ def main(argv=None):
         n = max(10, args.steps // 2)
         w4 = make_workload(4, seed=args.seed)
         leg, _ = decode_leg(w4, n, flush, kv_layout=layout, unique=True)
+        leg["roofline"]["traffic"] = counter_traffic(COUNTERS4, DECODE_SOURCES, split_blocks=0,
+                                                     kv_layout=args.kv_layout)
         if cpu:
             pick = sorted(np.random.default_rng(args.seed + 4).choice(w4.B, 4, replace=False).tolist())
             leg["cpu_baseline"] = decode_cpu_baseline(w4, seqs=pick, budget_s=4.0, single=False,
@@ -1029,6 +1033,8 @@ def main(argv=None):
         del w4
         w5 = make_workload(5, seed=args.seed)
         leg, _ = decode_leg(w5, n, flush, kv_layout=layout)
+        leg["roofline"]["traffic"] = counter_traffic(COUNTERS5, DECODE_SOURCES, split_blocks=0,
+                                                     kv_layout=args.kv_layout)
         if cpu:
             leg["cpu_baseline"] = decode_cpu_baseline(w5, seqs=[0], budget_s=4.0, single=False,
                                                       label="the 131k-token batch,")
