@@ -73,6 +73,8 @@ def parse(argv=None):
                     help="skip the vector against matrix-core decode kernel leg")
     ap.add_argument("--no-eviction", action="store_true",
                     help="skip the kernel-aware against hit-only eviction leg")
+    ap.add_argument("--no-box-peaks", action="store_true",
+                    help="skip re-measuring the HBM and bf16 matrix-core ceilings on the box")
     ap.add_argument("--no-chunk-sweep", action="store_true",
                     help="skip the prefill chunk-size curve")
     ap.add_argument("--no-layout", action="store_true",
@@ -799,6 +801,44 @@ def eviction_leg(args, flush, w):
                                                       - policies["latency_aware"]["us"], 3)}
 
 
+def box_peaks_leg():
+    """The roofline denominators re-measured on this GPU, for context beside
+    the published peaks: a 1 GiB streaming read (torch row sums over 4096
+    rows) and a 1 GiB device-to-device copy (HBM bytes per second), and a
+    large bf16 GEMM
+    (torch matmul through the vendor BLAS) as the practical matrix-core
+    ceiling.  Each is the best of several back-to-back runs after warm-up."""
+    import torch
+    st = torch.cuda.current_stream()
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    rows = a.view(4096, -1)
+    sink = torch.empty(4096, dtype=torch.float32, device="cuda")
+    rd = lambda: torch.sum(rows, dim=1, out=sink)
+    cp = lambda: b.copy_(a)
+    res = {}
+    for name, fn, nbytes in (("hbm_read_GB/s", rd, n), ("hbm_copy_GB/s", cp, 2 * n)):
+        for _ in range(3):
+            fn()
+        best = min(time_calls(fn, 5, st) for _ in range(4))
+        res[name] = round(nbytes / best / 1e9, 1)
+    del a, b
+    m = 8192
+    x = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    y = torch.randn(m, m, dtype=torch.bfloat16, device="cuda")
+    z = torch.empty(m, m, dtype=torch.bfloat16, device="cuda")
+    mm = lambda: torch.matmul(x, y, out=z)
+    warm_for(mm, 0.25)
+    best = min(time_calls(mm, 10, st) for _ in range(4))
+    res["bf16_gemm_TFLOP/s"] = round(2 * m ** 3 / best / 1e12, 1)
+    res["gemm"] = f"bf16 {m} x {m} x {m}, torch.matmul"
+    res["published"] = {"hbm_GB/s": HBM_PEAK_GBS, "bf16_dense_TFLOP/s": MFMA_BF16_PEAK_TFS}
+    del x, y, z
+    torch.cuda.empty_cache()
+    return res
+
+
 def chunk_sweep_leg(args, flush):
     """The prefill workload with the chunk length varied (8192 cached tokens,
     batch 4, 32 / 8 heads): the chunk-size curve, and the chunk length the
@@ -1083,6 +1123,8 @@ def main(argv=None):
             del wr
         if not args.no_chunk_sweep:
             result["chunk_sweep"] = chunk_sweep_leg(args, flush)
+    if not args.no_box_peaks:
+        result["box_peaks"] = box_peaks_leg()
     if args.copy_calibration:
         a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
         bb = torch.empty_like(a)
