@@ -193,8 +193,34 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
   const int T = p.split_blocks;
 
   const int s0 = p.indptr[b], s1 = p.indptr[b + 1];
+  // staged segment list: first block, physical id and block count of each
+  int32_t* st_start = reinterpret_cast<int32_t*>(&k_lds[0][0]);
+  int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
+  int32_t* st_nblk = st_phys + kMaxSplitBlocks + 1;
+  __shared__ int32_t st_alive;
+  auto stage = [&](int sf, int n) {
+    for (int i = tid; i < n; i += kThreads) {
+      const msa_segment sg = p.segs[sf + i];
+      st_start[i] = sg.alive_token_start / kBlk;
+      // the plan never emits a segment outside the pool; a foreign one is dropped
+      const bool in_pool = sg.phys_block >= 0 && sg.num_blocks >= 0 &&
+                           int64_t(sg.phys_block) + sg.num_blocks <= p.P;
+      st_phys[i] = in_pool ? sg.phys_block : -1;
+      st_nblk[i] = in_pool ? sg.num_blocks : 0;
+      if (sf + i == s1 - 1) st_alive = sg.alive_token_start + sg.num_tokens;
+    }
+  };
+  // A split holds at most T blocks, so at most T segments: when the
+  // sequence has no more, the first split stages the whole list at once and
+  // takes the alive length from its last segment (one dependent round trip
+  // to memory fewer than reading the last segment first)
+  const bool staged = s == 0 && s1 > s0 && s1 - s0 <= T;
   int A = 0;
-  if (s1 > s0) {
+  if (staged) {
+    stage(s0, s1 - s0);
+    __syncthreads();
+    A = st_alive;
+  } else if (s1 > s0) {
     const msa_segment last = p.segs[s1 - 1];
     A = last.alive_token_start + last.num_tokens;
   }
@@ -222,20 +248,10 @@ __global__ void __launch_bounds__(kThreads, 2) decode_kernel(DecodeParams p) {
 
   // ---- expand this split's segments into per-block physical ids ----------
   // (the first split starts at the sequence's first segment: no search)
+  // (staged: sf = s0 and ns <= s1 - s0, all of it in LDS already)
   const int sf = j0 == 0 ? s0 : wg_search_segment_n<kThreads>(p.segs, s0, s1, j0 * kBlk);
   const int ns = min(nblk, s1 - sf);
-  int32_t* st_start = reinterpret_cast<int32_t*>(&k_lds[0][0]);
-  int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
-  int32_t* st_nblk = st_phys + kMaxSplitBlocks + 1;
-  for (int i = tid; i < ns; i += kThreads) {
-    const msa_segment sg = p.segs[sf + i];
-    st_start[i] = sg.alive_token_start / kBlk;
-    // the plan never emits a segment outside the pool; a foreign one is dropped
-    const bool in_pool = sg.phys_block >= 0 && sg.num_blocks >= 0 &&
-                         int64_t(sg.phys_block) + sg.num_blocks <= p.P;
-    st_phys[i] = in_pool ? sg.phys_block : -1;
-    st_nblk[i] = in_pool ? sg.num_blocks : 0;
-  }
+  if (!staged) stage(sf, ns);
   {  // this KV head's G query rows -> LDS (contiguous G*ROW bytes)
     const uint8_t* qsrc = static_cast<const uint8_t*>(p.q) + (size_t(b) * p.Hq + size_t(g) * G) * ROW;
     for (int i = tid; i < G * CH; i += kThreads)
@@ -561,8 +577,33 @@ __global__ void __launch_bounds__(kThreads, KDMA ? 1 : 2) decode_mfma_kernel(Dec
   }
 
   const int s0 = p.indptr[b], s1 = p.indptr[b + 1];
+  // staged segment list: first block, physical id and block count of each
+  int32_t* st_start = reinterpret_cast<int32_t*>(&v_lds[0][0]);
+  int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
+  int32_t* st_nblk = st_phys + kMaxSplitBlocks + 1;
+  __shared__ int32_t st_alive;
+  auto stage = [&](int sf, int n) {
+    for (int i = tid; i < n; i += kThreads) {
+      const msa_segment sg = p.segs[sf + i];
+      st_start[i] = sg.alive_token_start / kBlk;
+      const bool in_pool = sg.phys_block >= 0 && sg.num_blocks >= 0 &&
+                           int64_t(sg.phys_block) + sg.num_blocks <= p.P;
+      st_phys[i] = in_pool ? sg.phys_block : -1;
+      st_nblk[i] = in_pool ? sg.num_blocks : 0;
+      if (sf + i == s1 - 1) st_alive = sg.alive_token_start + sg.num_tokens;
+    }
+  };
+  // A split holds at most T blocks, so at most T segments.  When the
+  // sequence has no more than that, the first split stages its whole list
+  // at once and takes the alive length from its last segment: one dependent
+  // round trip to memory fewer than reading the last segment first.
+  const bool staged = s == 0 && s1 > s0 && s1 - s0 <= T;
   int A = 0;
-  if (s1 > s0) {
+  if (staged) {
+    stage(s0, s1 - s0);
+    __syncthreads();
+    A = st_alive;
+  } else if (s1 > s0) {
     const msa_segment last = p.segs[s1 - 1];
     A = last.alive_token_start + last.num_tokens;
   }
@@ -589,19 +630,12 @@ __global__ void __launch_bounds__(kThreads, KDMA ? 1 : 2) decode_mfma_kernel(Dec
   {
     // the first split starts at the sequence's first segment: no search
     const int sf = j0 == 0 ? s0 : wg_search_segment_n<kThreads>(p.segs, s0, s1, j0 * kBlk);
+    // (staged: sf = s0 and ns <= s1 - s0, all of it in LDS already)
     const int ns = min(nblk, s1 - sf);
-    int32_t* st_start = reinterpret_cast<int32_t*>(&v_lds[0][0]);
-    int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
-    int32_t* st_nblk = st_phys + kMaxSplitBlocks + 1;
-    for (int i = tid; i < ns; i += kThreads) {
-      const msa_segment sg = p.segs[sf + i];
-      st_start[i] = sg.alive_token_start / kBlk;
-      const bool in_pool = sg.phys_block >= 0 && sg.num_blocks >= 0 &&
-                           int64_t(sg.phys_block) + sg.num_blocks <= p.P;
-      st_phys[i] = in_pool ? sg.phys_block : -1;
-      st_nblk[i] = in_pool ? sg.num_blocks : 0;
+    if (!staged) {
+      stage(sf, ns);
+      __syncthreads();
     }
-    __syncthreads();
     for (int jj = tid; jj < nblk; jj += kThreads) {
       const int j = j0 + jj;
       int lo = 0, hi = ns;
