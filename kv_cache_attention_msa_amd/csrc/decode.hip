@@ -729,12 +729,21 @@ __global__ void __launch_bounds__(kThreads, KDMA ? 1 : 2) decode_mfma_kernel(Dec
     }
   };
 
-  int ti = w;
+  // Streaming wavefronts.  With one workgroup per CU on a grid that fills
+  // most of the chip, the DRAM is oversubscribed and three wavefronts' loads
+  // in flight per CU move the same bytes a little sooner than four (cold,
+  // the 32 x 4k batch, two sessions: 73.5 / 74.1 against 75.3 / 74.8 us;
+  // head-major pools unchanged within noise); at two workgroups per CU four
+  // stay better (the 131k-token batch with this kernel: 200 against 197 us
+  // with three).  The idle wavefront joins the merge with an empty state.
+  const int nw_act =
+      KDMA && int64_t(gridDim.x) * gridDim.y * gridDim.z >= 3 * kCUs / 4 ? kNW - 1 : kNW;
+  int ti = w < nw_act ? w : ntiles;
   int ph[4], rows[4], phn[4], rowsn[4];
   tile_blocks(ti, ph, rows);
   issue_k(ph, rows);
   issue_v(ph, rows);
-  for (; ti < ntiles; ti += kNW) {
+  for (; ti < ntiles; ti += nw_act) {
     if constexpr (KDMA) {
       // K(t) has landed once at most the 16 V DMAs of this tile are in
       // flight; then the A operands come from the K tile (slot c ^ key)
@@ -758,7 +767,7 @@ __global__ void __launch_bounds__(kThreads, KDMA ? 1 : 2) decode_mfma_kernel(Dec
     }
     // next tile's K is in flight during softmax and PV of this one (KDMA:
     // once this tile's operand reads have returned)
-    tile_blocks(ti + kNW, phn, rowsn);
+    tile_blocks(ti + nw_act, phn, rowsn);
     if constexpr (KDMA) asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
     issue_k(phn, rowsn);
 
