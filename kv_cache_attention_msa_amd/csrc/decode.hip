@@ -1011,6 +1011,29 @@ __device__ __forceinline__ void block_excl_scan3(int u, int v, int x, int* red, 
   ex = bc + c - x;
 }
 
+// largest i in [lo, hi) with segs[i].alive_token_start <= x (the starts
+// ascend, segs[lo] starts at or before x), for a whole workgroup: with at
+// most 16 segments per thread every start is loaded in one round trip and the
+// answer is lo + (how many start at or before x) - 1; longer lists take the
+// narrowing search (red: kBHkv ints of LDS)
+__device__ __forceinline__ int wg_search_segment_wide(const msa_segment* segs, int lo, int hi, int x, int* red) {
+  if (hi - lo > 16 * kBThreads) return wg_search_segment_n<kBThreads>(segs, lo, hi, x);
+  int cnt = 0;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) {
+    const int idx = lo + k * kBThreads + int(threadIdx.x);
+    if (k * kBThreads < hi - lo) cnt += idx < hi && segs[idx].alive_token_start <= x;
+  }
+  cnt = wave_sum(cnt);
+  if ((threadIdx.x & (kWave - 1)) == 0) red[threadIdx.x / kWave] = cnt;
+  __syncthreads();
+  int total = 0;
+#pragma unroll
+  for (int i = 0; i < kBHkv; ++i) total += red[i];
+  __syncthreads();
+  return lo + total - 1;
+}
+
 // largest i in [0, n) with a[i] <= x (a ascending, a[0] <= x)
 __device__ __forceinline__ int lds_upper(const int32_t* a, int n, int x) {
   int lo = 0, hi = n;
@@ -1313,12 +1336,13 @@ __global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams
     if (is_head(i)) heads_mask |= 1 << (i - i0);
   int T = p.split_blocks;
   if (p.block_auto) {
-    // blocks actually read and the ranges they come in
+    // blocks actually read, and the ranges they come in (a sequence with no
+    // alive block counts as one range: it is one item at any T)
     int wsum = 0, ranges = 0;
     for (int i = i0; i < i1; ++i) {
       const int rest = nbc_of(i) - sh.lc[i];
       wsum += max(rest, 0);
-      ranges += rest > 0;
+      ranges += rest > 0 || sh.lc[i] == 0;
       if ((heads_mask >> (i - i0)) & 1) {
         wsum += sh.lc[i];
         ranges += 1;
@@ -1328,15 +1352,11 @@ __global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams
     block_sum2(wsum, ranges, sh.red, W, NR);
     const int target = p.block_target;
     // smallest T in [lo, hi] with at most target items and the partials
-    // within the workspace; both counts fall as T grows, and T =
-    // kMaxSplitBlocks always fits (the host sized grid and workspace for
-    // it).  Each round tests eight points of the interval, one per
-    // wavefront, each summing over all sequences in its own lanes.
-    int lo = min(max(kBMinSplit, (W + target - 1) / target), kMaxSplitBlocks);
-    int hi = kMaxSplitBlocks;
+    // within the workspace; both counts fall as T grows.  A round tests
+    // eight points, one per wavefront, each summing over all sequences in
+    // its own lanes, and returns which of them fit.
     const int w = tid / kWave, lane = tid & (kWave - 1);
-    while (lo < hi) {
-      const int cand = lo + ((hi - lo) * (w + 1)) / 9;
+    auto fits = [&](int cand) {
       int it = 0, pa = 0;
       for (int i = lane; i < B; i += kWave) {
         const int pv = priv_items(i, cand), sv = shared_items(sh.lc[i], cand);
@@ -1347,17 +1367,40 @@ __global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams
       pa = wave_sum(pa);
       if (lane == 0) sh.red[w] = it <= target && pa <= p.block_parts;
       __syncthreads();
-      int nlo = lo + ((hi - lo) * 8) / 9 + 1, nhi = hi;
+      int bits = 0;
 #pragma unroll
-      for (int k = kBHkv - 1; k >= 0; --k) {
-        if (sh.red[k]) {
-          nhi = lo + ((hi - lo) * (k + 1)) / 9;
-          nlo = k == 0 ? lo : lo + ((hi - lo) * k) / 9 + 1;
-        }
-      }
+      for (int k = 0; k < kBHkv; ++k) bits |= (sh.red[k] != 0) << k;
       __syncthreads();
-      lo = min(nlo, nhi);
-      hi = nhi;
+      return bits;
+    };
+    int lo = min(max(kBMinSplit, (W + target - 1) / target), kMaxSplitBlocks);
+    int hi = kMaxSplitBlocks;  // always fits: the host sized grid and workspace for it
+    // A range of r blocks makes ceil(r / T) <= r / T + 1 items, so every T
+    // >= W / (target - NR) meets the item bound; unless the partial bound
+    // binds, the answer lies in [lo, that].  A first round tests eight
+    // points ending there; then [lo, hi] narrows with hi known to fit.
+    const int slack = target - NR;
+    const int ha = min(max(slack > 0 ? (W + slack - 1) / slack : kMaxSplitBlocks, lo), kMaxSplitBlocks);
+    if (ha < hi) {
+      const int bits = fits(lo + ((ha - lo) * (w + 1)) / kBHkv);
+      if (bits != 0) {
+        const int k = __builtin_ctz(bits);
+        hi = lo + ((ha - lo) * (k + 1)) / kBHkv;
+        lo = k == 0 ? lo : lo + ((ha - lo) * k) / kBHkv + 1;
+      } else {
+        lo = ha + 1;
+      }
+    }
+    while (lo < hi) {
+      const int bits = fits(lo + ((hi - lo) * (w + 1)) / 9);
+      if (bits != 0) {
+        const int k = __builtin_ctz(bits);
+        const int nhi = lo + ((hi - lo) * (k + 1)) / 9;
+        lo = k == 0 ? lo : lo + ((hi - lo) * k) / 9 + 1;
+        hi = nhi;
+      } else {
+        lo = lo + ((hi - lo) * 8) / 9 + 1;
+      }
     }
     T = lo;
   }
@@ -1427,7 +1470,7 @@ __global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams
     if (nblk > 0) {
       // expand the item's segments into per-block physical ids
       const int s0 = p.indptr[b], s1 = p.indptr[b + 1];
-      const int sf = j0 == 0 ? s0 : wg_search_segment_n<kBThreads>(p.segs, s0, s1, j0 * kBlk);
+      const int sf = j0 == 0 ? s0 : wg_search_segment_wide(p.segs, s0, s1, j0 * kBlk, sh.red);
       const int ns = min(nblk, s1 - sf);
       int32_t* st_start = reinterpret_cast<int32_t*>(&kv_lds[0][0][0][0]);
       int32_t* st_phys = st_start + kMaxSplitBlocks + 1;
