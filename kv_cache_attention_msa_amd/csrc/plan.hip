@@ -80,31 +80,54 @@ __device__ __forceinline__ bool live(const PlanParams& p, const SeqView& v, int 
   return true;
 }
 
-__device__ __forceinline__ int block_sum_int(int x, int* red) {
-  // wave reduce with shuffles, then across the 4 waves through LDS
-  for (int o = 32; o > 0; o >>= 1) x += __shfl_xor(x, o);
-  const int w = threadIdx.x / kWave;
-  __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = x;
-  __syncthreads();
-  int t = 0;
-  for (int i = 0; i < kPlanThreads / kWave; ++i) t += red[i];
-  return t;
+// Inclusive prefix over the 64 lanes of a wavefront with DPP (no LDS round
+// trips): row shifts by 1, 2, 4, 8 scan each 16-lane row, then lane 15 is
+// folded into rows 1 and 3 and lane 31 into rows 2 and 3.  Lanes a shift
+// leaves without a source take the identity.
+template <typename Op>
+__device__ __forceinline__ int dpp_scan(int x, int ident, Op op) {
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x111, 0xf, 0xf, false));  // row_shr:1
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x112, 0xf, 0xf, false));  // row_shr:2
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x114, 0xf, 0xf, false));  // row_shr:4
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x118, 0xf, 0xf, false));  // row_shr:8
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  x = op(x, __builtin_amdgcn_update_dpp(ident, x, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return x;
 }
+struct AddOp {
+  __device__ int operator()(int a, int b) const { return a + b; }
+};
+struct OrOp {
+  __device__ int operator()(int a, int b) const { return a | b; }
+};
+struct MaxOp {
+  __device__ int operator()(int a, int b) const { return max(a, b); }
+};
 
-__device__ __forceinline__ int block_or_int(int x, int* red) {
-  for (int o = 32; o > 0; o >>= 1) x |= __shfl_xor(x, o);
+// workgroup sum of x and OR of y, both returned to every thread (red: two
+// ints per wavefront of LDS)
+__device__ __forceinline__ void block_sum_or(int x, int y, int* red, int& sum, int& any) {
+  x = __builtin_amdgcn_readlane(dpp_scan(x, 0, AddOp()), kWave - 1);
+  y = __builtin_amdgcn_readlane(dpp_scan(y, 0, OrOp()), kWave - 1);
+  constexpr int nw = kPlanThreads / kWave;
   const int w = threadIdx.x / kWave;
   __syncthreads();
-  if ((threadIdx.x & (kWave - 1)) == 0) red[w] = x;
+  if ((threadIdx.x & (kWave - 1)) == 0) {
+    red[w] = x;
+    red[nw + w] = y;
+  }
   __syncthreads();
-  int t = 0;
-  for (int i = 0; i < kPlanThreads / kWave; ++i) t |= red[i];
-  return t;
+  sum = 0;
+  any = 0;
+#pragma unroll
+  for (int i = 0; i < nw; ++i) {
+    sum += red[i];
+    any |= red[nw + i];
+  }
 }
 
 __global__ void __launch_bounds__(kPlanThreads) plan_count_kernel(PlanParams p) {
-  __shared__ int red[kPlanThreads / kWave];
+  __shared__ int red[2 * (kPlanThreads / kWave)];
   const int b = blockIdx.x;
   int flags = 0;
   const SeqView v = seq_view(p, b, flags);
@@ -121,8 +144,8 @@ __global__ void __launch_bounds__(kPlanThreads) plan_count_kernel(PlanParams p) 
       starts += cont ? 0 : 1;
     }
   }
-  const int total = block_sum_int(starts, red);
-  const int f = block_or_int(flags, red);
+  int total, f;
+  block_sum_or(starts, flags, red, total, f);
   if (threadIdx.x == 0) {
     p.ws[b] = total;
     p.ws[p.B + b] = f;
@@ -137,15 +160,10 @@ struct Scan3 {
 __device__ __forceinline__ Scan3 block_exclusive_scan3(Scan3 v, Scan3* lds, Scan3& total) {
   const int lane = threadIdx.x & (kWave - 1);
   const int w = threadIdx.x / kWave;
-  Scan3 inc = v;
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int a = __shfl_up(inc.a, o), t = __shfl_up(inc.t, o), m = __shfl_up(inc.m, o);
-    if (lane >= o) {
-      inc.a += a;
-      inc.t += t;
-      inc.m = max(inc.m, m);
-    }
-  }
+  Scan3 inc;
+  inc.a = dpp_scan(v.a, 0, AddOp());
+  inc.t = dpp_scan(v.t, 0, AddOp());
+  inc.m = dpp_scan(v.m, -1, MaxOp());
   __syncthreads();
   if (lane == kWave - 1) lds[w] = inc;
   __syncthreads();
@@ -173,7 +191,7 @@ __device__ __forceinline__ Scan3 block_exclusive_scan3(Scan3 v, Scan3* lds, Scan
 }
 
 __global__ void __launch_bounds__(kPlanThreads) plan_write_kernel(PlanParams p) {
-  __shared__ int red[kPlanThreads / kWave];
+  __shared__ int red[2 * (kPlanThreads / kWave)];
   __shared__ Scan3 scan_lds[kPlanThreads / kWave];
   const int b = blockIdx.x;
 
@@ -199,12 +217,13 @@ __global__ void __launch_bounds__(kPlanThreads) plan_write_kernel(PlanParams p) 
       all += c;
       fl |= p.ws[p.B + i];
     }
-    off = block_sum_int(before, red);
+    int unused;
+    block_sum_or(before, 0, red, off, unused);
     const int count_b = p.ws[b];
     if (threadIdx.x == 0) p.indptr[b + 1] = min(off + count_b, p.cap);
     if (b == 0) {
-      const int total = block_sum_int(all, red);
-      const int flags = block_or_int(fl, red);
+      int total, flags;
+      block_sum_or(all, fl, red, total, flags);
       if (threadIdx.x == 0) {
         p.indptr[0] = 0;
         p.dev_error[0] = flags | (total > p.cap ? MSA_DEVERR_CAPACITY : 0);
