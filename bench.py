@@ -51,7 +51,11 @@ COUNTERS5 = os.path.join(ROOT, "profiles", "decode_131k_counters.json")
 PREFILL_SOURCES = ["prefill.hip", "msa_internal.h"]
 FLUSH_BYTES = 512 << 20  # twice the Infinity Cache (256 MB), far above L2
 
-ONLY = ("decode", "decode-warm", "decode4", "decode5", "prefill", "kernels")
+ONLY = ("decode", "decode-warm", "decode4", "decode5", "prefill", "kernels", "choice")
+# (batch, context tokens) of the kernel-choice sweep: 128k tokens in all from
+# batch 4 up, 32k and 64k below
+CHOICE_POINTS = ((1, 32768), (2, 32768), (4, 32768), (8, 16384), (16, 8192), (32, 4096), (64, 2048),
+                 (128, 1024), (256, 512), (512, 256))
 
 
 def parse(argv=None):
@@ -87,9 +91,12 @@ def parse(argv=None):
     ap.add_argument("--kv-layout", choices=["nhd", "hnd"], default="nhd",
                     help="pool block layout of the headline decode leg: token-major "
                          "[P, 16, Hkv, D] (default) or head-major [P, Hkv, 16, D]")
+    ap.add_argument("--choice-points", default=None,
+                    help="with --only choice: comma-separated BxCTX points (default: the built-in sweep)")
     ap.add_argument("--only", choices=ONLY, default=None,
                     help="time only one call, cold (decode, decode4, decode5, prefill, kernels) "
-                         "or back to back (decode-warm), for profiler runs")
+                         "or back to back (decode-warm), for profiler runs; choice: the automatic "
+                         "decode-kernel choice against each kernel over batch sizes")
     return ap.parse_args(argv)
 
 
@@ -919,6 +926,30 @@ def main(argv=None):
                     result[f"{name}, {kname}"] = dist_us(cold_times(prep.attention, n, prep.stream, flush))
                     del prep
                     torch.cuda.empty_cache()
+        elif args.only == "choice":
+            # the automatic decode-kernel choice against each kernel forced,
+            # over batch sizes at a fixed total context (the headline recipe)
+            pts = []
+            points = CHOICE_POINTS if not args.choice_points else tuple(
+                (int(a), int(c)) for a, c in (x.split("x") for x in args.choice_points.split(",")))
+            for B, ctx in points:
+                w = make_workload(2, seed=args.seed, B=B, ctx=ctx)
+                d = None
+                row = {"B": B, "ctx": ctx}
+                for kname, k in (("auto", _lib.MSA_DECODE_AUTO), ("vector", _lib.MSA_DECODE_VECTOR),
+                                 ("matrix", _lib.MSA_DECODE_MATRIX), ("block", _lib.MSA_DECODE_BLOCK)):
+                    prep = Prepared(w, kernel=k, d=d)
+                    d = prep.d
+                    for _ in range(args.warmup):
+                        prep.step()
+                    prep.check_error()
+                    row[kname] = round(tmean(cold_times(prep.attention, n, prep.stream, flush)) * 1e6, 2)
+                    del prep
+                row["auto_vs_best"] = round(row["auto"] / min(row["vector"], row["matrix"], row["block"]), 3)
+                pts.append(row)
+                del d
+                torch.cuda.empty_cache()
+            result["points"] = pts
         elif args.only in ("decode4", "decode5"):
             w = make_workload(4 if args.only == "decode4" else 5, seed=args.seed)
             prep = Prepared(w, args.split_blocks, kv_layout=layout)

@@ -173,8 +173,10 @@ size_t msa_decode_workspace_size(int32_t B, int32_t Hq, int32_t Hkv, int32_t D,
  * the block kernel runs one workgroup per split for all KV heads and, with
  * split_blocks 0, chooses the split length on the device from the plan's
  * alive counts.  The automatic choice (msa_decode, MSA_DECODE_AUTO) is the
- * block kernel where it is built and B <= 256, except when one workgroup per
- * (sequence, KV head) fills the 256 CUs and no context exceeds 256 blocks.
+ * block kernel where it is built, B <= 256 and B * ceil(max_ctx_len / 16)
+ * >= 6144 (enough blocks for 256 work items of 24 blocks), except when one
+ * workgroup per (sequence, KV head) fills the 256 CUs and no context exceeds
+ * 256 blocks.
  * When a sequence has more than one partial they go to `workspace` and a
  * merge kernel stitches them by log-sum-exp (as msa_merge_partials).
  *

@@ -50,8 +50,9 @@ int check_attn_shape(const void* q, const void* k_pool, const void* v_pool, int3
 
 // The decode kernel a call runs: true for the block kernel.  Automatic
 // choice: the block kernel for up to 256 sequences (the range in which it
-// looks for shared prefixes), unless one workgroup per (sequence, KV head)
-// already fills the chip with no split (every context within 256 blocks):
+// looks for shared prefixes) holding at least 6144 blocks in all, unless
+// one workgroup per (sequence, KV head) already fills the chip with no
+// split (every context within 256 blocks):
 // there the per-head kernel needs no merge and no device-side set-up, and
 // wins (32 x 4k tokens, cold: 75.5 against 85 us).  Elsewhere the block
 // kernel's whole-block stream wins: 4 x 131k tokens 179 against 197 us, 64
@@ -62,6 +63,13 @@ bool decode_uses_block(msa_decode_kernel kernel, msa_dtype dtype, int32_t B, int
   if (kernel != MSA_DECODE_AUTO) return false;
   if (!decode_block_supported(dtype, D, Hkv, Hq / Hkv, B) || B > kDecodeBlockMaxShareSeq) return false;
   const int64_t nbm = (int64_t(max_ctx_len) + block_size - 1) / block_size;
+  // Its 256 items must be long enough to pay for the block kernel's set-up
+  // and merge: below 24 blocks per item on a fully alive batch the per-head
+  // kernel is faster (cold, headline recipe at 128k tokens or less: batch
+  // 1 x 32k 32.5 against 35.4 us, 1 x 64k 48.5 against 54.4, 2 x 32k 46.2
+  // against 52.8; at 6144 blocks the two are within 2% either way, above it
+  // the block kernel wins or ties).
+  if (int64_t(B) * nbm < 24 * 256) return false;
   return !(int64_t(B) * Hkv >= 256 && nbm <= 256);
 }
 
