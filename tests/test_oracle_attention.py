@@ -17,7 +17,6 @@ below fix it against things other than itself:
   at least one of these pins fail.
 """
 import math
-import os
 import types
 
 import numpy as np
