@@ -48,6 +48,14 @@ def test_plan_workloads_full(cfg, seed):
     assert_plan_equal(w.block_table, w.alive, w.ctx_len, w.block_size, w.num_phys_blocks)
 
 
+@pytest.mark.parametrize("B", [1024, 1025, 3000])
+def test_plan_batches_around_the_scan_launch(B):
+    # up to 1024 sequences each write workgroup sums the counts before its
+    # own; above that a one-workgroup scan launch computes the offsets
+    w = make_workload(2, seed=B, B=B, ctx=16 * 24 - 5, values=False)
+    assert_plan_equal(w.block_table, w.alive, w.ctx_len, w.block_size, w.num_phys_blocks)
+
+
 def test_plan_fuzz():
     rng = np.random.default_rng(123)
     for _ in range(150):
