@@ -515,7 +515,7 @@ def oracle_baseline(fn, work, unit, scale, sample, budget_s=6.0, max_reps=20, si
     return rec
 
 
-def decode_cpu_baseline(w, seqs=None, budget_s=6.0, single=True, label=""):
+def decode_cpu_baseline(w, seqs=None, budget_s=6.0, single=True, label="", max_reps=20):
     """The oracle's decode (decode_ref) on the whole batch or on the given
     sequences (all heads), as GB/s of algorithmic bytes."""
     import oracle
@@ -526,7 +526,7 @@ def decode_cpu_baseline(w, seqs=None, budget_s=6.0, single=True, label=""):
     return oracle_baseline(fn, work, "GB/s", 1e9,
                            f"fp64 numpy oracle (decode_ref) on {label} {which} x {w.Hq} heads "
                            f"({work / 1e6:.1f} MB of alive K/V + Q/O)", budget_s=budget_s,
-                           single=single)
+                           max_reps=max_reps, single=single)
 
 
 def prefill_cpu_baseline(w, row_step=16, budget_s=6.0, max_reps=5, single=True):
@@ -1066,7 +1066,8 @@ def main(argv=None):
     del prep
     torch.cuda.empty_cache()
     if cpu:
-        result["cpu_baseline"] = decode_cpu_baseline(w2, budget_s=8.0, label="the headline batch,")
+        result["cpu_baseline"] = decode_cpu_baseline(w2, budget_s=12.0, max_reps=60,
+                                                     label="the headline batch,")
     if not args.no_layout and not head_major:
         # the same batch with head-major pool blocks (msa_decode_ex)
         dh = dict(d2)
@@ -1141,7 +1142,7 @@ def main(argv=None):
                            "timing": "mean of back-to-back calls after a quarter second of warm-up",
                            "algorithmic_flops_per_call": leg.pop("flops")}
         if cpu:
-            leg["cpu_baseline"] = prefill_cpu_baseline(wp)
+            leg["cpu_baseline"] = prefill_cpu_baseline(wp, budget_s=10.0, max_reps=40)
         result["prefill"] = {"workload": NAMES[3], **leg}
         del wp
         if not args.no_recompute:
