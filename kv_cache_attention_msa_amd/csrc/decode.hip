@@ -1293,13 +1293,21 @@ __global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams
   }
   __syncthreads();
   // ---- sharing: groups of equal first physical block, their common prefix --
-  for (int i = i0; i < i1; ++i) {
-    int lc = 0, sub = -1, rank = 0;
-    const int key = sh.key[i];
+  // Each sequence's group is summed over the batch by NP threads, one slice
+  // of the batch each, whose partial sums meet in LDS (the ring bytes are
+  // free until the items start): with one thread per sequence the scan was
+  // one wavefront's serial loop over the whole batch.
+  if (share) {
+    const int Bc = B <= 64 ? 64 : (B <= 128 ? 128 : 256);  // B <= kDecodeBlockMaxShareSeq
+    const int NP = kBThreads / Bc;
+    const int i = tid % Bc, part = tid / Bc;
+    const int span = ((B + NP - 1) / NP + 3) & ~3;  // whole int4 reads per slice
+    const int jlo = part * span, jhi = min(B, jlo + span);
+    int size = 0, rank = 0, lead = B, lmin = INT_MAX;
+    const int key = i < B ? sh.key[i] : -1;
     if (key >= 0) {
-      int size = 0, lmin = sh.fb[i], lead = i;
       // four sequences per LDS read (the arrays are padded with key -1)
-      for (int j4 = 0; j4 < B; j4 += 4) {
+      for (int j4 = jlo; j4 < jhi; j4 += 4) {
         const int4 k4 = *reinterpret_cast<const int4*>(&sh.key[j4]);
         const int4 f4 = *reinterpret_cast<const int4*>(&sh.fb[j4]);
         const int kk[4] = {k4.x, k4.y, k4.z, k4.w}, ff[4] = {f4.x, f4.y, f4.z, f4.w};
@@ -1313,14 +1321,35 @@ __global__ void __launch_bounds__(kBThreads, 1) decode_block_kernel(DecodeParams
           lmin = same ? min(lmin, ff[u]) : lmin;
         }
       }
-      if (size >= 2 && lmin >= kBMinShare) {
-        lc = lmin;
-        sub = lead * 64 + rank / kMPI;
-      }
     }
-    sh.lc[i] = lc;
-    sh.sub[i] = sub;
-    sh.rank[i] = rank;
+    int4* part_sum = reinterpret_cast<int4*>(&kv_lds[0][0][0][0]);  // [NP][Bc]
+    part_sum[part * Bc + i] = make_int4(size, rank, lead, lmin);
+    __syncthreads();
+    if (part == 0 && i < B) {
+      int lc = 0, sub = -1;
+      if (key >= 0) {
+        for (int q = 1; q < NP; ++q) {
+          const int4 v = part_sum[q * Bc + i];
+          size += v.x;
+          rank += v.y;
+          lead = min(lead, v.z);
+          lmin = min(lmin, v.w);
+        }
+        if (size >= 2 && lmin >= kBMinShare) {
+          lc = lmin;
+          sub = lead * 64 + rank / kMPI;
+        }
+      }
+      sh.lc[i] = lc;
+      sh.sub[i] = sub;
+      sh.rank[i] = rank;
+    }
+  } else {
+    for (int i = i0; i < i1; ++i) {
+      sh.lc[i] = 0;
+      sh.sub[i] = -1;
+      sh.rank[i] = 0;
+    }
   }
   __syncthreads();
   // members join sub-groups in index order: the head is rank 0 of its sub-group
