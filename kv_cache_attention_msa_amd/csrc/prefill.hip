@@ -87,6 +87,9 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 x) { return __builtin_bit_ca
 // lds_addr + 16*i, without passing through VGPRs.  Lanes outside the
 // descriptor's range write zeros.  Completion is counted by vmcnt; the
 // compiler does not track these, so the tile loop waits for them itself.
+// The LDS address goes through M0, which the compiler treats as reserved
+// (it warns that the clobber is ignored): nothing else in this kernel uses
+// M0 -- in the generated code every M0 write is one of these.
 __device__ __forceinline__ void dma16(u32x4_t rsrc, uint32_t lds_addr, uint32_t voff) {
   asm volatile("s_mov_b32 m0, %0\n\ts_nop 0\n\tbuffer_load_dwordx4 %1, %2, 0 offen lds"
                :: "s"(lds_addr), "v"(voff), "s"(rsrc) : "memory", "m0");
