@@ -47,10 +47,14 @@
  *   prefill O   [B, C, Hq, D]             dtype;  LSE [B, C, Hq] float32
  *   Query head h reads KV head h / (Hq / Hkv) (grouped-query attention).
  *
- * Supported kernels: block_size 16; Hq/Hkv in {1, 2, 4, 8}; decode in
- * bfloat16 with D 64 or 128, or float32 with D 64; prefill in bfloat16 with
- * D 128.  Anything else returns MSA_ERR_UNSUPPORTED (msa_attention_supported
- * answers without launching).  The plan accepts any block_size >= 1.
+ * Supported kernels: block_size 16; Hq/Hkv in {1, 2, 4, 8}; decode and
+ * prefill in bfloat16 or float32 with D 64 or 128.  The tuned kernels cover
+ * decode in bfloat16 (D 64, 128) and float32 (D 64) and prefill in bfloat16
+ * with D 128; the other pairs (decode float32 D 128, prefill bfloat16 D 64,
+ * prefill float32 D 64 and 128) run on a plain float32 vector-ALU kernel with
+ * the same results and no throughput target.  Anything else returns
+ * MSA_ERR_UNSUPPORTED (msa_attention_supported answers without launching).
+ * The plan accepts any block_size >= 1.
  */
 #ifndef MSA_H
 #define MSA_H

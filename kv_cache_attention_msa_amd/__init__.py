@@ -254,7 +254,8 @@ def msa_prefill_chunk(q: torch.Tensor, q_pos0: torch.Tensor, k_pool: torch.Tenso
                       out: torch.Tensor | None = None, lse: torch.Tensor | None = None,
                       workspace: torch.Tensor | None = None, want_lse: bool = True,
                       kv_layout: str = "NHD", dev_error: torch.Tensor | None = None, stream=None):
-    """Chunked-prefill attention.  q [B, C, Hq, D] bf16; q_pos0 int32 [B]; pools
+    """Chunked-prefill attention.  q [B, C, Hq, D] bf16 or float32 (the pools'
+    dtype); q_pos0 int32 [B]; pools
     and dev_error as for msa_decode.
     Returns (out [B, C, Hq, D], lse [B, C, Hq] float32 or None)."""
     lib = _lib_handle()

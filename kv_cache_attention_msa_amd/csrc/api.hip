@@ -295,9 +295,10 @@ int msa_prefill_chunk_ex(const void* q, int32_t C, const int32_t* q_pos0, const 
       msa_prefill_workspace_size(B, C, Hq, Hkv, D, max_ctx_len, block_size, split_blocks);
   if (need > 0 && (!workspace || workspace_bytes < need)) return MSA_ERR_CAPACITY;
 
-  PrefillParams p;
+  PrefillParams p{};
   p.q = q;
   p.q_pos0 = q_pos0;
+  p.dtype = dtype;
   p.C = C;
   p.k_pool = k_pool;
   p.v_pool = v_pool;

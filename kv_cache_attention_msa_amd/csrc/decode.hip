@@ -1616,7 +1616,7 @@ hipError_t launch_g(const DecodeParams& p, hipStream_t stream) {
 bool decode_supported(msa_dtype dtype, int32_t D, int32_t G) {
   const bool g_ok = G == 1 || G == 2 || G == 4 || G == 8;
   if (dtype == MSA_BF16) return g_ok && (D == 64 || D == 128);
-  if (dtype == MSA_F32) return g_ok && D == 64;
+  if (dtype == MSA_F32) return g_ok && (D == 64 || D == 128);  // D 128: the generic kernel
   return false;
 }
 
@@ -1698,6 +1698,35 @@ hipError_t launch_decode(const DecodeParams& p, hipStream_t stream) {
     if (p.D == 64) return launch_g<uint16_t, 64>(p, stream);
   } else if (p.dtype == MSA_F32) {
     if (p.D == 64) return launch_g<float, 64>(p, stream);
+    if (p.D == 128) {
+      // float32 rows of 512 bytes do not fit the vector kernel's load
+      // layout: the generic kernel, one query row
+      GenericParams gp{};
+      gp.q = p.q;
+      gp.q_pos0 = nullptr;
+      gp.C = 1;
+      gp.k_pool = p.k_pool;
+      gp.v_pool = p.v_pool;
+      gp.P = p.P;
+      gp.segs = p.segs;
+      gp.indptr = p.indptr;
+      gp.B = p.B;
+      gp.Hq = p.Hq;
+      gp.Hkv = p.Hkv;
+      gp.D = p.D;
+      gp.head_major = p.head_major;
+      gp.dtype = p.dtype;
+      gp.scale_log2 = p.scale_log2;
+      gp.split_blocks = p.split_blocks;
+      gp.S = p.S;
+      gp.dev_error = p.dev_error;
+      gp.out = p.out;
+      gp.lse = p.lse;
+      gp.o_part = p.o_part;
+      gp.m_part = p.m_part;
+      gp.l_part = p.l_part;
+      return launch_generic(gp, stream);
+    }
   }
   return hipErrorInvalidValue;
 }

@@ -123,11 +123,36 @@ struct PrefillParams {
   const msa_segment* segs;
   const int32_t* indptr;
   int32_t B, Hq, Hkv, D;
+  msa_dtype dtype;       // bf16 D 128: the matrix-core kernel; else the generic kernel
   int32_t head_major;    // pool layout: 0 = [P, bs, Hkv, D], 1 = [P, Hkv, bs, D]
   float scale_log2;
   int32_t split_blocks;  // 0 = no split
   int32_t S;
   int32_t* dev_error;    // nullable: MSA_DEVERR_TRUNCATED is ORed in
+  void* out;
+  float* lse;
+  float* o_part;  // [B*S, C, Hq, D]
+  float* m_part;  // [B*S, C, Hq]
+  float* l_part;
+};
+
+// the generic (vector-ALU, float32) kernel: decode is C = 1 with no q_pos0
+struct GenericParams {
+  const void* q;
+  const int32_t* q_pos0;  // nullable: decode (every alive key is visible)
+  int32_t C;
+  const void* k_pool;
+  const void* v_pool;
+  int32_t P;
+  const msa_segment* segs;
+  const int32_t* indptr;
+  int32_t B, Hq, Hkv, D;
+  int32_t head_major;
+  msa_dtype dtype;
+  float scale_log2;
+  int32_t split_blocks;
+  int32_t S;
+  int32_t* dev_error;
   void* out;
   float* lse;
   float* o_part;  // [B*S, C, Hq, D]
@@ -186,6 +211,10 @@ hipError_t launch_plan(const PlanParams& p, hipStream_t stream);
 hipError_t launch_decode(const DecodeParams& p, hipStream_t stream);
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_gather(const GatherParams& p, hipStream_t stream);
+// (dtype, head_dim) pairs outside the specialised kernels: decode float32 D
+// 128, prefill bfloat16 D 64 and float32 D 64 / 128
+bool generic_supported(msa_dtype dtype, int32_t D, int32_t G);
+hipError_t launch_generic(const GenericParams& p, hipStream_t stream);
 // Merge of decode/prefill split partials; the partial count of each sequence
 // is derived from the plan (same rule as the attention launch).
 hipError_t launch_merge_from_plan(const float* o_part, const float* m_part, const float* l_part,

@@ -657,7 +657,10 @@ hipError_t launch_g(const PrefillParams& p, hipStream_t stream) {
 }  // namespace
 
 bool prefill_supported(msa_dtype dtype, int32_t D, int32_t G) {
-  return dtype == MSA_BF16 && D == kD && (G == 1 || G == 2 || G == 4 || G == 8);
+  // bf16 D 128 on the matrix cores (this file); the other pairs of {bf16,
+  // f32} x {64, 128} on the generic kernel
+  return (dtype == MSA_BF16 && D == kD && (G == 1 || G == 2 || G == 4 || G == 8)) ||
+         generic_supported(dtype, D, G);
 }
 
 int32_t prefill_max_split_blocks() { return kMaxSplitBlocks; }
@@ -704,6 +707,33 @@ int32_t prefill_chunk_rows(int32_t B, int32_t Hq, int32_t Hkv, int32_t remaining
 }
 
 hipError_t launch_prefill(const PrefillParams& p, hipStream_t stream) {
+  if (p.dtype != MSA_BF16 || p.D != kD) {
+    GenericParams gp{};
+    gp.q = p.q;
+    gp.q_pos0 = p.q_pos0;
+    gp.C = p.C;
+    gp.k_pool = p.k_pool;
+    gp.v_pool = p.v_pool;
+    gp.P = p.P;
+    gp.segs = p.segs;
+    gp.indptr = p.indptr;
+    gp.B = p.B;
+    gp.Hq = p.Hq;
+    gp.Hkv = p.Hkv;
+    gp.D = p.D;
+    gp.head_major = p.head_major;
+    gp.dtype = p.dtype;
+    gp.scale_log2 = p.scale_log2;
+    gp.split_blocks = p.split_blocks;
+    gp.S = p.S;
+    gp.dev_error = p.dev_error;
+    gp.out = p.out;
+    gp.lse = p.lse;
+    gp.o_part = p.o_part;
+    gp.m_part = p.m_part;
+    gp.l_part = p.l_part;
+    return launch_generic(gp, stream);
+  }
   switch (p.Hq / p.Hkv) {
     case 1: return launch_g<1>(p, stream);
     case 2: return launch_g<2>(p, stream);

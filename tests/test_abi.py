@@ -91,7 +91,8 @@ def test_decode_rejects_bad_args():
     assert _decode(lib, bs=32) == _lib.MSA_ERR_UNSUPPORTED
     assert _decode(lib, D=96) == _lib.MSA_ERR_UNSUPPORTED
     assert _decode(lib, Hq=24) == _lib.MSA_ERR_UNSUPPORTED          # G = 3
-    assert _decode(lib, dtype=_lib.MSA_F32, D=128) == _lib.MSA_ERR_UNSUPPORTED
+    assert _decode(lib, dtype=_lib.MSA_F32, D=96) == _lib.MSA_ERR_UNSUPPORTED
+    assert _decode(lib, dtype=_lib.MSA_F32, D=256) == _lib.MSA_ERR_UNSUPPORTED
     assert _decode(lib, dtype=7) == _lib.MSA_ERR_UNSUPPORTED
     assert _decode(lib, split=100000) == _lib.MSA_ERR_INVALID_ARG
     need = lib.msa_decode_workspace_size(2, 32, 8, 128, 4096, 16, 0)
@@ -243,8 +244,8 @@ def test_prefill_rejects_bad_args():
     assert _prefill(lib, C=0) == _lib.MSA_ERR_INVALID_ARG
     assert _prefill(lib, Hq=30) == _lib.MSA_ERR_INVALID_ARG        # Hq % Hkv
     assert _prefill(lib, scale=float("inf")) == _lib.MSA_ERR_INVALID_ARG
-    assert _prefill(lib, dtype=_lib.MSA_F32) == _lib.MSA_ERR_UNSUPPORTED
-    assert _prefill(lib, D=64) == _lib.MSA_ERR_UNSUPPORTED
+    assert _prefill(lib, D=96) == _lib.MSA_ERR_UNSUPPORTED
+    assert _prefill(lib, dtype=_lib.MSA_F32, D=256) == _lib.MSA_ERR_UNSUPPORTED
     assert _prefill(lib, Hq=24) == _lib.MSA_ERR_UNSUPPORTED        # G = 3
     assert _prefill(lib, Hq=128, Hkv=8) == _lib.MSA_ERR_UNSUPPORTED  # G = 16
     # a small chunk splits the key stream: the workspace must hold the partials
@@ -257,6 +258,25 @@ def test_prefill_rejects_bad_args():
     assert _prefill(lib, B=40000, C=16, maxctx=1 << 20, split=64) == _lib.MSA_ERR_UNSUPPORTED
     assert _prefill(lib, B=1, C=70000, maxctx=1 << 20, split=64) == _lib.MSA_ERR_UNSUPPORTED
 
+
+
+def test_supported_set_is_every_dtype_and_head_dim_pair():
+    """Every (dtype, head_dim) of {bf16, f32} x {64, 128} with block size 16
+    and 1, 2, 4 or 8 query heads per KV head is built for decode and prefill
+    (the pairs the specialised kernels do not cover run on the generic
+    kernel); other dtypes, head dims, group sizes and block sizes are not."""
+    lib = _lib.load()
+    for prefill in (0, 1):
+        for dt in (_lib.MSA_BF16, _lib.MSA_F32):
+            for D in (64, 128):
+                for G in (1, 2, 4, 8):
+                    assert lib.msa_attention_supported(prefill, dt, D, G, 16) == 1, (prefill, dt, D, G)
+                assert lib.msa_attention_supported(prefill, dt, D, 3, 16) == 0
+                assert lib.msa_attention_supported(prefill, dt, D, 16, 16) == 0
+                assert lib.msa_attention_supported(prefill, dt, D, 4, 32) == 0
+            for D in (32, 96, 256):
+                assert lib.msa_attention_supported(prefill, dt, D, 4, 16) == 0
+        assert lib.msa_attention_supported(prefill, 7, 128, 4, 16) == 0
 
 def test_header_compiles_as_c_and_cpp(tmp_path):
     import shutil
