@@ -11,6 +11,9 @@ kernels; there is no CPU or PyTorch fallback, and a missing library raises.
   msa_prefill_chunk   chunked-prefill attention over the segments (a2, a4, a5)
   msa_merge_partials  log-sum-exp merge of (m, l, o) partials (a5)
   msa_gather_alive    gather-then-attend baseline: alive blocks -> dense pools
+
+Each is also reachable without the prefix (plan_segments, decode,
+prefill_chunk, merge_partials, prefill_chunk_rows, gather_alive).
 """
 from __future__ import annotations
 
@@ -30,7 +33,9 @@ __all__ = ["msa_plan_segments", "msa_decode", "msa_prefill_chunk", "msa_merge_pa
            "MsaError", "MSA_F32", "MSA_BF16", "MSA_DEVERR_PHYS_RANGE", "MSA_DEVERR_CAPACITY",
            "MSA_DEVERR_CTX_RANGE", "MSA_DEVERR_TRUNCATED", "MSA_LAYOUT_NHD", "MSA_LAYOUT_HND",
            "MSA_DECODE_AUTO", "MSA_DECODE_VECTOR", "MSA_DECODE_MATRIX", "MSA_DECODE_BLOCK", "SEG_FIELDS",
-           "library_path", "prefill_available", "decode_available"]
+           "library_path", "prefill_available", "decode_available",
+           "plan_segments", "decode", "prefill_chunk", "merge_partials", "prefill_chunk_rows",
+           "gather_alive"]
 
 SEG_FIELDS = ("seq", "logical_block", "phys_block", "num_blocks", "num_tokens",
               "alive_token_start")
@@ -387,3 +392,12 @@ def msa_gather_alive(k_pool: torch.Tensor, v_pool: torch.Tensor, segs: torch.Ten
                               _dev_ptr(dense_indptr, "dense_indptr"), _stream(stream, dev))
     _lib.check(st, "msa_gather_alive")
     return dense_k, dense_v, dense_segs, dense_indptr
+
+
+# the same calls without the C prefix
+plan_segments = msa_plan_segments
+decode = msa_decode
+prefill_chunk = msa_prefill_chunk
+merge_partials = msa_merge_partials
+prefill_chunk_rows = msa_prefill_chunk_rows
+gather_alive = msa_gather_alive

@@ -129,3 +129,10 @@ def test_layout_argument():
     with pytest.raises(ValueError, match="shape mismatch"):
         msa.msa_decode(q, bf16(10, 2, 16, 32), bf16(10, 2, 16, 32), segs, ind, max_ctx_len=64,
                        kv_layout="HND")
+
+
+def test_unprefixed_names_are_the_same_calls():
+    for short in ("plan_segments", "decode", "prefill_chunk", "merge_partials", "prefill_chunk_rows",
+                  "gather_alive"):
+        assert getattr(msa, short) is getattr(msa, "msa_" + short)
+        assert short in msa.__all__
