@@ -51,7 +51,7 @@ COUNTERS5 = os.path.join(ROOT, "profiles", "decode_131k_counters.json")
 PREFILL_SOURCES = ["prefill.hip", "msa_internal.h"]
 FLUSH_BYTES = 512 << 20  # twice the Infinity Cache (256 MB), far above L2
 
-ONLY = ("decode", "decode-warm", "decode4", "decode5", "prefill", "kernels", "choice")
+ONLY = ("decode", "decode-warm", "decode4", "decode5", "prefill", "kernels", "choice", "peaks")
 # (batch, context tokens) of the kernel-choice sweep: 128k tokens in all from
 # batch 4 up, 32k and 64k below
 CHOICE_POINTS = ((1, 32768), (2, 32768), (4, 32768), (8, 16384), (16, 8192), (32, 4096), (64, 2048),
@@ -96,7 +96,8 @@ def parse(argv=None):
     ap.add_argument("--only", choices=ONLY, default=None,
                     help="time only one call, cold (decode, decode4, decode5, prefill, kernels) "
                          "or back to back (decode-warm), for profiler runs; choice: the automatic "
-                         "decode-kernel choice against each kernel over batch sizes")
+                         "decode-kernel choice against each kernel over batch sizes; peaks: the "
+                         "re-measured HBM and matrix-core denominators")
     return ap.parse_args(argv)
 
 
@@ -836,13 +837,40 @@ def eviction_leg(args, flush, w):
                       "differences against hit_only"}
 
 
+def mfma_rate(st):
+    """bf16 matrix-core rate with register operands only (libmsa_peaks.so):
+    8192 workgroups of four wavefronts, each issuing 256 x 8 independent
+    v_mfma_f32_32x32x16_bf16 -- about 1.1 ms of matrix work on 256 CUs."""
+    import ctypes
+    import torch
+    from kv_cache_attention_msa_amd import build as _build
+    lib = ctypes.CDLL(_build.PEAKS_LIB)
+    fn = lib.msa_peaks_mfma_bf16
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    wgs, iters = 8192, 256
+    sink = torch.empty(wgs * 256, dtype=torch.float32, device="cuda")
+
+    def call():
+        rc = fn(wgs, iters, ctypes.c_void_p(sink.data_ptr()), ctypes.c_void_p(st.cuda_stream))
+        if rc != 0:
+            raise RuntimeError(f"msa_peaks_mfma_bf16 returned {rc}")
+
+    for _ in range(3):
+        call()
+    best = min(time_calls(call, 5, st) for _ in range(4))
+    flops = wgs * 4 * iters * 8 * 32768
+    return round(flops / best / 1e12, 1)
+
+
 def box_peaks_leg():
     """The roofline denominators re-measured on this GPU, for context beside
     the published peaks: a 1 GiB streaming read (torch row sums over 4096
-    rows) and a 1 GiB device-to-device copy (HBM bytes per second), and a
-    large bf16 GEMM
-    (torch matmul through the vendor BLAS) as the practical matrix-core
-    ceiling.  Each is the best of several back-to-back runs after warm-up."""
+    rows) and a 1 GiB device-to-device copy (HBM bytes per second), the
+    matrix cores' bf16 rate with register operands (the instrument kernel in
+    libmsa_peaks.so), and a large bf16 GEMM (torch matmul through the vendor
+    BLAS) as the practical matrix-core ceiling with memory traffic.  Each is
+    the best of several back-to-back runs after warm-up."""
     import torch
     st = torch.cuda.current_stream()
     n = 1 << 30
@@ -867,6 +895,12 @@ def box_peaks_leg():
     warm_for(mm, 0.25)
     best = min(time_calls(mm, 10, st) for _ in range(4))
     res["bf16_gemm_TFLOP/s"] = round(2 * m ** 3 / best / 1e12, 1)
+    try:
+        res["mfma_bf16_TFLOP/s"] = mfma_rate(st)
+        res["mfma"] = "v_mfma_f32_32x32x16_bf16, register operands, every CU (libmsa_peaks.so)"
+    except (OSError, RuntimeError) as e:
+        res["mfma_bf16_TFLOP/s"] = None
+        res["mfma"] = f"not measured: {e}"
     res["gemm"] = f"bf16 {m} x {m} x {m}, torch.matmul"
     res["published"] = {"hbm_GB/s": HBM_PEAK_GBS, "bf16_dense_TFLOP/s": MFMA_BF16_PEAK_TFS}
     del x, y, z
@@ -994,6 +1028,8 @@ def main(argv=None):
             prep.check_error()
             warm_for(prep.attention)
             result["us_per_call"] = round(time_calls(prep.attention, n, prep.stream) * 1e6, 3)
+        elif args.only == "peaks":
+            result["box_peaks"] = box_peaks_leg()
         if args.copy_calibration:
             a = torch.empty(256 << 20, dtype=torch.uint8, device="cuda")
             bb = torch.empty_like(a)

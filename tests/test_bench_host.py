@@ -57,3 +57,24 @@ def test_prefill_cpu_baseline_record():
     assert rec["kind"] == "oracle" and rec["unit"] == "TFLOP/s"
     assert rec["value"] > 0 and rec["cores"] >= 1
     json.dumps(rec)
+
+
+def test_peaks_instrument_loads_and_checks_its_arguments():
+    # the matrix-core rate kernel the bench reports beside the published peak:
+    # built next to libmsa.so, and its argument checks return before any HIP
+    # call, so they run without a GPU
+    import ctypes
+    import pytest
+    from kv_cache_attention_msa_amd import build as _build
+    if not os.path.exists(_build.PEAKS_LIB):
+        pytest.skip("libmsa_peaks.so not built")
+    lib = ctypes.CDLL(_build.PEAKS_LIB)
+    fn = lib.msa_peaks_mfma_bf16
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_int32, ctypes.c_int32, ctypes.c_void_p, ctypes.c_void_p]
+    sink = ctypes.c_void_p(0x1000)  # never dereferenced: each call below is rejected first
+    assert fn(0, 1, sink, None) == -1
+    assert fn(1, 0, sink, None) == -1
+    assert fn((1 << 20) + 1, 1, sink, None) == -1
+    assert fn(1, (1 << 20) + 1, sink, None) == -1
+    assert fn(1, 1, None, None) == -1
