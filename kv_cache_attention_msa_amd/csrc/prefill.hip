@@ -605,6 +605,15 @@ __global__ void __launch_bounds__((PGeo<G>::THREADS), (PGeo<G>::WAVES / 4))
   }
 
   // ---- finish: combine the two half-waves' sums, write O and LSE --------
+  // the row index is rebuilt from the logical position the mask kept live
+  // through the tile loop (an opaque copy stops the compiler from folding it
+  // back to the original, which it would then keep live -- in scratch)
+#pragma unroll
+  for (int r = 0; r < RT; ++r) {
+    int qp = my_qpos[r];
+    asm volatile("" : "+v"(qp));
+    my_row[r] = qp - q0;
+  }
 #pragma unroll
   for (int r = 0; r < RT; ++r) {
     const float L = l_lane[r] + __shfl_xor(l_lane[r], 32);
