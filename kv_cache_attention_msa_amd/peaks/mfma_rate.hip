@@ -9,6 +9,8 @@
 
 #include <cstdint>
 
+#include "../../include/msa_peaks.h"
+
 namespace {
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));

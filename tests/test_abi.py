@@ -289,3 +289,27 @@ def test_header_compiles_as_c_and_cpp(tmp_path):
         r = subprocess.run([cc, "-x", lang, std, "-Wall", "-Werror", "-pedantic", "-fsyntax-only",
                             "-I", os.path.join(ROOT, "include"), str(src)], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr
+
+
+def test_peaks_header_matches_its_library(tmp_path):
+    # the bench's instrument library: its header compiles as C and C++, and
+    # the library exports exactly the function the header declares
+    import shutil
+    import subprocess
+    from kv_cache_attention_msa_amd import build as _build
+    hdr = os.path.join(ROOT, "include", "msa_peaks.h")
+    src = re.sub(r"/\*.*?\*/", "", open(hdr).read(), flags=re.S)
+    names = sorted(set(re.findall(r"\b(msa_[a-z_0-9]+)\s*\(", src)))
+    assert names == ["msa_peaks_mfma_bf16"]
+    if os.path.exists(_build.PEAKS_LIB):
+        lib = ctypes.CDLL(_build.PEAKS_LIB)
+        for n in names:
+            assert hasattr(lib, n), n
+    for cc, lang, std in (("gcc", "c", "-std=c99"), ("g++", "c++", "-std=c++11")):
+        if shutil.which(cc) is None:
+            pytest.skip(f"{cc} not available")
+        f = tmp_path / f"use_peaks.{lang[0]}"
+        f.write_text('#include "msa_peaks.h"\nint use(float* s) { return msa_peaks_mfma_bf16(1, 1, s, 0); }\n')
+        r = subprocess.run([cc, "-x", lang, std, "-Wall", "-Werror", "-pedantic", "-fsyntax-only",
+                            "-I", os.path.join(ROOT, "include"), str(f)], capture_output=True, text=True)
+        assert r.returncode == 0, r.stderr
